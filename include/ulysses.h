@@ -1,0 +1,189 @@
+/*
+ * ulysses.h -- C ABI of the per-rank Ulysses sequence-parallel hot path on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * After the sequence-to-head all-to-all, each of P ranks holds the whole
+ * gathered sequence for H/P of the heads and runs exact softmax attention on
+ * them; the inverse all-to-all then returns sequence shards.  This library
+ * provides, for one GPU on which the P ranks are simulated in memory:
+ *
+ *   ulysses_a2a_pack / ulysses_a2a_unpack    the layout permutation of the
+ *                                            all-to-all (all P ranks at once)
+ *   ulysses_cu_seqlens_from_positions        cu_seqlens / max_len rebuilt from
+ *                                            the gathered position_ids
+ *   ulysses_attn_fwd / ulysses_attn_bwd      one rank's attention, fwd and bwd
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is a DEVICE pointer owned by the caller.  The
+ *     library keeps no pointer after a call returns and allocates nothing.
+ *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *     NULL = the default stream) and never synchronises the host.
+ *   - Arguments are checked on the host before any launch.  A call returns 0
+ *     (ULY_OK) or a negative uly_status and then launches nothing;
+ *     ulysses_last_error() gives a readable reason (thread-local).
+ *   - bf16 tensors are raw IEEE bfloat16 bits; fp32 is IEEE binary32.
+ *
+ * Citations name the web pages this path is defined by:
+ *   [accelerate#4209]  accelerate PR "Add an FSDP2-native Ulysses sequence
+ *                      parallelism backend"
+ *   [lca#135]          long-context-attention issue "usage with pytorch FSDP"
+ *   [arctic#45]        ArcticTraining PR "Add Sequence Parallelism via Ulysses"
+ */
+#ifndef ULYSSES_H
+#define ULYSSES_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ULY_OK = 0,
+  ULY_ERR_NULL = -1,        /* a required pointer is NULL                          */
+  ULY_ERR_SHAPE = -2,       /* a size is <= 0, S % P != 0, or a size overflows     */
+  ULY_ERR_HEADS = -3,       /* H % P, Hkv % P or Hq % Hkv is not 0                 */
+  ULY_ERR_UNSUPPORTED = -4, /* head_dim, element size or mask not supported        */
+  ULY_ERR_CAPACITY = -5,    /* an output or workspace buffer is too small          */
+  ULY_ERR_ALIGN = -6,       /* a pointer is not aligned as documented              */
+  ULY_ERR_HIP = -7          /* a HIP launch failed                                 */
+} uly_status;
+
+/* ------------------------------------------------------------------------
+ * Layout permutation of the all-to-all ("scatter heads, gather sequence",
+ * [accelerate#4209] PR body; the layouts are stated in its reply on the four
+ * all-to-all call sites; the differentiable all-to-all's backward "swaps
+ * scatter and gather", so the same two calls serve dO and dQ/dK/dV).
+ *
+ * ulysses_a2a_pack: seq_shards [P][B][S/P][H][D] -> head_shards [P][B][S][H/P][D]
+ *   head[c][b][r*S/P + s][h'][d] = seq[r][b][s][c*H/P + h'][d]
+ *   Rank r holds tokens [r*S/P, (r+1)*S/P) (shards are numbered by where they
+ *   sit in the sequence, [accelerate#4209] _prepare_sp_model comment); rank c
+ *   receives heads [c*H/P, (c+1)*H/P).
+ * ulysses_a2a_unpack: the inverse, head_shards -> seq_shards.
+ *
+ *   elem_bytes in {1, 2, 4, 8}; the copy is bit-exact for any dtype.
+ *   The two buffers must not overlap.  Pointers need elem_bytes alignment;
+ *   16-byte aligned buffers whose runs of H/P*D elements are a multiple of
+ *   16 bytes take the vectorised path.
+ *   Errors: ULY_ERR_NULL, ULY_ERR_SHAPE (a size <= 0, S % P), ULY_ERR_HEADS
+ *   (H % P), ULY_ERR_UNSUPPORTED (elem_bytes), ULY_ERR_ALIGN.
+ * ---------------------------------------------------------------------- */
+int ulysses_a2a_pack(const void* seq_shards, void* head_shards, int P, int B, int S, int H,
+                     int D, int elem_bytes, void* stream);
+int ulysses_a2a_unpack(const void* head_shards, void* seq_shards, int P, int B, int S, int H,
+                       int D, int elem_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * cu_seqlens / max_len from the gathered position_ids ([accelerate#4209],
+ * comment on the flash-attention kwargs: a padding-free collator's
+ * cu_seq_lens/max_length describe the local shard, so they are dropped and
+ * rebuilt from the position_ids gathered over the whole sequence; the gather
+ * happens once per forward, comment on the per-layer all-gather).
+ *
+ *   pos_shards  [P][B][S/P] integers (pos_bytes = 4: int32, 8: int64), the P
+ *               rank shards in rank order; their concatenation along the
+ *               sequence is the gathered position_ids [B][S].
+ *   A document starts at every flattened token t = b*S + i with i == 0 or
+ *   pos[b][i] == 0.  Outputs (device, int32):
+ *     cu_seqlens[0..n]  document starts in increasing order, then B*S
+ *     *n_seqs           n, the number of documents
+ *     *max_len          the longest document
+ *   cu_capacity is the number of int32 slots in cu_seqlens; it must be at
+ *   least B*S + 1 (the worst case, one token per document), so the host never
+ *   needs n.  Slots past n are left untouched.
+ *   Errors: ULY_ERR_NULL, ULY_ERR_SHAPE, ULY_ERR_UNSUPPORTED (pos_bytes),
+ *   ULY_ERR_CAPACITY (cu_capacity < B*S + 1), ULY_ERR_ALIGN (pos_shards not
+ *   pos_bytes-aligned, outputs not 4-byte aligned).
+ * ---------------------------------------------------------------------- */
+int ulysses_cu_seqlens_from_positions(const void* pos_shards, int pos_bytes, int P, int B, int S,
+                                      int32_t* cu_seqlens, int cu_capacity, int32_t* n_seqs,
+                                      int32_t* max_len, void* stream);
+
+/* ------------------------------------------------------------------------
+ * One rank's attention over the whole gathered sequence ([accelerate#4209]
+ * PR body: the model's own attention runs between the two all-to-alls, with
+ * flash attention, packing and sliding windows; [lca#135] test script for the
+ * flash_attn_func arguments causal and window_size=(left, right), -1 meaning
+ * unbounded).
+ *
+ * Layouts (bf16, contiguous, 16-byte aligned):
+ *   q, out, dout, dq      [B][S][hq][D]
+ *   k, v, dk, dv          [B][S][hkv][D]
+ *   lse                   fp32 [B][hq][S], natural-log log-sum-exp per row
+ * GQA: query head h uses KV head h / (hq/hkv) (contiguous groups; the rank
+ * holds hq = Hq/P query heads and hkv = Hkv/P KV heads, [arctic#45] feature
+ * list "modern MHA-variations").
+ * Documents: cu_seqlens (int32, n+1 entries over the B*S flattened tokens,
+ * as produced by ulysses_cu_seqlens_from_positions) with *n_seqs on the
+ * device; both NULL means one document per batch row.  Documents must not
+ * cross batch rows.
+ * Mask: key j is visible to query i iff both lie in the same document, and
+ *   (!causal || j <= i), (window_left < 0 || i - j <= window_left),
+ *   (window_right < 0 || j - i <= window_right).
+ * Sink ([accelerate#4209] findings: one logit per head, sliced to the heads
+ * the rank holds): fp32 [hq] (pass sink + r*hq for rank r; 4-byte
+ * alignment) or NULL.  It is an extra logit in every row's softmax
+ * denominator, not multiplied by softmax_scale, with no value vector.
+ *   O_i = sum_j softmax_j(scale * q_i . k_j) v_j,  LSE_i = ln(sum_j e^{s_ij} + e^{sink})
+ * Rows that see no key and have no sink get O = 0 and LSE = -inf.
+ * Supported: D in {64, 128}; window_left, window_right >= -1.
+ * Errors: ULY_ERR_NULL, ULY_ERR_SHAPE, ULY_ERR_HEADS (hq % hkv),
+ *   ULY_ERR_UNSUPPORTED (D, window < -1, cu_seqlens given without n_seqs),
+ *   ULY_ERR_ALIGN.
+ * ---------------------------------------------------------------------- */
+int ulysses_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                     const float* sink, const int32_t* cu_seqlens, const int32_t* n_seqs, int B,
+                     int S, int hq, int hkv, int D, float softmax_scale, int causal,
+                     int window_left, int window_right, void* stream);
+
+/* Bytes of device workspace ulysses_attn_bwd needs for these sizes. */
+size_t ulysses_attn_bwd_workspace_bytes(int B, int S, int hq, int hkv, int D);
+
+/* Backward of ulysses_attn_fwd for the loss sum(out * dout) ([accelerate#4209]:
+ * gradients compared against an unsharded run; [lca#135]: backward of the
+ * sharded attention).  Inputs as in the forward, plus out and lse from it.
+ *   dq [B][S][hq][D], dk/dv [B][S][hkv][D] (bf16, overwritten; dk/dv summed
+ *   over the query heads of each group), dsink fp32 [hq] (overwritten; must be
+ *   non-NULL exactly when sink is non-NULL):
+ *     dsink_h = -sum_i exp(sink_h - LSE_i) * sum_d dout_i,d out_i,d
+ *   workspace: device memory of at least ulysses_attn_bwd_workspace_bytes()
+ *   bytes, 256-byte aligned, owned by the caller; its contents on entry do
+ *   not matter and on return are unspecified.
+ * Errors: as ulysses_attn_fwd, plus ULY_ERR_CAPACITY (workspace too small)
+ *   and ULY_ERR_NULL (sink and dsink not both NULL or both set).
+ */
+int ulysses_attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                     const void* dout, const float* lse, const float* sink,
+                     const int32_t* cu_seqlens, const int32_t* n_seqs, void* dq, void* dk,
+                     void* dv, float* dsink, void* workspace, size_t workspace_bytes, int B, int S,
+                     int hq, int hkv, int D, float softmax_scale, int causal, int window_left,
+                     int window_right, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Per-kernel timing (a measurement aid, not part of the computation).
+ * ulysses_profile_start(max_launches): from now on every kernel the library
+ *   launches is bracketed by two HIP events recorded on the caller's stream,
+ *   for up to max_launches launches (later ones are not recorded).  Creates
+ *   the HIP events it needs (the only allocation in the library); resets
+ *   earlier records.
+ * ulysses_profile_stop(): stop recording.
+ * ulysses_profile_report(buf, buf_bytes): waits for the recorded events and
+ *   writes one line per kernel name, "name count total_ms min_ms max_ms",
+ *   into buf (NUL-terminated); returns the number of recorded launches, or a
+ *   negative uly_status (ULY_ERR_CAPACITY if buf is too small).
+ * Not thread-safe: profile from one host thread.
+ * ---------------------------------------------------------------------- */
+int ulysses_profile_start(int max_launches);
+int ulysses_profile_stop(void);
+int ulysses_profile_report(char* buf, size_t buf_bytes);
+
+/* Reason for the last non-zero status returned on this thread ("" if none). */
+const char* ulysses_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ULYSSES_H */

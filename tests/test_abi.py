@@ -1,0 +1,126 @@
+"""The C-ABI library loads, exports every symbol ``include/ulysses.h`` declares,
+and rejects bad arguments on the host before any launch (CPU only: no call
+here reaches a kernel)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import ulysses_sequence_attention_rank_amd as uly
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ulysses.h")
+
+OK, NULL, SHAPE, HEADS, UNSUP, CAP, ALIGN = 0, -1, -2, -3, -4, -5, -6
+A = 1 << 20  # a 256-byte-aligned dummy address; never dereferenced by a rejected call
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(uly.lib_path()):
+        from ulysses_sequence_attention_rank_amd import build
+        build.build()
+    return uly.load()
+
+
+def declared():
+    text = open(HEADER).read()
+    return set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(ulysses_\w+)\s*\(", text, re.M))
+
+
+def test_header_declares_the_boundary():
+    assert declared() == {"ulysses_a2a_pack", "ulysses_a2a_unpack",
+                          "ulysses_cu_seqlens_from_positions", "ulysses_attn_fwd",
+                          "ulysses_attn_bwd_workspace_bytes", "ulysses_attn_bwd",
+                          "ulysses_profile_start", "ulysses_profile_stop",
+                          "ulysses_profile_report", "ulysses_last_error"}
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", uly.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\b(ulysses_\w+)\b", out))
+    assert declared() <= exported
+    for name in declared():
+        assert hasattr(lib, name)
+
+
+def _p(x):
+    return ctypes.c_void_p(x)
+
+
+def test_pack_argument_errors(lib):
+    f = lib.ulysses_a2a_pack
+    assert f(None, _p(A), 2, 1, 8, 4, 4, 2, None) == NULL
+    assert f(_p(A), _p(2 * A), 0, 1, 8, 4, 4, 2, None) == SHAPE
+    assert f(_p(A), _p(2 * A), 3, 1, 8, 6, 4, 2, None) == SHAPE      # S % P
+    assert f(_p(A), _p(2 * A), 2, 1, 8, 3, 4, 2, None) == HEADS      # H % P
+    assert f(_p(A), _p(2 * A), 2, 1, 8, 4, 4, 3, None) == UNSUP      # elem_bytes
+    assert f(_p(A + 1), _p(2 * A), 2, 1, 8, 4, 4, 2, None) == ALIGN
+    assert f(_p(A), _p(A + 64), 2, 1, 8, 4, 4, 2, None) == UNSUP     # overlap
+    assert b"overlap" in lib.ulysses_last_error()
+    assert lib.ulysses_a2a_unpack(_p(A), _p(2 * A), 2, 1, 8, 3, 4, 2, None) == HEADS
+
+
+def test_segments_argument_errors(lib):
+    f = lib.ulysses_cu_seqlens_from_positions
+    n, m, cu = _p(3 * A), _p(3 * A + 4), _p(4 * A)
+    assert f(_p(A), 8, 2, 1, 8, cu, 8, n, m, None) == CAP           # needs B*S+1 = 9
+    assert f(_p(A), 2, 2, 1, 8, cu, 9, n, m, None) == UNSUP         # pos_bytes
+    assert f(_p(A), 8, 3, 1, 8, cu, 9, n, m, None) == SHAPE         # S % P
+    assert f(None, 8, 2, 1, 8, cu, 9, n, m, None) == NULL
+    assert f(_p(A + 4), 8, 2, 1, 8, cu, 9, n, m, None) == ALIGN
+
+
+def _fwd(lib, q=A, k=2 * A, v=3 * A, out=4 * A, lse=5 * A, sink=None, cu=None, n=None,
+         B=1, S=64, hq=4, hkv=2, D=128, scale=0.125, causal=1, wl=-1, wr=-1):
+    return lib.ulysses_attn_fwd(_p(q), _p(k), _p(v), _p(out), _p(lse),
+                                None if sink is None else _p(sink), None if cu is None else _p(cu),
+                                None if n is None else _p(n), B, S, hq, hkv, D,
+                                ctypes.c_float(scale), causal, wl, wr, None)
+
+
+def test_attn_fwd_argument_errors(lib):
+    assert _fwd(lib, hq=6, hkv=4) == HEADS
+    assert _fwd(lib, D=96) == UNSUP
+    assert _fwd(lib, wl=-2) == UNSUP
+    assert _fwd(lib, scale=0.0) == UNSUP
+    assert _fwd(lib, S=0) == SHAPE
+    assert _fwd(lib, q=A + 8) == ALIGN
+    assert _fwd(lib, cu=6 * A) == NULL       # cu_seqlens without n_seqs
+    assert _fwd(lib, q=0) == NULL
+    assert _fwd(lib, hq=6, hkv=4) == HEADS
+    assert b"query heads" in lib.ulysses_last_error()
+
+
+def test_attn_bwd_argument_errors(lib):
+    need = lib.ulysses_attn_bwd_workspace_bytes(1, 64, 4, 2, 128)
+    assert need >= 64 * 4 * 4
+
+    def bwd(ws_bytes=need, sink=None, dsink=None, hq=4):
+        return lib.ulysses_attn_bwd(
+            _p(A), _p(2 * A), _p(3 * A), _p(4 * A), _p(5 * A), _p(6 * A),
+            None if sink is None else _p(sink), None, None, _p(7 * A), _p(8 * A), _p(9 * A),
+            None if dsink is None else _p(dsink), _p(10 * A), ctypes.c_size_t(ws_bytes),
+            1, 64, hq, 2, 128, ctypes.c_float(0.125), 1, -1, -1, None)
+
+    assert bwd(ws_bytes=need - 1) == CAP
+    assert bwd(sink=11 * A) == NULL          # sink without dsink
+    assert bwd(dsink=11 * A) == NULL
+    assert bwd(hq=3) == HEADS
+
+
+def test_workspace_bytes_grow_with_rows(lib):
+    a = lib.ulysses_attn_bwd_workspace_bytes(1, 1024, 8, 1, 64)
+    b = lib.ulysses_attn_bwd_workspace_bytes(1, 2048, 8, 1, 64)
+    assert b > a > 0
+    assert lib.ulysses_attn_bwd_workspace_bytes(0, 1024, 8, 1, 64) == 0
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    q = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        uly.attn_fwd(q, q, q)

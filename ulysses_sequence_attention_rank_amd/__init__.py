@@ -1,0 +1,244 @@
+"""Per-rank Ulysses sequence-parallel hot path on MI355X (gfx950).
+
+Thin Python binding over ``libulysses.so`` (C ABI in ``include/ulysses.h``).
+Every step runs in the library's HIP kernels; torch only supplies device
+memory and the current stream.  There is no CPU fallback: if the library is
+missing or cannot be loaded, every call raises.
+
+Build it with ``python -m ulysses_sequence_attention_rank_amd.build`` (or
+``__graft_entry__.build()``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "UlyssesError", "lib_path", "load", "a2a_pack", "a2a_unpack", "a2a_pack_into",
+    "a2a_unpack_into", "cu_seqlens_from_positions", "attn_fwd", "attn_bwd",
+    "attn_bwd_workspace_bytes", "profile_start", "profile_stop", "profile_report",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libulysses.so")
+_lib = None
+
+_STATUS = {0: "ULY_OK", -1: "ULY_ERR_NULL", -2: "ULY_ERR_SHAPE", -3: "ULY_ERR_HEADS",
+           -4: "ULY_ERR_UNSUPPORTED", -5: "ULY_ERR_CAPACITY", -6: "ULY_ERR_ALIGN",
+           -7: "ULY_ERR_HIP"}
+
+EXPORTS = ("ulysses_a2a_pack", "ulysses_a2a_unpack", "ulysses_cu_seqlens_from_positions",
+           "ulysses_attn_fwd", "ulysses_attn_bwd_workspace_bytes", "ulysses_attn_bwd",
+           "ulysses_profile_start", "ulysses_profile_stop", "ulysses_profile_report",
+           "ulysses_last_error")
+
+
+class UlyssesError(RuntimeError):
+    def __init__(self, code: int, fn: str, detail: str):
+        self.code = code
+        super().__init__(f"{fn} failed: {_STATUS.get(code, code)}: {detail}")
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load ``libulysses.so`` (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build the HIP library first "
+                           "(python -m ulysses_sequence_attention_rank_amd.build)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.ulysses_a2a_pack.argtypes = [vp, vp] + [i32] * 6 + [vp]
+    lib.ulysses_a2a_unpack.argtypes = [vp, vp] + [i32] * 6 + [vp]
+    lib.ulysses_cu_seqlens_from_positions.argtypes = [vp, i32, i32, i32, i32, vp, i32, vp, vp, vp]
+    lib.ulysses_attn_fwd.argtypes = [vp] * 8 + [i32] * 5 + [f32] + [i32] * 3 + [vp]
+    lib.ulysses_attn_bwd_workspace_bytes.argtypes = [i32] * 5
+    lib.ulysses_attn_bwd_workspace_bytes.restype = sz
+    lib.ulysses_attn_bwd.argtypes = [vp] * 14 + [sz] + [i32] * 5 + [f32] + [i32] * 3 + [vp]
+    lib.ulysses_profile_start.argtypes = [i32]
+    lib.ulysses_profile_stop.argtypes = []
+    lib.ulysses_profile_report.argtypes = [ctypes.c_char_p, sz]
+    lib.ulysses_last_error.argtypes = []
+    lib.ulysses_last_error.restype = ctypes.c_char_p
+    for fn in EXPORTS:
+        if not hasattr(lib, fn):
+            raise RuntimeError(f"{_LIB_PATH} does not export {fn}")
+    _lib = lib
+    return lib
+
+
+def _check(rc: int, fn: str):
+    if rc != 0:
+        raise UlyssesError(rc, fn, load().ulysses_last_error().decode())
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+# -------------------------------------------------------------- profiling
+
+def profile_start(max_launches: int = 4096):
+    """Record a HIP event pair around every kernel launch from now on."""
+    _check(load().ulysses_profile_start(int(max_launches)), "ulysses_profile_start")
+
+
+def profile_stop():
+    _check(load().ulysses_profile_stop(), "ulysses_profile_stop")
+
+
+def profile_report() -> dict:
+    """{kernel: (count, total_ms, min_ms, max_ms)} of the launches recorded so far."""
+    buf = ctypes.create_string_buffer(1 << 16)
+    n = load().ulysses_profile_report(buf, len(buf))
+    if n < 0:
+        _check(n, "ulysses_profile_report")
+    out = {}
+    for line in buf.value.decode().splitlines():
+        name, cnt, tot, mn, mx = line.split()
+        out[name] = (int(cnt), float(tot), float(mn), float(mx))
+    return out
+
+
+# ------------------------------------------------------------------ layout
+
+def a2a_pack_into(seq: torch.Tensor, head: torch.Tensor, P: int):
+    """``[P, B, S/P, H, D]`` sequence shards -> ``head`` ``[P, B, S, H/P, D]``."""
+    _dev(seq, "seq"), _dev(head, "head")
+    Pp, B, Sl, H, D = seq.shape
+    if Pp != P or head.numel() != seq.numel() or head.dtype != seq.dtype:
+        raise ValueError("pack: shape/dtype mismatch")
+    _check(load().ulysses_a2a_pack(_p(seq), _p(head), P, B, Sl * P, H, D, seq.element_size(),
+                                   _stream(seq.device)), "ulysses_a2a_pack")
+    return head
+
+
+def a2a_pack(seq: torch.Tensor) -> torch.Tensor:
+    P, B, Sl, H, D = seq.shape
+    head = torch.empty((P, B, Sl * P, H // P, D), dtype=seq.dtype, device=seq.device)
+    return a2a_pack_into(seq, head, P)
+
+
+def a2a_unpack_into(head: torch.Tensor, seq: torch.Tensor, P: int):
+    """``[P, B, S, H/P, D]`` head shards -> ``seq`` ``[P, B, S/P, H, D]``."""
+    _dev(head, "head"), _dev(seq, "seq")
+    Pp, B, S, hp, D = head.shape
+    if Pp != P or head.numel() != seq.numel() or head.dtype != seq.dtype:
+        raise ValueError("unpack: shape/dtype mismatch")
+    _check(load().ulysses_a2a_unpack(_p(head), _p(seq), P, B, S, hp * P, D, head.element_size(),
+                                     _stream(head.device)), "ulysses_a2a_unpack")
+    return seq
+
+
+def a2a_unpack(head: torch.Tensor) -> torch.Tensor:
+    P, B, S, hp, D = head.shape
+    seq = torch.empty((P, B, S // P, hp * P, D), dtype=head.dtype, device=head.device)
+    return a2a_unpack_into(head, seq, P)
+
+
+# ---------------------------------------------------------------- segments
+
+def cu_seqlens_from_positions(pos_shards: torch.Tensor, cu: Optional[torch.Tensor] = None,
+                              n_seqs: Optional[torch.Tensor] = None,
+                              max_len: Optional[torch.Tensor] = None):
+    """``[P, B, S/P]`` int32/int64 position shards -> (cu int32 [B*S+1], n_seqs int32 [1],
+    max_len int32 [1]), all on the device (entries of cu past n_seqs are unspecified)."""
+    _dev(pos_shards, "pos_shards")
+    if pos_shards.dtype not in (torch.int32, torch.int64):
+        raise ValueError("positions must be int32 or int64")
+    P, B, Sl = pos_shards.shape
+    dev = pos_shards.device
+    if cu is None:
+        cu = torch.empty(B * Sl * P + 1, dtype=torch.int32, device=dev)
+    if n_seqs is None:
+        n_seqs = torch.empty(1, dtype=torch.int32, device=dev)
+    if max_len is None:
+        max_len = torch.empty(1, dtype=torch.int32, device=dev)
+    _check(load().ulysses_cu_seqlens_from_positions(
+        _p(pos_shards), pos_shards.element_size(), P, B, Sl * P, _p(cu), cu.numel(), _p(n_seqs),
+        _p(max_len), _stream(dev)), "ulysses_cu_seqlens_from_positions")
+    return cu, n_seqs, max_len
+
+
+# --------------------------------------------------------------- attention
+
+def _shapes(q, k):
+    B, S, hq, D = q.shape
+    Bk, Sk, hkv, Dk = k.shape
+    if (Bk, Sk, Dk) != (B, S, D):
+        raise ValueError("q and k/v shapes disagree")
+    return B, S, hq, hkv, D
+
+
+def attn_fwd(q, k, v, *, sink=None, cu_seqlens=None, n_seqs=None, causal=True, window_left=-1,
+             window_right=-1, softmax_scale=None, out=None, lse=None):
+    """One rank's attention: q ``[B, S, hq, D]``, k/v ``[B, S, hkv, D]`` bf16.
+    Returns (out bf16 ``[B, S, hq, D]``, lse fp32 ``[B, hq, S]``)."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dev(t, name, torch.bfloat16)
+    B, S, hq, hkv, D = _shapes(q, k)
+    if softmax_scale is None:
+        softmax_scale = D ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, hq, S), dtype=torch.float32, device=q.device)
+    if sink is not None:
+        _dev(sink, "sink", torch.float32)
+    _check(load().ulysses_attn_fwd(
+        _p(q), _p(k), _p(v), _p(out), _p(lse), _p(sink), _p(cu_seqlens), _p(n_seqs), B, S, hq, hkv,
+        D, float(softmax_scale), int(bool(causal)), int(window_left), int(window_right),
+        _stream(q.device)), "ulysses_attn_fwd")
+    return out, lse
+
+
+def attn_bwd_workspace_bytes(B, S, hq, hkv, D) -> int:
+    return int(load().ulysses_attn_bwd_workspace_bytes(B, S, hq, hkv, D))
+
+
+def attn_bwd(q, k, v, out, dout, lse, *, sink=None, cu_seqlens=None, n_seqs=None, causal=True,
+             window_left=-1, window_right=-1, softmax_scale=None, dq=None, dk=None, dv=None,
+             dsink=None, workspace=None):
+    """Backward of ``attn_fwd`` for the loss ``sum(out * dout)``.
+    Returns (dq, dk, dv, dsink or None)."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _dev(t, name, torch.bfloat16)
+    _dev(lse, "lse", torch.float32)
+    B, S, hq, hkv, D = _shapes(q, k)
+    if softmax_scale is None:
+        softmax_scale = D ** -0.5
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if sink is not None and dsink is None:
+        dsink = torch.empty_like(sink)
+    need = attn_bwd_workspace_bytes(B, S, hq, hkv, D)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(load().ulysses_attn_bwd(
+        _p(q), _p(k), _p(v), _p(out), _p(dout), _p(lse), _p(sink), _p(cu_seqlens), _p(n_seqs),
+        _p(dq), _p(dk), _p(dv), _p(dsink), _p(workspace), workspace.numel(), B, S, hq, hkv, D,
+        float(softmax_scale), int(bool(causal)), int(window_left), int(window_right),
+        _stream(q.device)), "ulysses_attn_bwd")
+    return dq, dk, dv, (dsink if sink is not None else None)

@@ -1,0 +1,306 @@
+// C ABI of the per-rank Ulysses hot path: argument checks, workspace layout
+// and kernel dispatch.  Declared (with the meaning of every argument) in
+// include/ulysses.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/ulysses.h"
+#include "attn_common.hpp"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return ULY_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(ULY_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+constexpr int64_t kMaxI32 = 2147483647;
+
+int check_permute(const void* src, const void* dst, int P, int B, int S, int H, int D, int eb) {
+  if (!src || !dst) return fail(ULY_ERR_NULL, "NULL tensor pointer");
+  if (P <= 0 || B <= 0 || S <= 0 || H <= 0 || D <= 0)
+    return fail(ULY_ERR_SHAPE, "sizes must be positive (P=%d B=%d S=%d H=%d D=%d)", P, B, S, H, D);
+  if (S % P) return fail(ULY_ERR_SHAPE, "S=%d is not divisible by P=%d", S, P);
+  if (H % P) return fail(ULY_ERR_HEADS, "H=%d heads are not divisible by P=%d ranks", H, P);
+  if (eb != 1 && eb != 2 && eb != 4 && eb != 8)
+    return fail(ULY_ERR_UNSUPPORTED, "elem_bytes=%d not in {1,2,4,8}", eb);
+  const int64_t elems = (int64_t)B * S * H * D;
+  if (elems >= kMaxI32 || (int64_t)P * B * S >= kMaxI32)
+    return fail(ULY_ERR_SHAPE, "tensor of %lld elements exceeds 2^31 - 1", (long long)elems);
+  if (!aligned(src, eb) || !aligned(dst, eb))
+    return fail(ULY_ERR_ALIGN, "pointers must be aligned to elem_bytes=%d", eb);
+  const uintptr_t a0 = (uintptr_t)src, a1 = a0 + elems * eb, b0 = (uintptr_t)dst, b1 = b0 + elems * eb;
+  if (a0 < b1 && b0 < a1) return fail(ULY_ERR_UNSUPPORTED, "source and destination overlap");
+  return ok();
+}
+
+int check_attn(const void* q, const void* k, const void* v, const int32_t* cu, const int32_t* n_seqs,
+               int B, int S, int hq, int hkv, int D, float scale, int wl, int wr) {
+  if (!q || !k || !v) return fail(ULY_ERR_NULL, "NULL q/k/v");
+  if (cu && !n_seqs) return fail(ULY_ERR_NULL, "cu_seqlens given without n_seqs");
+  if (B <= 0 || S <= 0 || hq <= 0 || hkv <= 0)
+    return fail(ULY_ERR_SHAPE, "sizes must be positive (B=%d S=%d hq=%d hkv=%d)", B, S, hq, hkv);
+  if (hq % hkv) return fail(ULY_ERR_HEADS, "hq=%d query heads not divisible by hkv=%d", hq, hkv);
+  if (D != 64 && D != 128) return fail(ULY_ERR_UNSUPPORTED, "head_dim D=%d not in {64,128}", D);
+  if (wl < -1 || wr < -1)
+    return fail(ULY_ERR_UNSUPPORTED, "window (%d,%d): values below -1 are not a window", wl, wr);
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(ULY_ERR_UNSUPPORTED, "softmax_scale must be finite and > 0");
+  if ((int64_t)B * S * hq * D >= kMaxI32 * 8ll || (int64_t)B * S * hq >= kMaxI32)
+    return fail(ULY_ERR_SHAPE, "problem too large for 32-bit row indices");
+  return ok();
+}
+
+uly::AttnArgs make_args(const void* q, const void* k, const void* v, const float* sink,
+                        const int32_t* cu, const int32_t* n_seqs, int B, int S, int hq, int hkv,
+                        float scale, int causal, int wl, int wr) {
+  uly::AttnArgs a = {};
+  a.q = (const __bf16*)q;
+  a.k = (const __bf16*)k;
+  a.v = (const __bf16*)v;
+  a.sink = sink;
+  a.cu = cu;
+  a.n_seqs = cu ? n_seqs : nullptr;
+  a.B = B;
+  a.S = S;
+  a.T = B * S;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.G = hq / hkv;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.causal = causal ? 1 : 0;
+  a.wl = wl;
+  a.wr = wr;
+  return a;
+}
+
+constexpr int kDsinkParts = 64;
+
+// ---- optional per-kernel timing: a HIP event before and after each launch
+struct Prof {
+  bool on = false;
+  bool open = false;  // a start event is recorded, its stop is not
+  size_t n = 0;       // events recorded
+  std::vector<hipEvent_t> ev;
+  std::vector<const char*> name;  // one per launch
+};
+Prof g_prof;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+namespace uly {
+void prof_mark(const char* name, hipStream_t st) {
+  Prof& p = g_prof;
+  if (!p.on) return;
+  if (name != nullptr) {
+    if (p.n + 2 > p.ev.size()) return;  // full: later launches are not recorded
+    p.name[p.n / 2] = name;
+    p.open = hipEventRecord(p.ev[p.n], st) == hipSuccess;
+  } else if (p.open) {
+    if (hipEventRecord(p.ev[p.n + 1], st) == hipSuccess) p.n += 2;
+    p.open = false;
+  }
+}
+}  // namespace uly
+
+extern "C" {
+
+int ulysses_profile_start(int max_launches) {
+  if (max_launches <= 0) return fail(ULY_ERR_SHAPE, "max_launches must be positive");
+  Prof& p = g_prof;
+  const size_t need = 2 * (size_t)max_launches;
+  while (p.ev.size() < need) {
+    hipEvent_t e;
+    hipError_t err = hipEventCreate(&e);
+    if (err != hipSuccess) return hip_status(err, "hipEventCreate");
+    p.ev.push_back(e);
+  }
+  p.name.assign(p.ev.size() / 2, nullptr);
+  p.n = 0;
+  p.open = false;
+  p.on = true;
+  return ok();
+}
+
+int ulysses_profile_stop(void) {
+  g_prof.on = false;
+  return ok();
+}
+
+int ulysses_profile_report(char* buf, size_t buf_bytes) {
+  Prof& p = g_prof;
+  if (!buf || buf_bytes == 0) return fail(ULY_ERR_NULL, "NULL report buffer");
+  struct Agg {
+    std::string name;
+    int count;
+    double total_ms, min_ms, max_ms;
+  };
+  std::vector<Agg> agg;
+  for (size_t i = 0; i + 1 < p.n; i += 2) {
+    hipError_t err = hipEventSynchronize(p.ev[i + 1]);
+    if (err != hipSuccess) return hip_status(err, "hipEventSynchronize");
+    float ms = 0.f;
+    err = hipEventElapsedTime(&ms, p.ev[i], p.ev[i + 1]);
+    if (err != hipSuccess) return hip_status(err, "hipEventElapsedTime");
+    const char* nm = p.name[i / 2];
+    Agg* a = nullptr;
+    for (auto& x : agg)
+      if (x.name == nm) a = &x;
+    if (!a) {
+      agg.push_back({nm, 0, 0.0, 1e30, 0.0});
+      a = &agg.back();
+    }
+    a->count++;
+    a->total_ms += ms;
+    a->min_ms = ms < a->min_ms ? ms : a->min_ms;
+    a->max_ms = ms > a->max_ms ? ms : a->max_ms;
+  }
+  std::string out;
+  char line[256];
+  for (auto& x : agg) {
+    snprintf(line, sizeof(line), "%s %d %.6f %.6f %.6f\n", x.name.c_str(), x.count, x.total_ms,
+             x.min_ms, x.max_ms);
+    out += line;
+  }
+  if (out.size() + 1 > buf_bytes) return fail(ULY_ERR_CAPACITY, "report needs %zu bytes", out.size() + 1);
+  memcpy(buf, out.c_str(), out.size() + 1);
+  ok();
+  return (int)(p.n / 2);
+}
+
+int ulysses_a2a_pack(const void* seq_shards, void* head_shards, int P, int B, int S, int H, int D,
+                     int elem_bytes, void* stream) {
+  int rc = check_permute(seq_shards, head_shards, P, B, S, H, D, elem_bytes);
+  if (rc) return rc;
+  return hip_status(uly::permute_launch(true, seq_shards, head_shards, P, B, S, H, D, elem_bytes,
+                                        (hipStream_t)stream),
+                    "ulysses_a2a_pack launch");
+}
+
+int ulysses_a2a_unpack(const void* head_shards, void* seq_shards, int P, int B, int S, int H,
+                       int D, int elem_bytes, void* stream) {
+  int rc = check_permute(head_shards, seq_shards, P, B, S, H, D, elem_bytes);
+  if (rc) return rc;
+  return hip_status(uly::permute_launch(false, head_shards, seq_shards, P, B, S, H, D, elem_bytes,
+                                        (hipStream_t)stream),
+                    "ulysses_a2a_unpack launch");
+}
+
+int ulysses_cu_seqlens_from_positions(const void* pos_shards, int pos_bytes, int P, int B, int S,
+                                      int32_t* cu_seqlens, int cu_capacity, int32_t* n_seqs,
+                                      int32_t* max_len, void* stream) {
+  if (!pos_shards || !cu_seqlens || !n_seqs || !max_len) return fail(ULY_ERR_NULL, "NULL pointer");
+  if (P <= 0 || B <= 0 || S <= 0)
+    return fail(ULY_ERR_SHAPE, "sizes must be positive (P=%d B=%d S=%d)", P, B, S);
+  if (S % P) return fail(ULY_ERR_SHAPE, "S=%d is not divisible by P=%d", S, P);
+  if ((int64_t)B * S >= kMaxI32) return fail(ULY_ERR_SHAPE, "B*S exceeds 2^31 - 2");
+  if (pos_bytes != 4 && pos_bytes != 8)
+    return fail(ULY_ERR_UNSUPPORTED, "pos_bytes=%d not in {4,8}", pos_bytes);
+  if ((int64_t)cu_capacity < (int64_t)B * S + 1)
+    return fail(ULY_ERR_CAPACITY, "cu_capacity=%d < B*S+1=%lld", cu_capacity,
+                (long long)((int64_t)B * S + 1));
+  if (!aligned(pos_shards, pos_bytes) || !aligned(cu_seqlens, 4) || !aligned(n_seqs, 4) ||
+      !aligned(max_len, 4))
+    return fail(ULY_ERR_ALIGN, "misaligned pointer");
+  return hip_status(uly::segments_launch(pos_shards, pos_bytes, P, B, S, cu_seqlens, n_seqs,
+                                         max_len, (hipStream_t)stream),
+                    "ulysses_cu_seqlens_from_positions launch");
+}
+
+int ulysses_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                     const float* sink, const int32_t* cu_seqlens, const int32_t* n_seqs, int B,
+                     int S, int hq, int hkv, int D, float softmax_scale, int causal,
+                     int window_left, int window_right, void* stream) {
+  int rc = check_attn(q, k, v, cu_seqlens, n_seqs, B, S, hq, hkv, D, softmax_scale, window_left,
+                      window_right);
+  if (rc) return rc;
+  if (!out || !lse) return fail(ULY_ERR_NULL, "NULL out/lse");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+      !aligned(lse, 4) || !aligned(sink, 4) || !aligned(cu_seqlens, 4) || !aligned(n_seqs, 4))
+    return fail(ULY_ERR_ALIGN, "q/k/v/out need 16-byte alignment, lse/sink/cu 4-byte");
+  uly::AttnArgs a = make_args(q, k, v, sink, cu_seqlens, n_seqs, B, S, hq, hkv, softmax_scale,
+                              causal, window_left, window_right);
+  a.out = (__bf16*)out;
+  a.lse = lse;
+  return hip_status(uly::attn_fwd_launch(a, D, (hipStream_t)stream), "ulysses_attn_fwd launch");
+}
+
+size_t ulysses_attn_bwd_workspace_bytes(int B, int S, int hq, int hkv, int D) {
+  (void)hkv;
+  (void)D;
+  if (B <= 0 || S <= 0 || hq <= 0) return 0;
+  // delta, sum_j P dP (both [B][hq][S] fp32), dsink partial sums [hq][parts]
+  return 2 * align256((size_t)B * S * hq * sizeof(float)) +
+         align256((size_t)hq * kDsinkParts * sizeof(float));
+}
+
+int ulysses_attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                     const void* dout, const float* lse, const float* sink,
+                     const int32_t* cu_seqlens, const int32_t* n_seqs, void* dq, void* dk,
+                     void* dv, float* dsink, void* workspace, size_t workspace_bytes, int B, int S,
+                     int hq, int hkv, int D, float softmax_scale, int causal, int window_left,
+                     int window_right, void* stream) {
+  int rc = check_attn(q, k, v, cu_seqlens, n_seqs, B, S, hq, hkv, D, softmax_scale, window_left,
+                      window_right);
+  if (rc) return rc;
+  if (!out || !dout || !lse || !dq || !dk || !dv || !workspace)
+    return fail(ULY_ERR_NULL, "NULL out/dout/lse/dq/dk/dv/workspace");
+  if ((sink == nullptr) != (dsink == nullptr))
+    return fail(ULY_ERR_NULL, "sink and dsink must both be NULL or both be set");
+  const size_t need = ulysses_attn_bwd_workspace_bytes(B, S, hq, hkv, D);
+  if (workspace_bytes < need)
+    return fail(ULY_ERR_CAPACITY, "workspace of %zu bytes < %zu needed", workspace_bytes, need);
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(lse, 4) || !aligned(sink, 4) || !aligned(dsink, 4) || !aligned(workspace, 256) ||
+      !aligned(cu_seqlens, 4) || !aligned(n_seqs, 4))
+    return fail(ULY_ERR_ALIGN, "bf16 tensors need 16-byte alignment, workspace 256-byte");
+  uly::AttnArgs a = make_args(q, k, v, sink, cu_seqlens, n_seqs, B, S, hq, hkv, softmax_scale,
+                              causal, window_left, window_right);
+  a.o = (const __bf16*)out;
+  a.dout = (const __bf16*)dout;
+  a.lse = const_cast<float*>(lse);
+  a.out = (__bf16*)dq;
+  a.dk = (__bf16*)dk;
+  a.dv = (__bf16*)dv;
+  a.dsink = dsink;
+  char* ws = (char*)workspace;
+  const size_t rows = align256((size_t)B * S * hq * sizeof(float));
+  a.delta = (float*)ws;
+  a.pdp = (float*)(ws + rows);
+  a.dsink_part = (float*)(ws + 2 * rows);
+  a.n_part = kDsinkParts;
+  return hip_status(uly::attn_bwd_launch(a, D, (hipStream_t)stream), "ulysses_attn_bwd launch");
+}
+
+const char* ulysses_last_error(void) { return g_err; }
+
+}  // extern "C"

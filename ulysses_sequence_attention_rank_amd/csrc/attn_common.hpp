@@ -1,0 +1,257 @@
+// Device helpers shared by the attention kernels (gfx950, wave64, bf16 MFMA).
+//
+// Matrix-core conventions (v_mfma_f32_32x32x16_bf16, lane l, half hf = l / 32):
+//   A operand (32 x 16, M x K): lane holds A[l % 32][8 hf .. 8 hf + 7]
+//   B operand (16 x 32, K x N): lane holds B[8 hf .. 8 hf + 7][l % 32]
+//   C (32 x 32 fp32, 16 values): value 4 i + j is C[8 i + 4 hf + j][l % 32]
+// so after a product the lane owns one COLUMN.  Attention keeps the query in
+// that column (S^T = K Q^T): a lane then owns one query row's scores, its
+// running max/sum are per-lane scalars, and the only cross-lane step is one
+// swap between the two 32-lane halves.  The 16 scores a lane owns in a
+// 32-key block serve directly as the B operand of the next product that
+// contracts over keys, if the A operand reads its keys in the same order:
+// operand slot e of half hf  <->  key 4 hf + e (e < 4), 8 + 4 hf + (e - 4) (e >= 4)
+// within each 16-key step.  The "transposed" LDS tiles below store rows in
+// groups of four so that this A operand is two 8-byte reads.
+#pragma once
+
+#include "common.hpp"
+
+namespace uly {
+
+constexpr int kBK = 64;  // keys (or queries) per LDS tile
+
+struct AttnArgs {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  const __bf16* o;
+  const __bf16* dout;
+  __bf16* out;   // fwd: O; bwd dq kernel: dQ
+  __bf16* dk;
+  __bf16* dv;
+  float* lse;    // fwd output / bwd input, [B][hq][S]
+  float* delta;  // bwd: rowsum(dO * O) with the bf16 O, [B][hq][S]
+  float* pdp;    // bwd: sum_j P_ij dP_ij = dO_i . O_i with the exact O, [B][hq][S]
+  const float* sink;
+  float* dsink_part;  // [hq][n_part]
+  float* dsink;
+  const int32_t* cu;
+  const int32_t* n_seqs;
+  int B, S, T, hq, hkv, G;
+  float scale;       // softmax scale
+  float scale_log2;  // softmax scale * log2(e)
+  int causal, wl, wr;
+  int n_tiles;       // query tiles (fwd, dq) or key tiles (dkdv)
+  int n_part;
+};
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Values of the partner lane (l ^ 32) combined with this lane's: both
+// halves of v_permlane32_swap(v, v) together hold {v[l], v[l ^ 32]}.
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Document [start, end) of flattened token t.
+__device__ __forceinline__ void doc_bounds(const AttnArgs& a, int t, int& start, int& end) {
+  if (a.cu == nullptr) {
+    start = (t / a.S) * a.S;
+    end = start + a.S;
+    return;
+  }
+  int lo = 0, hi = max(*a.n_seqs, 1);  // largest d in [0, n) with cu[d] <= t
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.cu[mid] <= t) lo = mid; else hi = mid;
+  }
+  start = a.cu[lo];
+  end = a.cu[lo + 1];
+}
+
+// Keys visible to query i form the interval [klo, khi).
+__device__ __forceinline__ void key_interval(const AttnArgs& a, int i, int& klo, int& khi) {
+  int ds, de;
+  doc_bounds(a, i, ds, de);
+  klo = ds;
+  khi = de;
+  if (a.causal) khi = min(khi, i + 1);
+  if (a.wl >= 0) klo = max(klo, i - a.wl);
+  if (a.wr >= 0) khi = min(khi, i + a.wr + 1);
+  if (khi < klo) khi = klo;
+}
+
+// Queries that see key j form the interval [qlo, qhi).
+__device__ __forceinline__ void query_interval(const AttnArgs& a, int j, int& qlo, int& qhi) {
+  int ds, de;
+  doc_bounds(a, j, ds, de);
+  qlo = ds;
+  qhi = de;
+  if (a.causal) qlo = max(qlo, j);
+  if (a.wl >= 0) qhi = min(qhi, j + a.wl + 1);
+  if (a.wr >= 0) qlo = max(qlo, j - a.wr);
+  if (qhi < qlo) qhi = qlo;
+}
+
+__device__ __forceinline__ int lse_index(const AttnArgs& a, int t, int h) {
+  const int b = t / a.S;
+  return (b * a.hq + h) * a.S + (t - b * a.S);
+}
+
+// Work decode shared by the query-tile kernels.  Query tiles are ordered last
+// first (causal tiles near the end see the most keys); the G query heads of a
+// KV head that work on the same tile are put on one XCD (L2 shares their K/V).
+__device__ __forceinline__ bool decode_qtile(const AttnArgs& a, int& qt, int& h) {
+  const int L = blockIdx.x;
+  const int xcd = L % kXcds, slot = L / kXcds;
+  const int grp = (slot / a.G) * kXcds + xcd, member = slot % a.G;
+  if (grp >= a.n_tiles * a.hkv) return false;
+  qt = a.n_tiles - 1 - grp / a.hkv;
+  h = (grp % a.hkv) * a.G + member;
+  return true;
+}
+
+// ---------------------------------------------------------------- LDS tiles
+//
+// Natural tile: kBK rows x D, row stride D + 8 elements (16 bytes of padding
+// keep the 16-byte A-operand reads of 32 consecutive rows on distinct banks).
+// Transposed tile: rows in groups of four, [kBK/4][D][4], with the 16-byte
+// slot (d/2) XOR-swizzled by (d/16) % 8 so that both the staging writes and
+// the operand reads hit distinct banks.
+
+template <int D>
+struct Tile {
+  static constexpr int kNatStride = D + 8;
+  static constexpr int kNatElems = kBK * kNatStride;
+  static constexpr int kTrElems = kBK * D;
+
+  __device__ static __forceinline__ int tr_slot(int d2) { return d2 ^ ((d2 >> 3) & 7); }
+
+  // byte offset of 8-byte (4 x bf16) slot [group g][d] in a transposed tile
+  __device__ static __forceinline__ int tr_off(int g, int d) {
+    return g * (D * 8) + tr_slot(d >> 1) * 16 + (d & 1) * 8;
+  }
+};
+
+// Staging of one kBK x D tile from global (row stride `ld` elements) through
+// registers into LDS, in both layouts.  Rows at or past `row_end` are zero.
+template <int D, int NT>
+struct TileLoader {
+  static constexpr int kChunks = kBK * D / 8;                // 16-byte chunks in a tile
+  static constexpr int kNat = (kChunks + NT - 1) / NT;      // per thread
+  static constexpr int kUnits = (kBK / 4) * (D / 8);         // 4 rows x 8 columns
+  static constexpr int kTr = (kUnits + NT - 1) / NT;
+
+  u32x4 nat[kNat];
+  u32x4 tr[kTr][4];
+
+  __device__ __forceinline__ void load_nat(const __bf16* base, int ld, int row0, int row_end, int tid) {
+#pragma unroll
+    for (int c = 0; c < kNat; ++c) {
+      const int ch = tid + c * NT;
+      const int r = ch / (D / 8), col = (ch % (D / 8)) * 8;
+      u32x4 x = {0, 0, 0, 0};
+      if ((kChunks % NT == 0 || ch < kChunks) && row0 + r < row_end)
+        x = *reinterpret_cast<const u32x4*>(base + (int64_t)(row0 + r) * ld + col);
+      nat[c] = x;
+    }
+  }
+  __device__ __forceinline__ void store_nat(__bf16* lds, int tid) const {
+#pragma unroll
+    for (int c = 0; c < kNat; ++c) {
+      const int ch = tid + c * NT;
+      if (kChunks % NT == 0 || ch < kChunks) {
+        const int r = ch / (D / 8), col = (ch % (D / 8)) * 8;
+        *reinterpret_cast<u32x4*>(lds + r * Tile<D>::kNatStride + col) = nat[c];
+      }
+    }
+  }
+  __device__ __forceinline__ void load_tr(const __bf16* base, int ld, int row0, int row_end, int tid) {
+#pragma unroll
+    for (int c = 0; c < kTr; ++c) {
+      const int u = tid + c * NT;
+      const int g = u / (D / 8), col = (u % (D / 8)) * 8;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        u32x4 x = {0, 0, 0, 0};
+        if ((kUnits % NT == 0 || u < kUnits) && row0 + 4 * g + r < row_end)
+          x = *reinterpret_cast<const u32x4*>(base + (int64_t)(row0 + 4 * g + r) * ld + col);
+        tr[c][r] = x;
+      }
+    }
+  }
+  // 4 rows x 8 columns -> 8 columns x 4 rows, two columns per 16-byte store
+  __device__ __forceinline__ void store_tr(__bf16* lds, int tid) const {
+    char* base = reinterpret_cast<char*>(lds);
+#pragma unroll
+    for (int c = 0; c < kTr; ++c) {
+      const int u = tid + c * NT;
+      if (kUnits % NT == 0 || u < kUnits) {
+        const int g = u / (D / 8), col = (u % (D / 8)) * 8;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {  // word w holds columns col+2w (low) and col+2w+1 (high)
+          u32x4 o;
+          o[0] = __builtin_amdgcn_perm(tr[c][1][w], tr[c][0][w], 0x05040100u);
+          o[1] = __builtin_amdgcn_perm(tr[c][3][w], tr[c][2][w], 0x05040100u);
+          o[2] = __builtin_amdgcn_perm(tr[c][1][w], tr[c][0][w], 0x07060302u);
+          o[3] = __builtin_amdgcn_perm(tr[c][3][w], tr[c][2][w], 0x07060302u);
+          const int d2 = (col >> 1) + w;
+          *reinterpret_cast<u32x4*>(base + g * (D * 8) + Tile<D>::tr_slot(d2) * 16) = o;
+        }
+      }
+    }
+  }
+};
+
+// A operand from a natural tile: rows row0 + (l % 32), columns 16 s + 8 hf ..
+template <int D>
+__device__ __forceinline__ bf16x8 nat_frag(const __bf16* lds, int row0, int s, int lane) {
+  const u32x4 x = *reinterpret_cast<const u32x4*>(
+      lds + (row0 + (lane & 31)) * Tile<D>::kNatStride + 16 * s + 8 * (lane >> 5));
+  return __builtin_bit_cast(bf16x8, x);
+}
+
+// A operand from a transposed tile for the 16-row step starting at row r0
+// (a multiple of 16): column d = d0 + (l % 32), rows in the slot order above.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag(const __bf16* lds, int r0, int d0, int lane) {
+  const char* base = reinterpret_cast<const char*>(lds);
+  const int g = (r0 >> 2) + (lane >> 5);
+  const int d = d0 + (lane & 31);
+  const u32x2 lo = *reinterpret_cast<const u32x2*>(base + Tile<D>::tr_off(g, d));
+  const u32x2 hi = *reinterpret_cast<const u32x2*>(base + Tile<D>::tr_off(g + 2, d));
+  const u32x4 x = {lo[0], lo[1], hi[0], hi[1]};
+  return __builtin_bit_cast(bf16x8, x);
+}
+
+// B operand held in registers: row `row` (or zeros), columns 16 s + 8 hf ..
+template <int D>
+__device__ __forceinline__ void load_row_frags(bf16x8 (&f)[D / 16], const __bf16* rowp, bool valid, int lane) {
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    u32x4 x = {0, 0, 0, 0};
+    if (valid) x = *reinterpret_cast<const u32x4*>(rowp + 16 * s + 8 * (lane >> 5));
+    f[s] = __builtin_bit_cast(bf16x8, x);
+  }
+}
+
+// Eight accumulator values (C rows 8(2ii) + 4hf + j and 8(2ii+1) + 4hf + j)
+// as the bf16 operand of the next product: exactly slots e = 0..7 above.
+__device__ __forceinline__ bf16x8 acc_frag(const f32x16& c, int ii) {
+  u32x4 x;
+  x[0] = pack_bf16x2(c[8 * ii + 0], c[8 * ii + 1]);
+  x[1] = pack_bf16x2(c[8 * ii + 2], c[8 * ii + 3]);
+  x[2] = pack_bf16x2(c[8 * ii + 4], c[8 * ii + 5]);
+  x[3] = pack_bf16x2(c[8 * ii + 6], c[8 * ii + 7]);
+  return __builtin_bit_cast(bf16x8, x);
+}
+
+}  // namespace uly

@@ -1,0 +1,141 @@
+"""One simulated Ulysses step on one GPU: P ranks held in memory.
+
+The step follows the accelerate PR "Add an FSDP2-native Ulysses sequence
+parallelism backend": the position_ids are gathered once and cu_seqlens /
+max_len rebuilt from them; Q, K, V go from sequence shards to head shards
+("scatter heads, gather sequence"); every rank runs attention over the whole
+sequence for its heads with its slice of the sink logits; the output goes
+back to sequence shards.  Backward mirrors it: dO is packed, each rank runs
+the attention backward, dQ/dK/dV are unpacked ("swap scatter and gather").
+The exchange itself is a permutation here (one GPU); every step is a call
+into the HIP library.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional, Sequence
+
+import torch
+
+from . import (a2a_pack_into, a2a_unpack_into, attn_bwd, attn_bwd_workspace_bytes, attn_fwd,
+               cu_seqlens_from_positions)
+
+
+@dataclasses.dataclass
+class StepBuffers:
+    """Device buffers of one step; allocated once, reused by every call."""
+    P: int
+    B: int
+    S: int
+    Hq: int
+    Hkv: int
+    D: int
+    q_seq: torch.Tensor
+    k_seq: torch.Tensor
+    v_seq: torch.Tensor
+    dout_seq: torch.Tensor
+    pos_seq: torch.Tensor
+    sink: Optional[torch.Tensor]
+    # head-sharded (per rank) tensors
+    q_head: torch.Tensor = None
+    k_head: torch.Tensor = None
+    v_head: torch.Tensor = None
+    o_head: torch.Tensor = None
+    do_head: torch.Tensor = None
+    dq_head: torch.Tensor = None
+    dk_head: torch.Tensor = None
+    dv_head: torch.Tensor = None
+    lse: torch.Tensor = None
+    dsink: Optional[torch.Tensor] = None
+    o_seq: torch.Tensor = None
+    dq_seq: torch.Tensor = None
+    dk_seq: torch.Tensor = None
+    dv_seq: torch.Tensor = None
+    cu: torch.Tensor = None
+    n_seqs: torch.Tensor = None
+    max_len: torch.Tensor = None
+    workspace: torch.Tensor = None
+
+    @property
+    def hq(self):
+        return self.Hq // self.P
+
+    @property
+    def hkv(self):
+        return self.Hkv // self.P
+
+
+def allocate(q_seq, k_seq, v_seq, dout_seq, pos_seq, sink) -> StepBuffers:
+    """Wrap device sequence shards ``[P, B, S/P, H, D]`` and allocate the rest."""
+    P, B, Sl, Hq, D = q_seq.shape
+    Hkv = k_seq.shape[3]
+    S = P * Sl
+    dev = q_seq.device
+    bf = torch.bfloat16
+    b = StepBuffers(P, B, S, Hq, Hkv, D, q_seq, k_seq, v_seq, dout_seq, pos_seq, sink)
+    hq, hkv = Hq // P, Hkv // P
+    b.q_head = torch.empty((P, B, S, hq, D), dtype=bf, device=dev)
+    b.k_head = torch.empty((P, B, S, hkv, D), dtype=bf, device=dev)
+    b.v_head = torch.empty_like(b.k_head)
+    b.o_head = torch.empty_like(b.q_head)
+    b.do_head = torch.empty_like(b.q_head)
+    b.dq_head = torch.empty_like(b.q_head)
+    b.dk_head = torch.empty_like(b.k_head)
+    b.dv_head = torch.empty_like(b.k_head)
+    b.lse = torch.empty((P, B, hq, S), dtype=torch.float32, device=dev)
+    b.dsink = torch.empty(Hq, dtype=torch.float32, device=dev) if sink is not None else None
+    b.o_seq = torch.empty_like(q_seq)
+    b.dq_seq = torch.empty_like(q_seq)
+    b.dk_seq = torch.empty_like(k_seq)
+    b.dv_seq = torch.empty_like(v_seq)
+    b.cu = torch.empty(B * S + 1, dtype=torch.int32, device=dev)
+    b.n_seqs = torch.empty(1, dtype=torch.int32, device=dev)
+    b.max_len = torch.empty(1, dtype=torch.int32, device=dev)
+    b.workspace = torch.empty(attn_bwd_workspace_bytes(B, S, hq, hkv, D), dtype=torch.uint8,
+                              device=dev)
+    return b
+
+
+def forward(b: StepBuffers, *, causal: bool, window_left: int = -1, window_right: int = -1,
+            ranks: Optional[Sequence[int]] = None, softmax_scale: Optional[float] = None):
+    """Gather positions -> cu_seqlens, pack Q/K/V, attention per rank, unpack O."""
+    ranks = range(b.P) if ranks is None else ranks
+    cu_seqlens_from_positions(b.pos_seq, b.cu, b.n_seqs, b.max_len)
+    a2a_pack_into(b.q_seq, b.q_head, b.P)
+    a2a_pack_into(b.k_seq, b.k_head, b.P)
+    a2a_pack_into(b.v_seq, b.v_head, b.P)
+    hq = b.hq
+    for r in ranks:
+        sk = None if b.sink is None else b.sink[r * hq:(r + 1) * hq]
+        attn_fwd(b.q_head[r], b.k_head[r], b.v_head[r], sink=sk, cu_seqlens=b.cu,
+                 n_seqs=b.n_seqs, causal=causal, window_left=window_left,
+                 window_right=window_right, softmax_scale=softmax_scale, out=b.o_head[r],
+                 lse=b.lse[r])
+    a2a_unpack_into(b.o_head, b.o_seq, b.P)
+
+
+def backward(b: StepBuffers, *, causal: bool, window_left: int = -1, window_right: int = -1,
+             ranks: Optional[Sequence[int]] = None, softmax_scale: Optional[float] = None):
+    """Pack dO, attention backward per rank, unpack dQ/dK/dV."""
+    ranks = range(b.P) if ranks is None else ranks
+    a2a_pack_into(b.dout_seq, b.do_head, b.P)
+    hq = b.hq
+    for r in ranks:
+        sk = None if b.sink is None else b.sink[r * hq:(r + 1) * hq]
+        ds = None if b.dsink is None else b.dsink[r * hq:(r + 1) * hq]
+        attn_bwd(b.q_head[r], b.k_head[r], b.v_head[r], b.o_head[r], b.do_head[r], b.lse[r],
+                 sink=sk, cu_seqlens=b.cu, n_seqs=b.n_seqs, causal=causal,
+                 window_left=window_left, window_right=window_right,
+                 softmax_scale=softmax_scale, dq=b.dq_head[r], dk=b.dk_head[r],
+                 dv=b.dv_head[r], dsink=ds, workspace=b.workspace)
+    a2a_unpack_into(b.dq_head, b.dq_seq, b.P)
+    a2a_unpack_into(b.dk_head, b.dk_seq, b.P)
+    a2a_unpack_into(b.dv_head, b.dv_seq, b.P)
+
+
+def step(b: StepBuffers, *, causal: bool, window_left: int = -1, window_right: int = -1,
+         ranks: Optional[Sequence[int]] = None, softmax_scale: Optional[float] = None):
+    forward(b, causal=causal, window_left=window_left, window_right=window_right, ranks=ranks,
+            softmax_scale=softmax_scale)
+    backward(b, causal=causal, window_left=window_left, window_right=window_right, ranks=ranks,
+             softmax_scale=softmax_scale)
