@@ -19,8 +19,11 @@ ARCH = os.environ.get("ULYSSES_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in generated code.
+# -amdgpu-mfma-vgpr-form: MFMA accumulators in VGPRs, so the softmax works on
+# them in place instead of copying them out of AGPRs every tile.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _compile(src: str) -> str:

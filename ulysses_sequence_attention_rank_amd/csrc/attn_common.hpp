@@ -119,6 +119,81 @@ __device__ __forceinline__ bool decode_qtile(const AttnArgs& a, int& qt, int& h)
   return true;
 }
 
+// ------------------------------------------------ swizzled tiles (gfx950)
+//
+// A tile of R rows x D bf16 sits in LDS row-major, 2*D bytes a row, its
+// 16-byte slots XOR-swizzled per row: logical slot c of row r lives at
+// physical slot c ^ swz(r).  swz is a bijection on 16 consecutive rows, so
+// the 16-byte operand reads of 16 rows (one slot each) hit distinct banks,
+// and maps rows 4q..4q+3 to distinct slot pairs, so the transposing reads
+// (four rows, 32 bytes each) do too.  Tiles arrive by global_load_lds
+// (16 bytes a lane, lane l at byte 16*l of the instruction's 1 KiB): no
+// registers, no VALU beyond the address.  One tile serves both operand
+// forms:
+//   natural  (A or B): lane l gets row r0 + l%32, columns 16s + 8hf .. + 7
+//   transposed (A or B): lane l gets column d0 + l%32 of the rows in the
+//     k-slot order of attn_common.hpp, via two ds_read_b64_tr_b16: within a
+//     16-lane group, lane j receives element j%4 of the 8-byte chunks that
+//     lanes j/4, j/4+4, j/4+8, j/4+12 address, so lane s addresses row
+//     kb + s/4, columns c0 + 4(s%4) .. + 3 and gets rows kb..kb+3 of column
+//     c0 + (its own index in the group).
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+template <int D>
+struct Swz {
+  static constexpr int kSlots = D / 8;  // 16-byte slots per row
+  __device__ static __forceinline__ int f(int r) {
+    return D == 128 ? 2 * (r & 7) + ((r >> 3) & 1) : 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
+  }
+  // byte offset of logical 16-byte slot c of row r
+  __device__ static __forceinline__ int off(int r, int c) { return r * (2 * D) + ((c ^ f(r)) << 4); }
+};
+
+// Issue the direct-to-LDS loads of a R x D tile: rows row0 .. row0+R-1 of a
+// global matrix with row stride ld elements (rows at or past row_end are
+// clamped to row_end - 1: finite data that the masks then ignore).
+template <int D, int R, int NW>
+__device__ __forceinline__ void tile_load_lds(char* lds, const __bf16* g, int ld, int row0,
+                                              int row_end, int wave, int lane) {
+  constexpr int kInstr = R * D * 2 / 1024;  // 1 KiB per wave instruction
+  static_assert(kInstr % NW == 0, "tile must split evenly over the waves");
+#pragma unroll
+  for (int k = 0; k < kInstr / NW; ++k) {
+    const int i = wave + k * NW;
+    const int pos = i * 64 + lane;               // 16-byte slot index in the tile
+    const int r = pos / Swz<D>::kSlots;
+    const int c = (pos % Swz<D>::kSlots) ^ Swz<D>::f(r);
+    const int row = min(row0 + r, row_end - 1);
+    const __bf16* src = g + (int64_t)row * ld + c * 8;
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + i * 1024), 16, 0, 0);
+  }
+}
+
+// natural operand: rows r0 + l%32, columns 16 s + 8 hf .. + 7
+template <int D>
+__device__ __forceinline__ bf16x8 swz_nat(const char* lds, int r0, int s, int lane) {
+  const int r = r0 + (lane & 31);
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(lds + Swz<D>::off(r, 2 * s + (lane >> 5))));
+}
+
+// transposed operand for the 16-row step at r0: column d0 + l%32
+template <int D>
+__device__ __forceinline__ bf16x8 swz_tr(const char* lds, int r0, int d0, int lane) {
+  const int j = lane & 15, grp = lane >> 4;
+  const int col = d0 + 16 * (grp & 1) + 4 * (j & 3);
+  const int kb = r0 + 4 * (grp >> 1) + (j >> 2);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(lds + Swz<D>::off(kb, col >> 3) + (col & 7) * 2));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(lds + Swz<D>::off(kb + 8, col >> 3) + (col & 7) * 2));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 x = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, x);
+}
+
 // ---------------------------------------------------------------- LDS tiles
 //
 // Natural tile: kBK rows x D, row stride D + 8 elements (16 bytes of padding
@@ -241,6 +316,20 @@ __device__ __forceinline__ void load_row_frags(bf16x8 (&f)[D / 16], const __bf16
     if (valid) x = *reinterpret_cast<const u32x4*>(rowp + 16 * s + 8 * (lane >> 5));
     f[s] = __builtin_bit_cast(bf16x8, x);
   }
+}
+
+// Sum of eight bf16 values (v_dot2_f32_bf16 against ones): the row sum of
+// exactly the probabilities the P V product uses.
+__device__ __forceinline__ float sum_bf16x8(bf16x8 x) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2 p = {x[2 * i], x[2 * i + 1]};
+    s = __builtin_amdgcn_fdot2_f32_bf16(p, one, s, false);
+  }
+  return s;
 }
 
 // Eight accumulator values (C rows 8(2ii) + 4hf + j and 8(2ii+1) + 4hf + j)
