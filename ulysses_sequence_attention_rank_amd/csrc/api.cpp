@@ -257,8 +257,8 @@ size_t ulysses_attn_bwd_workspace_bytes(int B, int S, int hq, int hkv, int D) {
   (void)hkv;
   (void)D;
   if (B <= 0 || S <= 0 || hq <= 0) return 0;
-  // delta, sum_j P dP (both [B][hq][S] fp32), dsink partial sums [hq][parts]
-  return 2 * align256((size_t)B * S * hq * sizeof(float)) +
+  // delta, sum_j P dP, LSE*log2(e) (each [B][hq][S] fp32), dsink partials [hq][parts]
+  return 3 * align256((size_t)B * S * hq * sizeof(float)) +
          align256((size_t)hq * kDsinkParts * sizeof(float));
 }
 
@@ -296,7 +296,8 @@ int ulysses_attn_bwd(const void* q, const void* k, const void* v, const void* ou
   const size_t rows = align256((size_t)B * S * hq * sizeof(float));
   a.delta = (float*)ws;
   a.pdp = (float*)(ws + rows);
-  a.dsink_part = (float*)(ws + 2 * rows);
+  a.lse2 = (float*)(ws + 2 * rows);
+  a.dsink_part = (float*)(ws + 3 * rows);
   a.n_part = kDsinkParts;
   return hip_status(uly::attn_bwd_launch(a, D, (hipStream_t)stream), "ulysses_attn_bwd launch");
 }

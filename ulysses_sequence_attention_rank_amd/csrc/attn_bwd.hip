@@ -40,7 +40,10 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(AttnArgs a) {
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, TPR);
   if (valid && c == 0) {
     const int t = row / a.hq, h = row - t * a.hq;
-    a.delta[lse_index(a, t, h)] = acc;
+    const int idx = lse_index(a, t, h);
+    a.delta[idx] = acc;
+    const float l = a.lse[idx];
+    a.lse2[idx] = l == -INFINITY ? INFINITY : l * kLog2e;  // rows with no key: P = 0
   }
 }
 
@@ -74,17 +77,22 @@ __global__ void dsink_final_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------- dQ
+//
+// One work-group = NW waves x 32 query rows of one head (S^T form, as the
+// forward: a lane owns one query).  K and V tiles of 64 keys arrive by
+// global_load_lds into swizzled natural tiles; K also serves the K^T operand
+// of dQ^T += K^T dS^T through the transposing reads.
 
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnArgs a) {
-  constexpr int NT = NW * 64, BM = 32 * NW, NB = D / 32, KS = D / 16;
-  typedef Tile<D> TL;
-  constexpr int BUF = 2 * TL::kNatElems + TL::kTrElems;  // K natural, V natural, K transposed
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * BUF];
+__global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(AttnArgs a) {
+  constexpr int BM = 32 * NW, NB = D / 32, KS = D / 16;
+  constexpr int TILE = kBK * D * 2;
+  constexpr int STAGE = 2 * TILE;  // K, then V
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
   int qt, h;
   if (!decode_qtile(a, qt, h)) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hf = lane >> 5;
   const int g = h / a.G;
   const int q0 = qt * BM;
   const int qrow = q0 + 32 * wave + (lane & 31);
@@ -102,8 +110,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnArgs a) {
   load_row_frags<D>(dof, a.dout + ((int64_t)qrow * a.hq + h) * D, qvalid, lane);
   float lse2 = INFINITY, dlt = 0.f;  // invalid rows: P = 0
   if (qvalid) {
-    const float l = a.lse[lse_index(a, qrow, h)];
-    lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
+    lse2 = a.lse2[lse_index(a, qrow, h)];
     dlt = a.delta[lse_index(a, qrow, h)];
   }
 
@@ -114,80 +121,59 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnArgs a) {
     for (int e = 0; e < 16; ++e) dqacc[nb][e] = 0.f;
   const bool want_pdp = a.sink != nullptr;
   float pdp = 0.f;
+  const f32x16 zero = {};
 
   const __bf16* kbase = a.k + (int64_t)g * D;
   const __bf16* vbase = a.v + (int64_t)g * D;
   const int ld = a.hkv * D;
-  TileLoader<D, NT> ldk, ldv;  // ldk stages K in both layouts
-
   const int n_iter = (wg_hi - wg_lo + kBK - 1) / kBK;
   if (n_iter > 0) {
-    ldk.load_nat(kbase, ld, wg_lo, a.T, tid);
-    ldk.load_tr(kbase, ld, wg_lo, a.T, tid);
-    ldv.load_nat(vbase, ld, wg_lo, a.T, tid);
-    ldk.store_nat(smem, tid);
-    ldv.store_nat(smem + TL::kNatElems, tid);
-    ldk.store_tr(smem + 2 * TL::kNatElems, tid);
+    tile_load_lds<D, kBK, NW>(smem, kbase, ld, wg_lo, a.T, wave, lane);
+    tile_load_lds<D, kBK, NW>(smem + TILE, vbase, ld, wg_lo, a.T, wave, lane);
   }
-  __syncthreads();
 
   for (int it = 0; it < n_iter; ++it) {
     const int cur = it & 1;
     const int k0 = wg_lo + it * kBK;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
     if (it + 1 < n_iter) {
-      ldk.load_nat(kbase, ld, k0 + kBK, a.T, tid);
-      ldk.load_tr(kbase, ld, k0 + kBK, a.T, tid);
-      ldv.load_nat(vbase, ld, k0 + kBK, a.T, tid);
+      char* nxt = smem + (cur ^ 1) * STAGE;
+      tile_load_lds<D, kBK, NW>(nxt, kbase, ld, k0 + kBK, a.T, wave, lane);
+      tile_load_lds<D, kBK, NW>(nxt + TILE, vbase, ld, k0 + kBK, a.T, wave, lane);
     }
-    const __bf16* ks = smem + cur * BUF;
-    const __bf16* vs = ks + TL::kNatElems;
-    const __bf16* kt = ks + 2 * TL::kNatElems;
+    const char* kt = smem + cur * STAGE;
+    const char* vt = kt + TILE;
 
-    f32x16 sacc[2], dpacc[2];
+    const bool full = k0 >= full_lo && k0 + kBK <= full_hi;
+    // one 32-key block at a time keeps two accumulators live, not four
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        sacc[mb][e] = 0.f;
-        dpacc[mb][e] = 0.f;
-      }
+      f32x16 sacc, dpacc;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        sacc[mb] = mfma32(nat_frag<D>(ks, 32 * mb, s, lane), qf[s], sacc[mb]);
-        dpacc[mb] = mfma32(nat_frag<D>(vs, 32 * mb, s, lane), dof[s], dpacc[mb]);
+        sacc = mfma32(swz_nat<D>(kt, 32 * mb, s, lane), qf[s], s == 0 ? zero : sacc);
+        dpacc = mfma32(swz_nat<D>(vt, 32 * mb, s, lane), dof[s], s == 0 ? zero : dpacc);
       }
-    }
-    const bool full = k0 >= full_lo && k0 + kBK <= full_hi;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mb][e], a.scale_log2, -lse2));
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], a.scale_log2, -lse2));
         if (!full) {
           const int key = k0 + 32 * mb + 8 * (e >> 2) + 4 * hf + (e & 3);
           if (key < klo || key >= khi) p = 0.f;
         }
-        if (want_pdp) pdp = __builtin_fmaf(p, dpacc[mb][e], pdp);
-        sacc[mb][e] = p * (dpacc[mb][e] - dlt);  // dS^T
+        if (want_pdp) pdp = __builtin_fmaf(p, dpacc[e], pdp);
+        sacc[e] = p * (dpacc[e] - dlt);  // dS^T
       }
-    // dQ^T += K^T dS^T
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+      // dQ^T += K^T dS^T
 #pragma unroll
       for (int ii = 0; ii < 2; ++ii) {
-        const bf16x8 df = acc_frag(sacc[mb], ii);
+        const bf16x8 df = acc_frag(sacc, ii);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
-          dqacc[nb] = mfma32(tr_frag<D>(kt, 32 * mb + 16 * ii, 32 * nb, lane), df, dqacc[nb]);
+          dqacc[nb] = mfma32(swz_tr<D>(kt, 32 * mb + 16 * ii, 32 * nb, lane), df, dqacc[nb]);
       }
-
-    if (it + 1 < n_iter) {
-      __bf16* nb_ = smem + (cur ^ 1) * BUF;
-      ldk.store_nat(nb_, tid);
-      ldv.store_nat(nb_ + TL::kNatElems, tid);
-      ldk.store_tr(nb_ + 2 * TL::kNatElems, tid);
     }
-    __syncthreads();
   }
 
   pdp = halves_sum(pdp);
@@ -207,19 +193,26 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------ dK, dV
+//
+// One work-group = NW waves x 32 keys of one KV head; K and V rows stay in
+// registers as B operands.  The work-group walks every query tile (64 rows)
+// of every query head of the group: Q and dO tiles plus their LSE*log2(e)
+// and delta rows arrive by global_load_lds, and each tile serves both the
+// natural operand (S = Q K^T, dP = dO V^T) and, through the transposing
+// reads, the operand of dV += P^T dO and dK += dS^T Q.
 
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(AttnArgs a) {
-  constexpr int NT = NW * 64, BN = 32 * NW, NB = D / 32, KS = D / 16;
-  typedef Tile<D> TL;
-  // Q natural, dO natural, Q transposed, dO transposed, then LSE*log2e and delta
-  constexpr int BUF = 2 * TL::kNatElems + 2 * TL::kTrElems + 2 * kBK * 2;  // in bf16 units
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * BUF];
+  static_assert(NW >= 2, "two waves stage the per-row statistics");
+  constexpr int BN = 32 * NW, NB = D / 32, KS = D / 16;
+  constexpr int TILE = kBK * D * 2;
+  constexpr int STAGE = 2 * TILE + 2 * kBK * 4;  // Q, dO, LSE*log2e, delta
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
   const int L = blockIdx.x;
   if (L >= a.n_tiles * a.hkv) return;
   const int kt = L / a.hkv, g = L % a.hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hf = lane >> 5;
   const int k0 = kt * BN;
   const int krow = k0 + 32 * wave + (lane & 31);
   const bool kvalid = krow < a.T;
@@ -243,73 +236,45 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(AttnArgs a) {
       dkacc[nb][e] = 0.f;
       dvacc[nb][e] = 0.f;
     }
+  const f32x16 zero = {};
 
   const int ld = a.hq * D;
   const int nq = (wg_hi - wg_lo + kBK - 1) / kBK;  // query tiles per head
   const int n_iter = nq * a.G;
-  TileLoader<D, NT> ldq, ldo;  // both layouts each
-  float ls_reg = 0.f, dl_reg = 0.f;
 
-  auto fetch = [&](int it) {
+  auto issue = [&](int it, char* buf) {
     const int hh = it / nq, qa = wg_lo + (it - hh * nq) * kBK;
     const int h = g * a.G + hh;
-    ldq.load_nat(a.q + (int64_t)h * D, ld, qa, a.T, tid);
-    ldq.load_tr(a.q + (int64_t)h * D, ld, qa, a.T, tid);
-    ldo.load_nat(a.dout + (int64_t)h * D, ld, qa, a.T, tid);
-    ldo.load_tr(a.dout + (int64_t)h * D, ld, qa, a.T, tid);
-    if (tid < kBK) {
-      const int t = qa + tid;
-      ls_reg = INFINITY;
-      dl_reg = 0.f;
-      if (t < a.T) {
-        const float l = a.lse[lse_index(a, t, h)];
-        ls_reg = l == -INFINITY ? INFINITY : l * kLog2e;
-        dl_reg = a.delta[lse_index(a, t, h)];
-      }
-    }
-  };
-  auto stage = [&](__bf16* buf) {
-    ldq.store_nat(buf, tid);
-    ldo.store_nat(buf + TL::kNatElems, tid);
-    ldq.store_tr(buf + 2 * TL::kNatElems, tid);
-    ldo.store_tr(buf + 2 * TL::kNatElems + TL::kTrElems, tid);
-    float* f = reinterpret_cast<float*>(buf + 2 * TL::kNatElems + 2 * TL::kTrElems);
-    if (tid < kBK) {
-      f[tid] = ls_reg;
-      f[kBK + tid] = dl_reg;
+    tile_load_lds<D, kBK, NW>(buf, a.q + (int64_t)h * D, ld, qa, a.T, wave, lane);
+    tile_load_lds<D, kBK, NW>(buf + TILE, a.dout + (int64_t)h * D, ld, qa, a.T, wave, lane);
+    if (wave < 2) {
+      const int idx = lse_index(a, min(qa + lane, a.T - 1), h);
+      const float* src = wave == 0 ? a.lse2 + idx : a.delta + idx;
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(buf + 2 * TILE + wave * kBK * 4), 4, 0, 0);
     }
   };
 
-  if (n_iter > 0) {
-    fetch(0);
-    stage(smem);
-  }
-  __syncthreads();
+  if (n_iter > 0) issue(0, smem);
 
   for (int it = 0; it < n_iter; ++it) {
     const int cur = it & 1;
     const int hh = it / nq, qa = wg_lo + (it - hh * nq) * kBK;
-    if (it + 1 < n_iter) fetch(it + 1);
-    const __bf16* qs = smem + cur * BUF;
-    const __bf16* dos = qs + TL::kNatElems;
-    const __bf16* qtr = qs + 2 * TL::kNatElems;
-    const __bf16* dotr = qtr + TL::kTrElems;
-    const float* lsd = reinterpret_cast<const float*>(qs + 2 * TL::kNatElems + 2 * TL::kTrElems);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (it + 1 < n_iter) issue(it + 1, smem + (cur ^ 1) * STAGE);
+    const char* qs = smem + cur * STAGE;
+    const char* dos = qs + TILE;
+    const float* lsd = reinterpret_cast<const float*>(qs + 2 * TILE);
     const bool full = qa >= full_lo && qa + kBK <= full_hi;
 
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
+      // S = Q K^T and dP = dO V^T: column = this lane's key, rows = 32 queries
       f32x16 sacc, dpacc;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        sacc[e] = 0.f;
-        dpacc[e] = 0.f;
-      }
-      // S = Q K^T and dP = dO V^T: column = this lane's key, rows = 32 queries
-#pragma unroll
       for (int s = 0; s < KS; ++s) {
-        sacc = mfma32(nat_frag<D>(qs, 32 * qb, s, lane), kf[s], sacc);
-        dpacc = mfma32(nat_frag<D>(dos, 32 * qb, s, lane), vf[s], dpacc);
+        sacc = mfma32(swz_nat<D>(qs, 32 * qb, s, lane), kf[s], s == 0 ? zero : sacc);
+        dpacc = mfma32(swz_nat<D>(dos, 32 * qb, s, lane), vf[s], s == 0 ? zero : dpacc);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -334,14 +299,11 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(AttnArgs a) {
         const bf16x8 df = acc_frag(dpacc, ii);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          dvacc[nb] = mfma32(pf, tr_frag<D>(dotr, 32 * qb + 16 * ii, 32 * nb, lane), dvacc[nb]);
-          dkacc[nb] = mfma32(df, tr_frag<D>(qtr, 32 * qb + 16 * ii, 32 * nb, lane), dkacc[nb]);
+          dvacc[nb] = mfma32(pf, swz_tr<D>(dos, 32 * qb + 16 * ii, 32 * nb, lane), dvacc[nb]);
+          dkacc[nb] = mfma32(df, swz_tr<D>(qs, 32 * qb + 16 * ii, 32 * nb, lane), dkacc[nb]);
         }
       }
     }
-
-    if (it + 1 < n_iter) stage(smem + (cur ^ 1) * BUF);
-    __syncthreads();
   }
 
   // dK, dV: lane holds column d = 32 nb + l % 32 of key rows 8 i + 4 hf + j

@@ -33,6 +33,7 @@ struct AttnArgs {
   float* lse;    // fwd output / bwd input, [B][hq][S]
   float* delta;  // bwd: rowsum(dO * O) with the bf16 O, [B][hq][S]
   float* pdp;    // bwd: sum_j P_ij dP_ij = dO_i . O_i with the exact O, [B][hq][S]
+  float* lse2;   // bwd: LSE * log2(e) (+inf for rows without keys), [B][hq][S]
   const float* sink;
   float* dsink_part;  // [hq][n_part]
   float* dsink;
