@@ -5,6 +5,8 @@ non-causal, packed varlen (documents straddling shard and tile boundaries,
 one-token documents), sliding and two-sided windows, GQA with group sizes
 1, 2, 4 and 7, sinks, batch > 1 and both head dims.
 """
+import zlib
+
 import pytest
 import torch
 
@@ -32,7 +34,7 @@ CASES = [
 def _run(row):
     from ulysses_sequence_attention_rank_amd import sim
     name, P, B, S, Hq, Hkv, D, causal, wl, wr, sink, docs = row
-    inp = small_case(abs(hash(name)) % 10000, P=P, B=B, S=S, Hq=Hq, Hkv=Hkv, D=D, sink=sink,
+    inp = small_case(zlib.crc32(name.encode()) % 10000, P=P, B=B, S=S, Hq=Hq, Hkv=Hkv, D=D, sink=sink,
                      doc_lengths=docs)
     dev = torch.device("cuda", 0)
     bufs = sim.allocate(seq_shards(inp.q, P).to(dev), seq_shards(inp.k, P).to(dev),

@@ -16,6 +16,7 @@ the gathered position_ids and the sink is one logit per head (accelerate PR
 import json
 import math
 import os
+import zlib
 
 import pytest
 import torch
@@ -123,7 +124,7 @@ def _setup(case_row, seed):
 
 @pytest.mark.parametrize("row", CASES, ids=[c[0] for c in CASES])
 def test_fwd_bwd_match_torch_sdpa(row):
-    inp, cu, causal, wl, wr, scale = _setup(row, seed=hash(row[0]) % 1000)
+    inp, cu, causal, wl, wr, scale = _setup(row, seed=zlib.crc32(row[0].encode()) % 1000)
     kw = dict(sink=inp.sink, cu=cu, causal=causal, window_left=wl, window_right=wr, scale=scale)
     o, lse = oracle.attn_fwd(inp.q, inp.k, inp.v, **kw)
     dq, dk, dv, ds = oracle.attn_bwd(inp.q, inp.k, inp.v, inp.dout, **kw)

@@ -14,7 +14,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libulysses.so")
-SOURCES = ["api.cpp", "permute.hip", "segments.hip", "attn_fwd.hip", "attn_bwd.hip"]
+SOURCES = ["api.cpp", "permute.hip", "segments.hip", "attn_fwd.hip", "attn_bwd.hip",
+           "attn_bwd_dkdv.hip"]
 ARCH = os.environ.get("ULYSSES_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -26,9 +27,14 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
          "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
+# Per-file scheduler choice: the dK/dV kernel runs one wave per SIMD and needs
+# the ILP-oriented strategy to issue LDS operand reads ahead of the products.
+EXTRA = {"attn_bwd_dkdv.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + FLAGS + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd = [HIPCC] + FLAGS + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)

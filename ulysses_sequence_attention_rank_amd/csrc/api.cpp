@@ -254,12 +254,12 @@ int ulysses_attn_fwd(const void* q, const void* k, const void* v, void* out, flo
 }
 
 size_t ulysses_attn_bwd_workspace_bytes(int B, int S, int hq, int hkv, int D) {
-  (void)hkv;
-  (void)D;
-  if (B <= 0 || S <= 0 || hq <= 0) return 0;
-  // delta, sum_j P dP, LSE*log2(e) (each [B][hq][S] fp32), dsink partials [hq][parts]
-  return 3 * align256((size_t)B * S * hq * sizeof(float)) +
-         align256((size_t)hq * kDsinkParts * sizeof(float));
+  if (B <= 0 || S <= 0 || hq <= 0 || hkv <= 0 || D <= 0) return 0;
+  // delta, sum_j P dP, LSE*log2(e) (each [B][hq][S] fp32), dsink partials [hq][parts],
+  // fp16 copies of q, dout ([B][S][hq][D]) and k, v ([B][S][hkv][D])
+  const size_t rows = align256((size_t)B * S * hq * sizeof(float));
+  const size_t qsz = align256((size_t)B * S * hq * D * 2), kvsz = align256((size_t)B * S * hkv * D * 2);
+  return 3 * rows + align256((size_t)hq * kDsinkParts * sizeof(float)) + 2 * qsz + 2 * kvsz;
 }
 
 int ulysses_attn_bwd(const void* q, const void* k, const void* v, const void* out,
@@ -298,6 +298,12 @@ int ulysses_attn_bwd(const void* q, const void* k, const void* v, const void* ou
   a.pdp = (float*)(ws + rows);
   a.lse2 = (float*)(ws + 2 * rows);
   a.dsink_part = (float*)(ws + 3 * rows);
+  char* h16 = ws + 3 * rows + align256((size_t)hq * kDsinkParts * sizeof(float));
+  const size_t qsz = align256((size_t)B * S * hq * D * 2), kvsz = align256((size_t)B * S * hkv * D * 2);
+  a.q16 = (_Float16*)h16;
+  a.do16 = (_Float16*)(h16 + qsz);
+  a.k16 = (_Float16*)(h16 + 2 * qsz);
+  a.v16 = (_Float16*)(h16 + 2 * qsz + kvsz);
   a.n_part = kDsinkParts;
   return hip_status(uly::attn_bwd_launch(a, D, (hipStream_t)stream), "ulysses_attn_bwd launch");
 }

@@ -11,7 +11,13 @@
 //          with D_i = sum_j P_ij dP_ij accumulated by attn_bwd_dq: equal to
 //          dO_i . O_i for the exact O, not the bf16-rounded O delta_i uses
 // Both main kernels recompute P from LSE; neither uses atomics, so the
-// gradients are deterministic.
+// gradients are deterministic.  Their products run in fp16 on exact fp16
+// copies of q, k, v, dout (made here, in the workspace): P and dS are rounded
+// to fp16's 11 significant bits instead of bf16's 8 before the dV, dK and dQ
+// products, which keeps the gradients within the bf16-output tolerance even
+// where attention is concentrated on few keys.
+#include <climits>
+
 #include "attn_common.hpp"
 #include "launch.hpp"
 
@@ -32,9 +38,13 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(AttnArgs a) {
   if (valid) {
     const u32x4 x = *reinterpret_cast<const u32x4*>(a.dout + (int64_t)row * D + 8 * c);
     const u32x4 y = *reinterpret_cast<const u32x4*>(a.o + (int64_t)row * D + 8 * c);
+    u32x4 h;
 #pragma unroll
-    for (int w = 0; w < 4; ++w)
+    for (int w = 0; w < 4; ++w) {
       acc += bf16_lo(x[w]) * bf16_lo(y[w]) + bf16_hi(x[w]) * bf16_hi(y[w]);
+      h[w] = pack_f16x2(clamp_f16(bf16_lo(x[w])), clamp_f16(bf16_hi(x[w])));
+    }
+    *reinterpret_cast<u32x4*>(a.do16 + (int64_t)row * D + 8 * c) = h;
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, TPR);
@@ -44,6 +54,20 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(AttnArgs a) {
     a.delta[idx] = acc;
     const float l = a.lse[idx];
     a.lse2[idx] = l == -INFINITY ? INFINITY : l * kLog2e;  // rows with no key: P = 0
+  }
+}
+
+// Exact fp16 copy of a bf16 array (n a multiple of 8): every bf16 value of
+// magnitude <= 65504 is an fp16 value (fp16 keeps 11 significant bits, bf16 8);
+// larger magnitudes saturate, values below 2^-14 round to fp16's subnormals.
+__global__ __launch_bounds__(256) void to_f16_kernel(const __bf16* src, _Float16* dst, int64_t n) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i < n) {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(src + i);
+    u32x4 h;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) h[w] = pack_f16x2(clamp_f16(bf16_lo(x[w])), clamp_f16(bf16_hi(x[w])));
+    *reinterpret_cast<u32x4*>(dst + i) = h;
   }
 }
 
@@ -106,8 +130,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(AttnArgs a) {
   key_interval(a, q_last, full_lo, wg_hi);
 
   bf16x8 qf[KS], dof[KS];
-  load_row_frags<D>(qf, a.q + ((int64_t)qrow * a.hq + h) * D, qvalid, lane);
-  load_row_frags<D>(dof, a.dout + ((int64_t)qrow * a.hq + h) * D, qvalid, lane);
+  load_row_frags<D>(qf, a.q16 + ((int64_t)qrow * a.hq + h) * D, qvalid, lane);
+  load_row_frags<D>(dof, a.do16 + ((int64_t)qrow * a.hq + h) * D, qvalid, lane);
   float lse2 = INFINITY, dlt = 0.f;  // invalid rows: P = 0
   if (qvalid) {
     lse2 = a.lse2[lse_index(a, qrow, h)];
@@ -123,8 +147,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(AttnArgs a) {
   float pdp = 0.f;
   const f32x16 zero = {};
 
-  const __bf16* kbase = a.k + (int64_t)g * D;
-  const __bf16* vbase = a.v + (int64_t)g * D;
+  const _Float16* kbase = a.k16 + (int64_t)g * D;
+  const _Float16* vbase = a.v16 + (int64_t)g * D;
   const int ld = a.hkv * D;
   const int n_iter = (wg_hi - wg_lo + kBK - 1) / kBK;
   if (n_iter > 0) {
@@ -152,8 +176,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(AttnArgs a) {
       f32x16 sacc, dpacc;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        sacc = mfma32(swz_nat<D>(kt, 32 * mb, s, lane), qf[s], s == 0 ? zero : sacc);
-        dpacc = mfma32(swz_nat<D>(vt, 32 * mb, s, lane), dof[s], s == 0 ? zero : dpacc);
+        sacc = mfma32h(swz_nat<D>(kt, 32 * mb, s, lane), qf[s], s == 0 ? zero : sacc);
+        dpacc = mfma32h(swz_nat<D>(vt, 32 * mb, s, lane), dof[s], s == 0 ? zero : dpacc);
       }
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -168,10 +192,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(AttnArgs a) {
       // dQ^T += K^T dS^T
 #pragma unroll
       for (int ii = 0; ii < 2; ++ii) {
-        const bf16x8 df = acc_frag(sacc, ii);
+        const bf16x8 df = acc_frag_h(sacc, ii);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
-          dqacc[nb] = mfma32(swz_tr<D>(kt, 32 * mb + 16 * ii, 32 * nb, lane), df, dqacc[nb]);
+          dqacc[nb] = mfma32h(swz_tr<D>(kt, 32 * mb + 16 * ii, 32 * nb, lane), df, dqacc[nb]);
       }
     }
   }
@@ -192,134 +216,6 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(AttnArgs a) {
   }
 }
 
-// ------------------------------------------------------------------ dK, dV
-//
-// One work-group = NW waves x 32 keys of one KV head; K and V rows stay in
-// registers as B operands.  The work-group walks every query tile (64 rows)
-// of every query head of the group: Q and dO tiles plus their LSE*log2(e)
-// and delta rows arrive by global_load_lds, and each tile serves both the
-// natural operand (S = Q K^T, dP = dO V^T) and, through the transposing
-// reads, the operand of dV += P^T dO and dK += dS^T Q.
-
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(AttnArgs a) {
-  static_assert(NW >= 2, "two waves stage the per-row statistics");
-  constexpr int BN = 32 * NW, NB = D / 32, KS = D / 16;
-  constexpr int TILE = kBK * D * 2;
-  constexpr int STAGE = 2 * TILE + 2 * kBK * 4;  // Q, dO, LSE*log2e, delta
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
-
-  const int L = blockIdx.x;
-  if (L >= a.n_tiles * a.hkv) return;
-  const int kt = L / a.hkv, g = L % a.hkv;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hf = lane >> 5;
-  const int k0 = kt * BN;
-  const int krow = k0 + 32 * wave + (lane & 31);
-  const bool kvalid = krow < a.T;
-
-  int qlo = 0, qhi = 0;
-  if (kvalid) query_interval(a, krow, qlo, qhi);
-  const int k_last = min(k0 + BN, a.T) - 1;
-  int wg_lo, wg_hi, full_lo, full_hi;
-  query_interval(a, k0, wg_lo, full_hi);
-  query_interval(a, k_last, full_lo, wg_hi);
-
-  bf16x8 kf[KS], vf[KS];
-  load_row_frags<D>(kf, a.k + ((int64_t)krow * a.hkv + g) * D, kvalid, lane);
-  load_row_frags<D>(vf, a.v + ((int64_t)krow * a.hkv + g) * D, kvalid, lane);
-
-  f32x16 dkacc[NB], dvacc[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      dkacc[nb][e] = 0.f;
-      dvacc[nb][e] = 0.f;
-    }
-  const f32x16 zero = {};
-
-  const int ld = a.hq * D;
-  const int nq = (wg_hi - wg_lo + kBK - 1) / kBK;  // query tiles per head
-  const int n_iter = nq * a.G;
-
-  auto issue = [&](int it, char* buf) {
-    const int hh = it / nq, qa = wg_lo + (it - hh * nq) * kBK;
-    const int h = g * a.G + hh;
-    tile_load_lds<D, kBK, NW>(buf, a.q + (int64_t)h * D, ld, qa, a.T, wave, lane);
-    tile_load_lds<D, kBK, NW>(buf + TILE, a.dout + (int64_t)h * D, ld, qa, a.T, wave, lane);
-    if (wave < 2) {
-      const int idx = lse_index(a, min(qa + lane, a.T - 1), h);
-      const float* src = wave == 0 ? a.lse2 + idx : a.delta + idx;
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(buf + 2 * TILE + wave * kBK * 4), 4, 0, 0);
-    }
-  };
-
-  if (n_iter > 0) issue(0, smem);
-
-  for (int it = 0; it < n_iter; ++it) {
-    const int cur = it & 1;
-    const int hh = it / nq, qa = wg_lo + (it - hh * nq) * kBK;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (it + 1 < n_iter) issue(it + 1, smem + (cur ^ 1) * STAGE);
-    const char* qs = smem + cur * STAGE;
-    const char* dos = qs + TILE;
-    const float* lsd = reinterpret_cast<const float*>(qs + 2 * TILE);
-    const bool full = qa >= full_lo && qa + kBK <= full_hi;
-
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      // S = Q K^T and dP = dO V^T: column = this lane's key, rows = 32 queries
-      f32x16 sacc, dpacc;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        sacc = mfma32(swz_nat<D>(qs, 32 * qb, s, lane), kf[s], s == 0 ? zero : sacc);
-        dpacc = mfma32(swz_nat<D>(dos, 32 * qb, s, lane), vf[s], s == 0 ? zero : dpacc);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r0 = 32 * qb + 8 * i + 4 * hf;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lsd + r0);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(lsd + kBK + r0);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * i + j], a.scale_log2, -l4[j]));
-          if (!full) {
-            const int qi = qa + r0 + j;
-            if (qi < qlo || qi >= qhi) p = 0.f;
-          }
-          sacc[4 * i + j] = p;
-          dpacc[4 * i + j] = p * (dpacc[4 * i + j] - d4[j]);
-        }
-      }
-      // dV += P^T dO, dK += dS^T Q (contraction over the 32 queries)
-#pragma unroll
-      for (int ii = 0; ii < 2; ++ii) {
-        const bf16x8 pf = acc_frag(sacc, ii);
-        const bf16x8 df = acc_frag(dpacc, ii);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          dvacc[nb] = mfma32(pf, swz_tr<D>(dos, 32 * qb + 16 * ii, 32 * nb, lane), dvacc[nb]);
-          dkacc[nb] = mfma32(df, swz_tr<D>(qs, 32 * qb + 16 * ii, 32 * nb, lane), dkacc[nb]);
-        }
-      }
-    }
-  }
-
-  // dK, dV: lane holds column d = 32 nb + l % 32 of key rows 8 i + 4 hf + j
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int key = k0 + 32 * wave + 8 * (e >> 2) + 4 * hf + (e & 3);
-      if (key < a.T) {
-        const int64_t off = ((int64_t)key * a.hkv + g) * D + 32 * nb + (lane & 31);
-        a.dk[off] = (__bf16)(dkacc[nb][e] * a.scale);
-        a.dv[off] = (__bf16)dvacc[nb][e];
-      }
-    }
-}
-
 // ------------------------------------------------------------------ launches
 
 template <int D, int NW>
@@ -331,11 +227,13 @@ static hipError_t launch_bwd_t(const AttnArgs& args, hipStream_t st) {
     hipLaunchKernelGGL(attn_bwd_pre_kernel<D>, dim3((rows + rpb - 1) / rpb), dim3(256), 0, st, a);
   }
   {
-    AttnArgs b = a;
-    b.n_tiles = (a.T + 32 * NW - 1) / (32 * NW);
-    ProfScope prof("attn_bwd_dkdv", st);
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, NW>), dim3(b.n_tiles * a.hkv), dim3(NW * 64), 0, st, b);
+    ProfScope prof("attn_bwd_f16", st);
+    const int64_t nq = (int64_t)a.T * a.hq * D, nkv = (int64_t)a.T * a.hkv * D;
+    hipLaunchKernelGGL(to_f16_kernel, dim3((nq / 8 + 255) / 256), dim3(256), 0, st, a.q, a.q16, nq);
+    hipLaunchKernelGGL(to_f16_kernel, dim3((nkv / 8 + 255) / 256), dim3(256), 0, st, a.k, a.k16, nkv);
+    hipLaunchKernelGGL(to_f16_kernel, dim3((nkv / 8 + 255) / 256), dim3(256), 0, st, a.v, a.v16, nkv);
   }
+  dkdv_launch(a, D, st);
   {
     AttnArgs b = a;
     b.n_tiles = (a.T + 32 * NW - 1) / (32 * NW);

@@ -1,0 +1,196 @@
+// Attention backward of one Ulysses rank: the key-stationary dK/dV kernel.
+// (The delta pre-pass, the dQ kernel and dsink are in attn_bwd.hip; this file
+// is compiled with an ILP-oriented machine scheduler: at one wave per SIMD the
+// kernel must hide LDS latency inside the wave, by issuing operand reads well
+// ahead of their products.)
+#include <climits>
+
+#include "attn_common.hpp"
+#include "launch.hpp"
+
+namespace uly {
+
+// ------------------------------------------------------------------ dK, dV
+//
+// Products in fp16 on the fp16 copies the pre-pass makes (see attn_bwd.hip).
+// One work-group = NW waves x 32 keys of one KV head.  The work-group's K and
+// V rows are staged once in LDS (swizzled natural tiles) and read as B
+// operands when needed, which leaves registers for the dK/dV accumulators and
+// for operand prefetch.  The work-group walks every query tile (64 rows) of
+// every query head of the group: Q and dO tiles plus their LSE*log2(e) and
+// delta rows arrive by global_load_lds, double-buffered in two distinct LDS
+// arrays (the loop is unrolled by two, so reads of one stage are provably
+// disjoint from the loads into the other), and each tile serves both the
+// natural operand (S = Q K^T, dP = dO V^T) and, through the transposing
+// reads, the operand of dV += P^T dO and dK += dS^T Q.
+
+template <int D, int NW>
+struct DkdvSmem {
+  static constexpr int kTile = kBK * D * 2;
+  static constexpr int kStage = 2 * kTile + 2 * kBK * 4;  // Q, dO, LSE*log2e, delta
+  static constexpr int kKV = 32 * NW * D * 2;              // K or V rows of the work-group
+};
+
+template <int D, int NW>
+__device__ __forceinline__ void dkdv_tile(const AttnArgs& a, const char* buf, const char* kvs,
+                                          f32x16 (&dkacc)[D / 32], f32x16 (&dvacc)[D / 32],
+                                          int qa, int full_lo, int full_hi, int qlo, int qhi,
+                                          int wave, int lane) {
+  typedef DkdvSmem<D, NW> SM;
+  constexpr int NB = D / 32, KS = D / 16;
+  const int hf = lane >> 5;
+  const char* qs = buf;
+  const char* dos = buf + SM::kTile;
+  const float* lsd = reinterpret_cast<const float*>(buf + 2 * SM::kTile);
+  const char* ks = kvs;
+  const char* vs = kvs + SM::kKV;
+  const f32x16 zero = {};
+
+  // visible queries of this lane's key; a fully visible tile opens the interval
+  const bool full = qa >= full_lo && qa + kBK <= full_hi;
+  const int mlo = full ? INT_MIN : qlo - qa, mhi = full ? INT_MAX : qhi - qa;
+
+  f32x16 sacc[2], dpacc[2];
+  bf16x8 pf[2][2], df[2][2];
+  auto sdp = [&](int qb) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      sacc[qb] = mfma32h(swz_nat<D>(qs, 32 * qb, s, lane), swz_nat<D>(ks, 32 * wave, s, lane),
+                         s == 0 ? zero : sacc[qb]);
+      dpacc[qb] = mfma32h(swz_nat<D>(dos, 32 * qb, s, lane), swz_nat<D>(vs, 32 * wave, s, lane),
+                          s == 0 ? zero : dpacc[qb]);
+    }
+  };
+  auto softmax = [&](int qb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r0 = 32 * qb + 8 * i + 4 * hf;
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(lsd + r0);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(lsd + kBK + r0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][4 * i + j], a.scale_log2, -l4[j]));
+        p = (r0 + j >= mlo && r0 + j < mhi) ? p : 0.f;
+        sacc[qb][4 * i + j] = p;
+        dpacc[qb][4 * i + j] = p * (dpacc[qb][4 * i + j] - d4[j]);
+      }
+    }
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+      pf[qb][ii] = acc_frag_h(sacc[qb], ii);
+      df[qb][ii] = acc_frag_h(dpacc[qb], ii);
+    }
+  };
+  // dV += P^T dO, dK += dS^T Q (contraction over the block's 32 queries)
+  auto dvdk = [&](int qb) {
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        dvacc[nb] = mfma32h(pf[qb][ii], swz_tr<D>(dos, 32 * qb + 16 * ii, 32 * nb, lane), dvacc[nb]);
+        dkacc[nb] = mfma32h(df[qb][ii], swz_tr<D>(qs, 32 * qb + 16 * ii, 32 * nb, lane), dkacc[nb]);
+      }
+  };
+  // two 32-query blocks in a software pipeline (block 1's products are
+  // independent of block 0's softmax, block 0's dV/dK of block 1's softmax)
+  sdp(0);
+  softmax(0);
+  sdp(1);
+  dvdk(0);
+  softmax(1);
+  dvdk(1);
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(AttnArgs a) {
+  static_assert(NW >= 2, "two waves stage the per-row statistics");
+  typedef DkdvSmem<D, NW> SM;
+  constexpr int BN = 32 * NW, NB = D / 32;
+  __shared__ __attribute__((aligned(1024))) char kvs[2 * SM::kKV];
+  __shared__ __attribute__((aligned(1024))) char st0[SM::kStage];
+  __shared__ __attribute__((aligned(1024))) char st1[SM::kStage];
+
+  const int L = blockIdx.x;
+  if (L >= a.n_tiles * a.hkv) return;
+  const int kt = L / a.hkv, g = L % a.hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hf = lane >> 5;
+  const int k0 = kt * BN;
+  const int krow = k0 + 32 * wave + (lane & 31);
+  const bool kvalid = krow < a.T;
+
+  int qlo = 0, qhi = 0;
+  if (kvalid) query_interval(a, krow, qlo, qhi);
+  const int k_last = min(k0 + BN, a.T) - 1;
+  int wg_lo, wg_hi, full_lo, full_hi;
+  query_interval(a, k0, wg_lo, full_hi);
+  query_interval(a, k_last, full_lo, wg_hi);
+
+  // the work-group's K and V rows, once
+  tile_load_lds<D, BN, NW>(kvs, a.k16 + (int64_t)g * D, a.hkv * D, k0, a.T, wave, lane);
+  tile_load_lds<D, BN, NW>(kvs + SM::kKV, a.v16 + (int64_t)g * D, a.hkv * D, k0, a.T, wave, lane);
+
+  f32x16 dkacc[NB], dvacc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      dkacc[nb][e] = 0.f;
+      dvacc[nb][e] = 0.f;
+    }
+
+  const int ld = a.hq * D;
+  const int nq = (wg_hi - wg_lo + kBK - 1) / kBK;  // query tiles per head
+  const int n_iter = nq * a.G;
+  auto tile_q0 = [&](int it) { return wg_lo + (it % nq) * kBK; };
+  auto issue = [&](int it, char* buf) {
+    const int hh = it / nq, qa = wg_lo + (it - hh * nq) * kBK;
+    const int h = g * a.G + hh;
+    tile_load_lds<D, kBK, NW>(buf, a.q16 + (int64_t)h * D, ld, qa, a.T, wave, lane);
+    tile_load_lds<D, kBK, NW>(buf + SM::kTile, a.do16 + (int64_t)h * D, ld, qa, a.T, wave, lane);
+    if (wave < 2) {
+      const int idx = lse_index(a, min(qa + lane, a.T - 1), h);
+      const float* src = wave == 0 ? a.lse2 + idx : a.delta + idx;
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(buf + 2 * SM::kTile + wave * kBK * 4), 4, 0, 0);
+    }
+  };
+  auto step = [&](int it, const char* buf, char* nxt) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile `it` have landed
+    __syncthreads();                // everyone's have, and the other stage is free
+    if (it + 1 < n_iter) issue(it + 1, nxt);
+    dkdv_tile<D, NW>(a, buf, kvs, dkacc, dvacc, tile_q0(it), full_lo, full_hi, qlo, qhi, wave, lane);
+  };
+
+  if (n_iter > 0) issue(0, st0);
+  for (int it = 0; it < n_iter; it += 2) {
+    step(it, st0, st1);
+    if (it + 1 < n_iter) step(it + 1, st1, st0);
+  }
+
+  // dK, dV: lane holds column d = 32 nb + l % 32 of key rows 8 i + 4 hf + j
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int key = k0 + 32 * wave + 8 * (e >> 2) + 4 * hf + (e & 3);
+      if (key < a.T) {
+        const int64_t off = ((int64_t)key * a.hkv + g) * D + 32 * nb + (lane & 31);
+        a.dk[off] = (__bf16)(dkacc[nb][e] * a.scale);
+        a.dv[off] = (__bf16)dvacc[nb][e];
+      }
+    }
+}
+
+template <int D, int NW>
+static void launch_dkdv_t(const AttnArgs& args, hipStream_t st) {
+  AttnArgs b = args;
+  b.n_tiles = (b.T + 32 * NW - 1) / (32 * NW);
+  ProfScope prof("attn_bwd_dkdv", st);
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, NW>), dim3(b.n_tiles * b.hkv), dim3(NW * 64), 0, st, b);
+}
+
+void dkdv_launch(const AttnArgs& a, int D, hipStream_t st) {
+  if (D == 128) launch_dkdv_t<128, 4>(a, st);
+  else launch_dkdv_t<64, 4>(a, st);
+}
+
+}  // namespace uly

@@ -34,6 +34,12 @@ struct AttnArgs {
   float* delta;  // bwd: rowsum(dO * O) with the bf16 O, [B][hq][S]
   float* pdp;    // bwd: sum_j P_ij dP_ij = dO_i . O_i with the exact O, [B][hq][S]
   float* lse2;   // bwd: LSE * log2(e) (+inf for rows without keys), [B][hq][S]
+  // bwd: exact fp16 copies of q, k, v, dout (the backward's products run in
+  // fp16, whose 11-bit significand rounds P and dS 8x finer than bf16)
+  _Float16* q16;
+  _Float16* k16;
+  _Float16* v16;
+  _Float16* do16;
   const float* sink;
   float* dsink_part;  // [hq][n_part]
   float* dsink;
@@ -49,6 +55,14 @@ struct AttnArgs {
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// The same product on fp16 operands.  Operand fragments travel as 16-bit
+// bit patterns (bf16x8); the backward kernels fill them with fp16 data.
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x16 mfma32h(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
 // Values of the partner lane (l ^ 32) combined with this lane's: both
@@ -124,10 +138,13 @@ __device__ __forceinline__ bool decode_qtile(const AttnArgs& a, int& qt, int& h)
 //
 // A tile of R rows x D bf16 sits in LDS row-major, 2*D bytes a row, its
 // 16-byte slots XOR-swizzled per row: logical slot c of row r lives at
-// physical slot c ^ swz(r).  swz is a bijection on 16 consecutive rows, so
-// the 16-byte operand reads of 16 rows (one slot each) hit distinct banks,
-// and maps rows 4q..4q+3 to distinct slot pairs, so the transposing reads
-// (four rows, 32 bytes each) do too.  Tiles arrive by global_load_lds
+// physical slot c ^ swz(r).  The LDS has 64 four-byte banks (256 bytes a
+// pass).  A 16-byte operand read serves 16 lanes a pass: 16 consecutive rows,
+// one slot each, so swz is a bijection on 16 rows.  A transposing read serves
+// 32 lanes a pass: four consecutive rows, 64 bytes each, so swz also sends
+// those four rows' 64-byte groups to the four distinct 64-byte bank groups
+// (bits 2-3 of the slot for D=128; the row parity and bit 2 for D=64).
+// Measured with SQ_LDS_BANK_CONFLICT: zero conflicts for both read forms.  Tiles arrive by global_load_lds
 // (16 bytes a lane, lane l at byte 16*l of the instruction's 1 KiB): no
 // registers, no VALU beyond the address.  One tile serves both operand
 // forms:
@@ -147,7 +164,7 @@ template <int D>
 struct Swz {
   static constexpr int kSlots = D / 8;  // 16-byte slots per row
   __device__ static __forceinline__ int f(int r) {
-    return D == 128 ? 2 * (r & 7) + ((r >> 3) & 1) : 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
+    return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
   }
   // byte offset of logical 16-byte slot c of row r
   __device__ static __forceinline__ int off(int r, int c) { return r * (2 * D) + ((c ^ f(r)) << 4); }
@@ -156,9 +173,10 @@ struct Swz {
 // Issue the direct-to-LDS loads of a R x D tile: rows row0 .. row0+R-1 of a
 // global matrix with row stride ld elements (rows at or past row_end are
 // clamped to row_end - 1: finite data that the masks then ignore).
-template <int D, int R, int NW>
-__device__ __forceinline__ void tile_load_lds(char* lds, const __bf16* g, int ld, int row0,
+template <int D, int R, int NW, typename E>
+__device__ __forceinline__ void tile_load_lds(char* lds, const E* g, int ld, int row0,
                                               int row_end, int wave, int lane) {
+  static_assert(sizeof(E) == 2, "16-bit elements");
   constexpr int kInstr = R * D * 2 / 1024;  // 1 KiB per wave instruction
   static_assert(kInstr % NW == 0, "tile must split evenly over the waves");
 #pragma unroll
@@ -168,8 +186,8 @@ __device__ __forceinline__ void tile_load_lds(char* lds, const __bf16* g, int ld
     const int r = pos / Swz<D>::kSlots;
     const int c = (pos % Swz<D>::kSlots) ^ Swz<D>::f(r);
     const int row = min(row0 + r, row_end - 1);
-    const __bf16* src = g + (int64_t)row * ld + c * 8;
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + i * 1024), 16, 0, 0);
+    const char* src = reinterpret_cast<const char*>(g) + ((int64_t)row * ld + c * 8) * 2;
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(lds + i * 1024), 16, 0, 0);
   }
 }
 
@@ -309,14 +327,33 @@ __device__ __forceinline__ bf16x8 tr_frag(const __bf16* lds, int r0, int d0, int
 }
 
 // B operand held in registers: row `row` (or zeros), columns 16 s + 8 hf ..
-template <int D>
-__device__ __forceinline__ void load_row_frags(bf16x8 (&f)[D / 16], const __bf16* rowp, bool valid, int lane) {
+template <int D, typename E>
+__device__ __forceinline__ void load_row_frags(bf16x8 (&f)[D / 16], const E* rowp, bool valid, int lane) {
+  static_assert(sizeof(E) == 2, "16-bit elements");
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
     u32x4 x = {0, 0, 0, 0};
     if (valid) x = *reinterpret_cast<const u32x4*>(rowp + 16 * s + 8 * (lane >> 5));
     f[s] = __builtin_bit_cast(bf16x8, x);
   }
+}
+
+// fp16 round-to-nearest-even from fp32, two at a time (v_cvt_pk_f16_f32).
+__device__ __forceinline__ u32 pack_f16x2(float lo, float hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  const f32x2 x = {lo, hi};
+  return __builtin_bit_cast(u32, __builtin_convertvector(x, f16x2));
+}
+
+// Eight accumulator values as an fp16 operand (slot order as acc_frag).
+__device__ __forceinline__ bf16x8 acc_frag_h(const f32x16& c, int ii) {
+  u32x4 x;
+  x[0] = pack_f16x2(c[8 * ii + 0], c[8 * ii + 1]);
+  x[1] = pack_f16x2(c[8 * ii + 2], c[8 * ii + 3]);
+  x[2] = pack_f16x2(c[8 * ii + 4], c[8 * ii + 5]);
+  x[3] = pack_f16x2(c[8 * ii + 6], c[8 * ii + 7]);
+  return __builtin_bit_cast(bf16x8, x);
 }
 
 // Sum of eight bf16 values (v_dot2_f32_bf16 against ones): the row sum of

@@ -45,6 +45,9 @@ __device__ __forceinline__ u32 pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(u32, p);
 }
 
+// Saturate to the finite fp16 range before an fp16 conversion.
+__device__ __forceinline__ float clamp_f16(float x) { return fminf(fmaxf(x, -65504.f), 65504.f); }
+
 __device__ __forceinline__ float bf16_lo(u32 w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(u32 w) { return __uint_as_float(w & 0xffff0000u); }
 

@@ -15,6 +15,7 @@ hipError_t segments_launch(const void* pos, int pos_bytes, int P, int B, int S, 
                            int32_t* n_seqs, int32_t* max_len, hipStream_t st);
 hipError_t attn_fwd_launch(const AttnArgs& a, int D, hipStream_t st);
 hipError_t attn_bwd_launch(const AttnArgs& a, int D, hipStream_t st);
+void dkdv_launch(const AttnArgs& a, int D, hipStream_t st);  // part of attn_bwd_launch
 
 // When profiling is on, prof_mark(name, st) records a HIP event on `st`
 // before a kernel launch and prof_mark(nullptr, st) after it.
