@@ -83,6 +83,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=2,
                     help="query heads of rank 0 the CPU oracle baseline runs")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches instead of a captured HIP graph of the step")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -121,17 +123,39 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    log(f"timing {args.steps} steps")
-    uly.profile_start(max_launches=64 * args.steps * len(case.variants) * P + 64)
+    # The whole step is captured once into a HIP graph and replayed: about 50
+    # kernel launches per step, many of them a few microseconds long, so
+    # launch gaps would otherwise dominate the small workloads.
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+
+    log(f"timing {args.steps} steps ({'HIP graph' if graph is not None else 'eager'})")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        if graph is not None:
+            graph.replay()
+        else:
+            step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    ms_per_step = 1e3 * elapsed / args.steps
+
+    # per-kernel durations: the same steps launched eagerly, each kernel
+    # bracketed by HIP events on the stream it runs on
+    log(f"per-kernel timing over {args.steps} eager steps")
+    uly.profile_start(max_launches=64 * args.steps * len(case.variants) * P + 64)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
     uly.profile_stop()
     kern = uly.profile_report()
-    ms_per_step = 1e3 * elapsed / args.steps
 
     docs = docs_of(inp)
     credit = kernel_credit(case, docs)
@@ -195,6 +219,7 @@ def main():
         "config": {"workload": case.name, "P": P, "B": case.B, "S": case.S, "Hq": case.Hq,
                    "Hkv": case.Hkv, "D": case.D, "layers": [v.name for v in case.variants],
                    "sink": case.sink, "packed_docs": len(docs) if inp.doc_lengths else None},
+        "execution": "hip_graph" if graph is not None else "eager",
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "attn_tflops": round(attn_tflops, 2),
         "pack_gbps": round(rows.get("a2a_pack", {}).get("gbps", 0.0), 1),

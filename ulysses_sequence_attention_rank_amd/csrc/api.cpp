@@ -97,10 +97,26 @@ uly::AttnArgs make_args(const void* q, const void* k, const void* v, const float
   a.causal = causal ? 1 : 0;
   a.wl = wl;
   a.wr = wr;
+  a.nsplit = 1;
   return a;
 }
 
 constexpr int kDsinkParts = 64;
+
+size_t align256(size_t x);
+
+// fp32 partial sums of the split backward kernels (they run one after the
+// other, so one buffer serves both): max(dQ partials, dK+dV partials) plus
+// the split sums of P dP.
+size_t split_part_bytes(int B, int S, int hq, int hkv, int D) {
+  const size_t T = (size_t)B * S;
+  const int nq = uly::qtile_splits(B, S, hq), nk = uly::dkdv_splits(B, S, hkv);
+  size_t part = 0;
+  if (nq > 1) part = (size_t)nq * T * hq * D * 4;
+  if (nk > 1 && (size_t)nk * 2 * T * hkv * D * 4 > part) part = (size_t)nk * 2 * T * hkv * D * 4;
+  const size_t pdp = nq > 1 ? (size_t)nq * T * hq * 4 : 0;
+  return align256(part) + align256(pdp);
+}
 
 // ---- optional per-kernel timing: a HIP event before and after each launch
 struct Prof {
@@ -259,7 +275,8 @@ size_t ulysses_attn_bwd_workspace_bytes(int B, int S, int hq, int hkv, int D) {
   // fp16 copies of q, dout ([B][S][hq][D]) and k, v ([B][S][hkv][D])
   const size_t rows = align256((size_t)B * S * hq * sizeof(float));
   const size_t qsz = align256((size_t)B * S * hq * D * 2), kvsz = align256((size_t)B * S * hkv * D * 2);
-  return 3 * rows + align256((size_t)hq * kDsinkParts * sizeof(float)) + 2 * qsz + 2 * kvsz;
+  return 3 * rows + align256((size_t)hq * kDsinkParts * sizeof(float)) + 2 * qsz + 2 * kvsz +
+         split_part_bytes(B, S, hq, hkv, D);
 }
 
 int ulysses_attn_bwd(const void* q, const void* k, const void* v, const void* out,
@@ -304,6 +321,15 @@ int ulysses_attn_bwd(const void* q, const void* k, const void* v, const void* ou
   a.do16 = (_Float16*)(h16 + qsz);
   a.k16 = (_Float16*)(h16 + 2 * qsz);
   a.v16 = (_Float16*)(h16 + 2 * qsz + kvsz);
+  {
+    const size_t T = (size_t)B * S;
+    const int nq = uly::qtile_splits(B, S, hq), nk = uly::dkdv_splits(B, S, hkv);
+    size_t part = 0;
+    if (nq > 1) part = (size_t)nq * T * hq * D * 4;
+    if (nk > 1 && (size_t)nk * 2 * T * hkv * D * 4 > part) part = (size_t)nk * 2 * T * hkv * D * 4;
+    a.part = (float*)(h16 + 2 * qsz + 2 * kvsz);
+    a.part_pdp = (float*)(h16 + 2 * qsz + 2 * kvsz + align256(part));
+  }
   a.n_part = kDsinkParts;
   return hip_status(uly::attn_bwd_launch(a, D, (hipStream_t)stream), "ulysses_attn_bwd launch");
 }

@@ -150,18 +150,20 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(AttnArgs a) {
   const _Float16* kbase = a.k16 + (int64_t)g * D;
   const _Float16* vbase = a.v16 + (int64_t)g * D;
   const int ld = a.hkv * D;
-  const int n_iter = (wg_hi - wg_lo + kBK - 1) / kBK;
-  if (n_iter > 0) {
-    tile_load_lds<D, kBK, NW>(smem, kbase, ld, wg_lo, a.T, wave, lane);
-    tile_load_lds<D, kBK, NW>(smem + TILE, vbase, ld, wg_lo, a.T, wave, lane);
+  // this split's share of the key tiles
+  int it_lo, it_hi;
+  split_range((wg_hi - wg_lo + kBK - 1) / kBK, blockIdx.y, a.nsplit, it_lo, it_hi);
+  if (it_lo < it_hi) {
+    tile_load_lds<D, kBK, NW>(smem, kbase, ld, wg_lo + it_lo * kBK, a.T, wave, lane);
+    tile_load_lds<D, kBK, NW>(smem + TILE, vbase, ld, wg_lo + it_lo * kBK, a.T, wave, lane);
   }
 
-  for (int it = 0; it < n_iter; ++it) {
-    const int cur = it & 1;
+  for (int it = it_lo; it < it_hi; ++it) {
+    const int cur = (it - it_lo) & 1;
     const int k0 = wg_lo + it * kBK;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (it + 1 < n_iter) {
+    if (it + 1 < it_hi) {
       char* nxt = smem + (cur ^ 1) * STAGE;
       tile_load_lds<D, kBK, NW>(nxt, kbase, ld, k0 + kBK, a.T, wave, lane);
       tile_load_lds<D, kBK, NW>(nxt + TILE, vbase, ld, k0 + kBK, a.T, wave, lane);
@@ -201,6 +203,22 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(AttnArgs a) {
   }
 
   pdp = halves_sum(pdp);
+  if (a.nsplit > 1) {  // fp32 partials, summed by dq_reduce_kernel
+    if (qvalid && want_pdp && hf == 0)
+      a.part_pdp[(int64_t)blockIdx.y * a.T * a.hq + lse_index(a, qrow, h)] = pdp;
+    if (qvalid) {
+      float* row = a.part + ((int64_t)blockIdx.y * a.T * a.hq + (int64_t)qrow * a.hq + h) * D;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 w = {dqacc[nb][4 * i + 0], dqacc[nb][4 * i + 1], dqacc[nb][4 * i + 2],
+                           dqacc[nb][4 * i + 3]};
+          *reinterpret_cast<f32x4*>(row + 32 * nb + 8 * i + 4 * hf) = w;
+        }
+    }
+    return;
+  }
   if (qvalid && want_pdp && hf == 0) a.pdp[lse_index(a, qrow, h)] = pdp;
   if (qvalid) {
     __bf16* row = a.out + ((int64_t)qrow * a.hq + h) * D;
@@ -213,6 +231,27 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(AttnArgs a) {
         w[1] = pack_bf16x2(dqacc[nb][4 * i + 2] * a.scale, dqacc[nb][4 * i + 3] * a.scale);
         *reinterpret_cast<u32x2*>(row + 32 * nb + 8 * i + 4 * hf) = w;
       }
+  }
+}
+
+// dQ = scale * sum of the split partials (fixed order), to bf16; the same for
+// the rows' sum of P dP.
+__global__ __launch_bounds__(256) void dq_reduce_kernel(AttnArgs a, int64_t n) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i < n) {
+    f32x4 q = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < a.nsplit; ++s) q += *reinterpret_cast<const f32x4*>(a.part + s * n + i);
+    u32x2 w;
+    w[0] = pack_bf16x2(q[0] * a.scale, q[1] * a.scale);
+    w[1] = pack_bf16x2(q[2] * a.scale, q[3] * a.scale);
+    *reinterpret_cast<u32x2*>(a.out + i) = w;
+  }
+  const int64_t rows = (int64_t)a.T * a.hq;
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (a.sink != nullptr && r < rows) {
+    float p = 0.f;
+    for (int s = 0; s < a.nsplit; ++s) p += a.part_pdp[s * rows + r];
+    a.pdp[r] = p;
   }
 }
 
@@ -239,8 +278,17 @@ static hipError_t launch_bwd_t(const AttnArgs& args, hipStream_t st) {
     b.n_tiles = (a.T + 32 * NW - 1) / (32 * NW);
     const int groups = b.n_tiles * a.hkv;
     const int blocks = ((groups + kXcds - 1) / kXcds) * kXcds * a.G;
-    ProfScope prof("attn_bwd_dq", st);
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, NW>), dim3(blocks), dim3(NW * 64), 0, st, b);
+    b.nsplit = qtile_splits(a.B, a.S, a.hq);
+    {
+      ProfScope prof("attn_bwd_dq", st);
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<D, NW>), dim3(blocks, b.nsplit), dim3(NW * 64), 0, st, b);
+    }
+    if (b.nsplit > 1) {
+      ProfScope prof("attn_bwd_dq_reduce", st);
+      const int64_t n = (int64_t)a.T * a.hq * D;
+      const int64_t items = n / 4 > (int64_t)a.T * a.hq ? n / 4 : (int64_t)a.T * a.hq;
+      hipLaunchKernelGGL(dq_reduce_kernel, dim3((items + 255) / 256), dim3(256), 0, st, b, n);
+    }
   }
   if (a.sink != nullptr) {
     ProfScope prof("attn_bwd_dsink", st);

@@ -153,20 +153,28 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(AttnArgs a) {
       __builtin_amdgcn_global_load_lds(src, (lds_void*)(buf + 2 * SM::kTile + wave * kBK * 4), 4, 0, 0);
     }
   };
+  int it_end = n_iter;  // set to this split's end below
   auto step = [&](int it, const char* buf, char* nxt) {
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile `it` have landed
     __syncthreads();                // everyone's have, and the other stage is free
-    if (it + 1 < n_iter) issue(it + 1, nxt);
+    if (it + 1 < it_end) issue(it + 1, nxt);
     dkdv_tile<D, NW>(a, buf, kvs, dkacc, dvacc, tile_q0(it), full_lo, full_hi, qlo, qhi, wave, lane);
   };
 
-  if (n_iter > 0) issue(0, st0);
-  for (int it = 0; it < n_iter; it += 2) {
+  // this split's share of the (head, query tile) iterations
+  int it_lo, it_hi;
+  split_range(n_iter, blockIdx.y, a.nsplit, it_lo, it_hi);
+  it_end = it_hi;
+  if (it_lo < it_hi) issue(it_lo, st0);
+  for (int it = it_lo; it < it_hi; it += 2) {
     step(it, st0, st1);
-    if (it + 1 < n_iter) step(it + 1, st1, st0);
+    if (it + 1 < it_hi) step(it + 1, st1, st0);
   }
 
   // dK, dV: lane holds column d = 32 nb + l % 32 of key rows 8 i + 4 hf + j
+  const int64_t plane = (int64_t)a.T * a.hkv * D;
+  float* pk = a.part + blockIdx.y * plane;
+  float* pv = a.part + (a.nsplit + blockIdx.y) * plane;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -174,18 +182,50 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(AttnArgs a) {
       const int key = k0 + 32 * wave + 8 * (e >> 2) + 4 * hf + (e & 3);
       if (key < a.T) {
         const int64_t off = ((int64_t)key * a.hkv + g) * D + 32 * nb + (lane & 31);
-        a.dk[off] = (__bf16)(dkacc[nb][e] * a.scale);
-        a.dv[off] = (__bf16)dvacc[nb][e];
+        if (a.nsplit == 1) {
+          a.dk[off] = (__bf16)(dkacc[nb][e] * a.scale);
+          a.dv[off] = (__bf16)dvacc[nb][e];
+        } else {
+          pk[off] = dkacc[nb][e];
+          pv[off] = dvacc[nb][e];
+        }
       }
     }
+}
+
+// dK = scale * sum of the split partials, dV = sum (fixed order), to bf16.
+__global__ __launch_bounds__(256) void dkdv_reduce_kernel(AttnArgs a, int64_t n) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  f32x4 k = {0.f, 0.f, 0.f, 0.f}, v = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < a.nsplit; ++s) {
+    k += *reinterpret_cast<const f32x4*>(a.part + s * n + i);
+    v += *reinterpret_cast<const f32x4*>(a.part + (a.nsplit + s) * n + i);
+  }
+  u32x2 wk, wv;
+  wk[0] = pack_bf16x2(k[0] * a.scale, k[1] * a.scale);
+  wk[1] = pack_bf16x2(k[2] * a.scale, k[3] * a.scale);
+  wv[0] = pack_bf16x2(v[0], v[1]);
+  wv[1] = pack_bf16x2(v[2], v[3]);
+  *reinterpret_cast<u32x2*>(a.dk + i) = wk;
+  *reinterpret_cast<u32x2*>(a.dv + i) = wv;
 }
 
 template <int D, int NW>
 static void launch_dkdv_t(const AttnArgs& args, hipStream_t st) {
   AttnArgs b = args;
   b.n_tiles = (b.T + 32 * NW - 1) / (32 * NW);
-  ProfScope prof("attn_bwd_dkdv", st);
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, NW>), dim3(b.n_tiles * b.hkv), dim3(NW * 64), 0, st, b);
+  b.nsplit = dkdv_splits(b.B, b.S, b.hkv);
+  {
+    ProfScope prof("attn_bwd_dkdv", st);
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, NW>), dim3(b.n_tiles * b.hkv, b.nsplit), dim3(NW * 64),
+                       0, st, b);
+  }
+  if (b.nsplit > 1) {
+    ProfScope prof("attn_bwd_dkdv_reduce", st);
+    const int64_t n = (int64_t)b.T * b.hkv * D;
+    hipLaunchKernelGGL(dkdv_reduce_kernel, dim3((n / 4 + 255) / 256), dim3(256), 0, st, b, n);
+  }
 }
 
 void dkdv_launch(const AttnArgs& a, int D, hipStream_t st) {

@@ -51,6 +51,12 @@ struct AttnArgs {
   int causal, wl, wr;
   int n_tiles;       // query tiles (fwd, dq) or key tiles (dkdv)
   int n_part;
+  // Split of the reduction dimension over blockIdx.y when the natural grid is
+  // too small for the GPU: partial sums in fp32, summed by a fixed-order
+  // reduce kernel (so results stay deterministic).
+  int nsplit;
+  float* part;       // dq: [nsplit][T][hq][D]; dkdv: dK then dV, [nsplit][T][hkv][D]
+  float* part_pdp;   // dq: [nsplit][B][hq][S]
 };
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -211,6 +217,12 @@ __device__ __forceinline__ bf16x8 swz_tr(const char* lds, int r0, int d0, int la
   typedef short i16x8 __attribute__((ext_vector_type(8)));
   const i16x8 x = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8, x);
+}
+
+// Contiguous share [lo, hi) of n iterations for split s of ns.
+__device__ __forceinline__ void split_range(int n, int s, int ns, int& lo, int& hi) {
+  lo = (int)(((int64_t)n * s) / ns);
+  hi = (int)(((int64_t)n * (s + 1)) / ns);
 }
 
 // ---------------------------------------------------------------- LDS tiles

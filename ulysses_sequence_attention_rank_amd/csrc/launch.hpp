@@ -17,6 +17,36 @@ hipError_t attn_fwd_launch(const AttnArgs& a, int D, hipStream_t st);
 hipError_t attn_bwd_launch(const AttnArgs& a, int D, hipStream_t st);
 void dkdv_launch(const AttnArgs& a, int D, hipStream_t st);  // part of attn_bwd_launch
 
+// Number of splits of a reduction dimension for a kernel whose natural grid
+// has `wgs` work-groups of which `per_round` are resident at once on MI355X
+// (256 CUs times the work-groups a CU holds): the split count (at most 4, at
+// most one per 64-row tile) that minimises the rounds of resident work-groups
+// per unit of work, ceil(wgs * ns / per_round) / ns; ties go to fewer splits.
+// A function of the sizes only, so the workspace query and the launch agree.
+inline int choose_splits(long wgs, long tiles, long per_round) {
+  if (wgs <= 0) return 1;
+  int best = 1;
+  double best_t = (double)((wgs + per_round - 1) / per_round);
+  for (long ns = 2; ns <= 4 && ns <= tiles; ++ns) {
+    const double t = (double)((wgs * ns + per_round - 1) / per_round) / (double)ns;
+    if (t < best_t - 1e-9) {
+      best_t = t;
+      best = (int)ns;
+    }
+  }
+  return best;
+}
+// dK/dV: 128-key work-groups, one per CU (its LDS footprint)
+inline int dkdv_splits(int B, int S, int hkv) {
+  const long T = (long)B * S;
+  return choose_splits(((T + 127) / 128) * hkv, (T + 63) / 64, 256);
+}
+// dQ: 128-query work-groups, two per CU
+inline int qtile_splits(int B, int S, int hq) {
+  const long T = (long)B * S;
+  return choose_splits(((T + 127) / 128) * hq, (T + 63) / 64, 512);
+}
+
 // When profiling is on, prof_mark(name, st) records a HIP event on `st`
 // before a kernel launch and prof_mark(nullptr, st) after it.
 void prof_mark(const char* name, hipStream_t st);
