@@ -185,8 +185,7 @@ def main():
         rows["a2a_pack"]["frac_of_peak"] = rows["a2a_pack"]["gbps"] / PEAK_HBM_GBPS
     if "a2a_unpack" in kern:
         rows["a2a_unpack"]["gbps"] = unpack_bytes * nl / (kern["a2a_unpack"][1] * 1e-3) / 1e9
-    attn_ms = sum(kern[k][1] for k in ("attn_fwd", "attn_bwd_pre", "attn_bwd_dkdv",
-                                        "attn_bwd_dq", "attn_bwd_dsink") if k in kern)
+    attn_ms = sum(v[1] for k, v in kern.items() if k.startswith("attn_"))
     attn_tflops = step_flops * args.steps / (attn_ms * 1e-3) / 1e12
 
     # roofline of the kernel that takes the most time in the step

@@ -128,15 +128,25 @@ int ulysses_cu_seqlens_from_positions(const void* pos_shards, int pos_bytes, int
  * denominator, not multiplied by softmax_scale, with no value vector.
  *   O_i = sum_j softmax_j(scale * q_i . k_j) v_j,  LSE_i = ln(sum_j e^{s_ij} + e^{sink})
  * Rows that see no key and have no sink get O = 0 and LSE = -inf.
+ * workspace: device memory of at least ulysses_attn_fwd_workspace_bytes()
+ *   bytes, 256-byte aligned, owned by the caller (may be NULL when that is
+ *   zero); its contents on entry do not matter and on return are unspecified.
  * Supported: D in {64, 128}; window_left, window_right >= -1.
  * Errors: ULY_ERR_NULL, ULY_ERR_SHAPE, ULY_ERR_HEADS (hq % hkv),
  *   ULY_ERR_UNSUPPORTED (D, window < -1, cu_seqlens given without n_seqs),
- *   ULY_ERR_ALIGN.
+ *   ULY_ERR_CAPACITY (workspace too small), ULY_ERR_ALIGN.
  * ---------------------------------------------------------------------- */
 int ulysses_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
-                     const float* sink, const int32_t* cu_seqlens, const int32_t* n_seqs, int B,
-                     int S, int hq, int hkv, int D, float softmax_scale, int causal,
-                     int window_left, int window_right, void* stream);
+                     const float* sink, const int32_t* cu_seqlens, const int32_t* n_seqs,
+                     void* workspace, size_t workspace_bytes, int B, int S, int hq, int hkv, int D,
+                     float softmax_scale, int causal, int window_left, int window_right,
+                     void* stream);
+
+/* Bytes of device workspace ulysses_attn_fwd needs for these sizes: zero when
+ * one pass of query tiles fills the GPU, else room for fp32 partial outputs of
+ * the key-range splits that small problems are cut into (merged, with the
+ * sink, by a second kernel).  Zero also for sizes ulysses_attn_fwd rejects. */
+size_t ulysses_attn_fwd_workspace_bytes(int B, int S, int hq, int hkv, int D);
 
 /* Bytes of device workspace ulysses_attn_bwd needs for these sizes. */
 size_t ulysses_attn_bwd_workspace_bytes(int B, int S, int hq, int hkv, int D);

@@ -33,6 +33,7 @@ def declared():
 def test_header_declares_the_boundary():
     assert declared() == {"ulysses_a2a_pack", "ulysses_a2a_unpack",
                           "ulysses_cu_seqlens_from_positions", "ulysses_attn_fwd",
+                          "ulysses_attn_fwd_workspace_bytes",
                           "ulysses_attn_bwd_workspace_bytes", "ulysses_attn_bwd",
                           "ulysses_profile_start", "ulysses_profile_stop",
                           "ulysses_profile_report", "ulysses_last_error"}
@@ -74,11 +75,12 @@ def test_segments_argument_errors(lib):
     assert f(_p(A + 4), 8, 2, 1, 8, cu, 9, n, m, None) == ALIGN
 
 
-def _fwd(lib, q=A, k=2 * A, v=3 * A, out=4 * A, lse=5 * A, sink=None, cu=None, n=None,
-         B=1, S=64, hq=4, hkv=2, D=128, scale=0.125, causal=1, wl=-1, wr=-1):
+def _fwd(lib, q=A, k=2 * A, v=3 * A, out=4 * A, lse=5 * A, sink=None, cu=None, n=None, ws=None,
+         ws_bytes=0, B=1, S=64, hq=4, hkv=2, D=128, scale=0.125, causal=1, wl=-1, wr=-1):
     return lib.ulysses_attn_fwd(_p(q), _p(k), _p(v), _p(out), _p(lse),
                                 None if sink is None else _p(sink), None if cu is None else _p(cu),
-                                None if n is None else _p(n), B, S, hq, hkv, D,
+                                None if n is None else _p(n), None if ws is None else _p(ws),
+                                ctypes.c_size_t(ws_bytes), B, S, hq, hkv, D,
                                 ctypes.c_float(scale), causal, wl, wr, None)
 
 
@@ -93,6 +95,18 @@ def test_attn_fwd_argument_errors(lib):
     assert _fwd(lib, q=0) == NULL
     assert _fwd(lib, hq=6, hkv=4) == HEADS
     assert b"query heads" in lib.ulysses_last_error()
+
+
+def test_attn_fwd_workspace(lib):
+    # a small problem (few query tiles) is split over its keys and needs a workspace
+    need = lib.ulysses_attn_fwd_workspace_bytes(1, 4096, 6, 6, 128)
+    assert need > 4096 * 6 * 128 * 4
+    assert _fwd(lib, S=4096, hq=6, hkv=6) == NULL                            # none given
+    assert _fwd(lib, S=4096, hq=6, hkv=6, ws=6 * A, ws_bytes=need - 1) == CAP
+    assert _fwd(lib, S=4096, hq=6, hkv=6, ws=6 * A + 16, ws_bytes=need) == ALIGN
+    # a problem that fills the GPU in one pass needs none
+    assert lib.ulysses_attn_fwd_workspace_bytes(1, 131072, 7, 1, 128) == 0
+    assert lib.ulysses_attn_fwd_workspace_bytes(1, 4096, 6, 6, 96) == 0
 
 
 def test_attn_bwd_argument_errors(lib):

@@ -19,7 +19,7 @@ import torch
 __all__ = [
     "UlyssesError", "lib_path", "load", "a2a_pack", "a2a_unpack", "a2a_pack_into",
     "a2a_unpack_into", "cu_seqlens_from_positions", "attn_fwd", "attn_bwd",
-    "attn_bwd_workspace_bytes", "profile_start", "profile_stop", "profile_report",
+    "attn_fwd_workspace_bytes", "attn_bwd_workspace_bytes", "profile_start", "profile_stop", "profile_report",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -31,7 +31,7 @@ _STATUS = {0: "ULY_OK", -1: "ULY_ERR_NULL", -2: "ULY_ERR_SHAPE", -3: "ULY_ERR_HE
            -7: "ULY_ERR_HIP"}
 
 EXPORTS = ("ulysses_a2a_pack", "ulysses_a2a_unpack", "ulysses_cu_seqlens_from_positions",
-           "ulysses_attn_fwd", "ulysses_attn_bwd_workspace_bytes", "ulysses_attn_bwd",
+           "ulysses_attn_fwd", "ulysses_attn_fwd_workspace_bytes", "ulysses_attn_bwd_workspace_bytes", "ulysses_attn_bwd",
            "ulysses_profile_start", "ulysses_profile_stop", "ulysses_profile_report",
            "ulysses_last_error")
 
@@ -59,7 +59,9 @@ def load():
     lib.ulysses_a2a_pack.argtypes = [vp, vp] + [i32] * 6 + [vp]
     lib.ulysses_a2a_unpack.argtypes = [vp, vp] + [i32] * 6 + [vp]
     lib.ulysses_cu_seqlens_from_positions.argtypes = [vp, i32, i32, i32, i32, vp, i32, vp, vp, vp]
-    lib.ulysses_attn_fwd.argtypes = [vp] * 8 + [i32] * 5 + [f32] + [i32] * 3 + [vp]
+    lib.ulysses_attn_fwd.argtypes = [vp] * 9 + [sz] + [i32] * 5 + [f32] + [i32] * 3 + [vp]
+    lib.ulysses_attn_fwd_workspace_bytes.argtypes = [i32] * 5
+    lib.ulysses_attn_fwd_workspace_bytes.restype = sz
     lib.ulysses_attn_bwd_workspace_bytes.argtypes = [i32] * 5
     lib.ulysses_attn_bwd_workspace_bytes.restype = sz
     lib.ulysses_attn_bwd.argtypes = [vp] * 14 + [sz] + [i32] * 5 + [f32] + [i32] * 3 + [vp]
@@ -191,8 +193,12 @@ def _shapes(q, k):
     return B, S, hq, hkv, D
 
 
+def attn_fwd_workspace_bytes(B, S, hq, hkv, D) -> int:
+    return int(load().ulysses_attn_fwd_workspace_bytes(B, S, hq, hkv, D))
+
+
 def attn_fwd(q, k, v, *, sink=None, cu_seqlens=None, n_seqs=None, causal=True, window_left=-1,
-             window_right=-1, softmax_scale=None, out=None, lse=None):
+             window_right=-1, softmax_scale=None, out=None, lse=None, workspace=None):
     """One rank's attention: q ``[B, S, hq, D]``, k/v ``[B, S, hkv, D]`` bf16.
     Returns (out bf16 ``[B, S, hq, D]``, lse fp32 ``[B, hq, S]``)."""
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -206,9 +212,12 @@ def attn_fwd(q, k, v, *, sink=None, cu_seqlens=None, n_seqs=None, causal=True, w
         lse = torch.empty((B, hq, S), dtype=torch.float32, device=q.device)
     if sink is not None:
         _dev(sink, "sink", torch.float32)
+    if workspace is None:
+        need = attn_fwd_workspace_bytes(B, S, hq, hkv, D)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
     _check(load().ulysses_attn_fwd(
-        _p(q), _p(k), _p(v), _p(out), _p(lse), _p(sink), _p(cu_seqlens), _p(n_seqs), B, S, hq, hkv,
-        D, float(softmax_scale), int(bool(causal)), int(window_left), int(window_right),
+        _p(q), _p(k), _p(v), _p(out), _p(lse), _p(sink), _p(cu_seqlens), _p(n_seqs), _p(workspace),
+        0 if workspace is None else workspace.numel(), B, S, hq, hkv, D, float(softmax_scale), int(bool(causal)), int(window_left), int(window_right),
         _stream(q.device)), "ulysses_attn_fwd")
     return out, lse
 

@@ -251,21 +251,42 @@ int ulysses_cu_seqlens_from_positions(const void* pos_shards, int pos_bytes, int
                     "ulysses_cu_seqlens_from_positions launch");
 }
 
+// Forward workspace: the split partials, O_s fp32 [nsplit][T][hq][D], then the
+// running max and sum of each split, fp32 [2][nsplit][B][hq][S].
+size_t ulysses_attn_fwd_workspace_bytes(int B, int S, int hq, int hkv, int D) {
+  if (B <= 0 || S <= 0 || hq <= 0 || hkv <= 0 || (D != 64 && D != 128)) return 0;
+  const int ns = uly::fwd_splits(B, S, hq, uly::fwd_block_rows(B, S, hq, D));
+  if (ns == 1) return 0;
+  const size_t rows = (size_t)B * S * hq;
+  return align256((size_t)ns * rows * D * 4) + align256(2 * (size_t)ns * rows * 4);
+}
+
 int ulysses_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
-                     const float* sink, const int32_t* cu_seqlens, const int32_t* n_seqs, int B,
-                     int S, int hq, int hkv, int D, float softmax_scale, int causal,
-                     int window_left, int window_right, void* stream) {
+                     const float* sink, const int32_t* cu_seqlens, const int32_t* n_seqs,
+                     void* workspace, size_t workspace_bytes, int B, int S, int hq, int hkv, int D,
+                     float softmax_scale, int causal, int window_left, int window_right,
+                     void* stream) {
   int rc = check_attn(q, k, v, cu_seqlens, n_seqs, B, S, hq, hkv, D, softmax_scale, window_left,
                       window_right);
   if (rc) return rc;
   if (!out || !lse) return fail(ULY_ERR_NULL, "NULL out/lse");
+  const size_t need = ulysses_attn_fwd_workspace_bytes(B, S, hq, hkv, D);
+  if (need > 0 && !workspace) return fail(ULY_ERR_NULL, "NULL workspace (%zu bytes needed)", need);
+  if (workspace_bytes < need)
+    return fail(ULY_ERR_CAPACITY, "workspace of %zu bytes < %zu needed", workspace_bytes, need);
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
-      !aligned(lse, 4) || !aligned(sink, 4) || !aligned(cu_seqlens, 4) || !aligned(n_seqs, 4))
-    return fail(ULY_ERR_ALIGN, "q/k/v/out need 16-byte alignment, lse/sink/cu 4-byte");
+      !aligned(lse, 4) || !aligned(sink, 4) || !aligned(cu_seqlens, 4) || !aligned(n_seqs, 4) ||
+      !aligned(workspace, 256))
+    return fail(ULY_ERR_ALIGN, "q/k/v/out need 16-byte alignment, lse/sink/cu 4-byte, workspace 256-byte");
   uly::AttnArgs a = make_args(q, k, v, sink, cu_seqlens, n_seqs, B, S, hq, hkv, softmax_scale,
                               causal, window_left, window_right);
   a.out = (__bf16*)out;
   a.lse = lse;
+  if (need > 0) {
+    a.nsplit = uly::fwd_splits(B, S, hq, uly::fwd_block_rows(B, S, hq, D));
+    a.part = (float*)workspace;
+    a.part_pdp = (float*)((char*)workspace + align256((size_t)a.nsplit * B * S * hq * D * 4));
+  }
   return hip_status(uly::attn_fwd_launch(a, D, (hipStream_t)stream), "ulysses_attn_fwd launch");
 }
 

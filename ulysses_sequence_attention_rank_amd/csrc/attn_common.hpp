@@ -56,7 +56,7 @@ struct AttnArgs {
   // reduce kernel (so results stay deterministic).
   int nsplit;
   float* part;       // dq: [nsplit][T][hq][D]; dkdv: dK then dV, [nsplit][T][hkv][D]
-  float* part_pdp;   // dq: [nsplit][B][hq][S]
+  float* part_pdp;   // dq: [nsplit][B][hq][S]; fwd: running max then sum, [2][nsplit][B][hq][S]
 };
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {

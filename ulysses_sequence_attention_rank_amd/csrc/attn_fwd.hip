@@ -62,19 +62,21 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnArgs a) {
   const __bf16* kbase = a.k + (int64_t)g * D;
   const __bf16* vbase = a.v + (int64_t)g * D;
   const int ld = a.hkv * D;
-  const int n_iter = (wg_hi - wg_lo + kBK - 1) / kBK;
-  if (n_iter > 0) {
-    tile_load_lds<D, kBK, NW>(smem, kbase, ld, wg_lo, a.T, wave, lane);
-    tile_load_lds<D, kBK, NW>(smem + TILE, vbase, ld, wg_lo, a.T, wave, lane);
+  // this split's share of the key tiles
+  int it_lo, it_hi;
+  split_range((wg_hi - wg_lo + kBK - 1) / kBK, blockIdx.y, a.nsplit, it_lo, it_hi);
+  if (it_lo < it_hi) {
+    tile_load_lds<D, kBK, NW>(smem, kbase, ld, wg_lo + it_lo * kBK, a.T, wave, lane);
+    tile_load_lds<D, kBK, NW>(smem + TILE, vbase, ld, wg_lo + it_lo * kBK, a.T, wave, lane);
   }
   const f32x16 zero = {};
 
-  for (int it = 0; it < n_iter; ++it) {
-    const int cur = it & 1;
+  for (int it = it_lo; it < it_hi; ++it) {
+    const int cur = (it - it_lo) & 1;
     const int k0 = wg_lo + it * kBK;
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile `it` have landed
     __syncthreads();                // everyone's have, and tile it-1 is no longer read
-    if (it + 1 < n_iter) {
+    if (it + 1 < it_hi) {
       char* nxt = smem + (cur ^ 1) * STAGE;
       tile_load_lds<D, kBK, NW>(nxt, kbase, ld, k0 + kBK, a.T, wave, lane);
       tile_load_lds<D, kBK, NW>(nxt + TILE, vbase, ld, k0 + kBK, a.T, wave, lane);
@@ -153,6 +155,32 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnArgs a) {
       }
   }
 
+  if (a.nsplit > 1) {
+    // this split's unnormalised output, running max (log2 domain) and sum,
+    // merged by attn_fwd_merge_kernel
+    const int64_t rows = (int64_t)a.T * a.hq;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float l_tot = halves_sum(l_run[qb]);
+      if (!qvalid[qb]) continue;
+      float* orow = a.part + ((int64_t)blockIdx.y * rows + (int64_t)qrow[qb] * a.hq + h) * D;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 w = {oacc[qb][nb][4 * i + 0], oacc[qb][nb][4 * i + 1], oacc[qb][nb][4 * i + 2],
+                           oacc[qb][nb][4 * i + 3]};
+          *reinterpret_cast<f32x4*>(orow + 32 * nb + 8 * i + 4 * hf) = w;
+        }
+      if (hf == 0) {
+        const int idx = lse_index(a, qrow[qb], h);
+        a.part_pdp[(int64_t)blockIdx.y * rows + idx] = m_run[qb];
+        a.part_pdp[(int64_t)(a.nsplit + blockIdx.y) * rows + idx] = l_tot;
+      }
+    }
+    return;
+  }
+
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     // both halves hold partial sums of the same row; fold in the sink
@@ -186,14 +214,57 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnArgs a) {
   }
 }
 
+// Merge of the split partials of one (row, head): with M = max(m_s, sink),
+// Z = sum_s l_s 2^(m_s - M) + 2^(sink - M), O = sum_s O_s 2^(m_s - M) / Z and
+// LSE = (M + log2 Z) ln 2.  One thread per 4 output columns.
+template <int D>
+__global__ __launch_bounds__(256) void attn_fwd_merge_kernel(AttnArgs a) {
+  const int64_t rows = (int64_t)a.T * a.hq;
+  const int64_t idx4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t r = idx4 / (D / 4);  // flattened (token, head) row
+  const int c = (int)(idx4 % (D / 4)) * 4;
+  if (r >= rows) return;
+  const int t = (int)(r / a.hq), h = (int)(r % a.hq);
+  const int li = lse_index(a, t, h);
+  float m = -INFINITY;
+  for (int s = 0; s < a.nsplit; ++s) m = fmaxf(m, a.part_pdp[s * rows + li]);
+  const float s2 = a.sink != nullptr ? a.sink[h] * 1.4426950408889634f : -INFINITY;
+  const float mf = fmaxf(m, s2);
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  float z = 0.f;
+  if (mf != -INFINITY) {
+    for (int s = 0; s < a.nsplit; ++s) {
+      const float ms = a.part_pdp[s * rows + li];
+      if (ms == -INFINITY) continue;
+      const float w = exp2f(ms - mf);
+      z += a.part_pdp[(a.nsplit + s) * rows + li] * w;
+      o += *reinterpret_cast<const f32x4*>(a.part + (s * rows + r) * D + c) * w;
+    }
+    if (a.sink != nullptr) z += exp2f(s2 - mf);
+  }
+  const float inv = z > 0.f ? 1.f / z : 0.f;
+  u32x2 w;
+  w[0] = pack_bf16x2(o[0] * inv, o[1] * inv);
+  w[1] = pack_bf16x2(o[2] * inv, o[3] * inv);
+  *reinterpret_cast<u32x2*>(a.out + r * D + c) = w;
+  if (c == 0) a.lse[li] = z > 0.f ? (mf + __log2f(z)) * 0.6931471805599453f : -INFINITY;
+}
+
 template <int D, int NW, int QB>
 static hipError_t launch_fwd_t(const AttnArgs& args, hipStream_t st) {
   AttnArgs a = args;
   a.n_tiles = (a.T + 32 * QB * NW - 1) / (32 * QB * NW);
   const int groups = a.n_tiles * a.hkv;
   const int blocks = ((groups + kXcds - 1) / kXcds) * kXcds * a.G;
-  ProfScope prof("attn_fwd", st);
-  hipLaunchKernelGGL((attn_fwd_kernel<D, NW, QB>), dim3(blocks), dim3(NW * 64), 0, st, a);
+  {
+    ProfScope prof("attn_fwd", st);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, NW, QB>), dim3(blocks, a.nsplit), dim3(NW * 64), 0, st, a);
+  }
+  if (a.nsplit > 1) {
+    ProfScope prof("attn_fwd_merge", st);
+    const int64_t items = (int64_t)a.T * a.hq * (D / 4);
+    hipLaunchKernelGGL(attn_fwd_merge_kernel<D>, dim3((items + 255) / 256), dim3(256), 0, st, a);
+  }
   return hipGetLastError();
 }
 
@@ -201,8 +272,8 @@ static hipError_t launch_fwd_t(const AttnArgs& args, hipStream_t st) {
 // product) still fit two waves per SIMD; D=128 takes one block per wave.
 hipError_t attn_fwd_launch(const AttnArgs& a, int D, hipStream_t st) {
   if (D == 128) return launch_fwd_t<128, 4, 1>(a, st);
-  const bool big = (long)((a.T + 255) / 256) * a.hq >= 512;
-  return big ? launch_fwd_t<64, 4, 2>(a, st) : launch_fwd_t<64, 4, 1>(a, st);
+  return fwd_block_rows(a.B, a.S, a.hq, D) == 256 ? launch_fwd_t<64, 4, 2>(a, st)
+                                                  : launch_fwd_t<64, 4, 1>(a, st);
 }
 
 }  // namespace uly

@@ -47,6 +47,17 @@ inline int qtile_splits(int B, int S, int hq) {
   return choose_splits(((T + 127) / 128) * hq, (T + 63) / 64, 512);
 }
 
+// Forward: query tiles of `bm` rows, two work-groups per CU.
+inline int fwd_splits(int B, int S, int hq, int bm) {
+  const long T = (long)B * S;
+  return choose_splits(((T + bm - 1) / bm) * hq, (T + 63) / 64, 512);
+}
+// Rows of a forward query tile for head dim D (the launcher's variant choice).
+inline int fwd_block_rows(int B, int S, int hq, int D) {
+  if (D == 128) return 128;
+  return (long)(((long)B * S + 255) / 256) * hq >= 512 ? 256 : 128;
+}
+
 // When profiling is on, prof_mark(name, st) records a HIP event on `st`
 // before a kernel launch and prof_mark(nullptr, st) after it.
 void prof_mark(const char* name, hipStream_t st);

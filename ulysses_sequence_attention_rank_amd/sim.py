@@ -18,7 +18,7 @@ from typing import Optional, Sequence
 import torch
 
 from . import (a2a_pack_into, a2a_unpack_into, attn_bwd, attn_bwd_workspace_bytes, attn_fwd,
-               cu_seqlens_from_positions)
+               attn_fwd_workspace_bytes, cu_seqlens_from_positions)
 
 
 @dataclasses.dataclass
@@ -91,8 +91,9 @@ def allocate(q_seq, k_seq, v_seq, dout_seq, pos_seq, sink) -> StepBuffers:
     b.cu = torch.empty(B * S + 1, dtype=torch.int32, device=dev)
     b.n_seqs = torch.empty(1, dtype=torch.int32, device=dev)
     b.max_len = torch.empty(1, dtype=torch.int32, device=dev)
-    b.workspace = torch.empty(attn_bwd_workspace_bytes(B, S, hq, hkv, D), dtype=torch.uint8,
-                              device=dev)
+    # the forward and backward run one after the other on one stream: one workspace
+    ws = max(attn_bwd_workspace_bytes(B, S, hq, hkv, D), attn_fwd_workspace_bytes(B, S, hq, hkv, D))
+    b.workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
     return b
 
 
@@ -110,7 +111,7 @@ def forward(b: StepBuffers, *, causal: bool, window_left: int = -1, window_right
         attn_fwd(b.q_head[r], b.k_head[r], b.v_head[r], sink=sk, cu_seqlens=b.cu,
                  n_seqs=b.n_seqs, causal=causal, window_left=window_left,
                  window_right=window_right, softmax_scale=softmax_scale, out=b.o_head[r],
-                 lse=b.lse[r])
+                 lse=b.lse[r], workspace=b.workspace)
     a2a_unpack_into(b.o_head, b.o_seq, b.P)
 
 
