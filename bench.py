@@ -31,8 +31,43 @@ PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E
 DEFAULT_WORKLOAD = 2         # S=4096, 12 heads, D=128, full + causal layers, P=2
 
 
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "traffic.json")
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_digest():
+    """sha256 over the kernel sources and the build flags: HBM traffic taken with
+    rocprofv3 counters is reported only while this digest is unchanged."""
+    import hashlib
+    h = hashlib.sha256()
+    pkg = os.path.join(ROOT, "ulysses_sequence_attention_rank_amd")
+    files = [os.path.join(pkg, "build.py")]
+    csrc = os.path.join(pkg, "csrc")
+    files += [os.path.join(csrc, f) for f in sorted(os.listdir(csrc))]
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_per_launch(workload, kernel):
+    """HBM bytes per launch of `kernel` on `workload` from the committed counter
+    summary (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads for
+    the pack kernel's known bytes), or None if absent or taken on other sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_digest():
+        return None
+    k = rec.get("workloads", {}).get(workload, {}).get(kernel)
+    return None if k is None else k["bytes_per_launch"]
 
 
 def visible_pairs(doc_lengths, causal, wl, wr):
@@ -81,11 +116,21 @@ def main():
     ap.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD, choices=[1, 2, 3, 4, 5],
                     help="which of the five simulated workloads (default: the S=4096 one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=2,
-                    help="query heads of rank 0 the CPU oracle baseline runs")
+    ap.add_argument("--cpu-heads", type=int, default=None,
+                    help="query heads of rank 0 the CPU oracle baseline runs (default: every "
+                         "head of every rank, the whole step, for the S<=4096 workloads; one KV "
+                         "group of rank 0 for the S=32768 one; none for the larger ones)")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches instead of a captured HIP graph of the step")
+    ap.add_argument("--rocprof-summary", metavar="DIR",
+                    help="no GPU run: summarise rocprofv3 CSV output under DIR (trace/, sq/, "
+                         "fetch/, write/ and commands.txt) of a run of this script on --workload "
+                         "into profiles/, and record the measured HBM traffic per kernel")
     args = ap.parse_args()
+
+    if args.rocprof_summary:
+        rocprof_summary(args.rocprof_summary, args.workload)
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU: the P Ulysses ranks are simulated in memory "
@@ -194,13 +239,19 @@ def main():
     achieved = per_launch_flops / (kern[dom][1] / kern[dom][0] * 1e-3) / 1e12
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic_per_launch(case.name, dom),
                 "flops_per_launch": per_launch_flops,
                 "avg_launch_ms": round(kern[dom][1] / kern[dom][0], 5)}
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(inp, args.cpu_heads)
+        if args.cpu_heads is not None:
+            cpu = cpu_baseline(inp, ranks=[0], n_heads=args.cpu_heads)
+        elif case.S <= 4096:
+            cpu = cpu_baseline(inp, ranks=list(range(P)), n_heads=case.Hq // P)
+        elif case.S <= 32768:
+            cpu = cpu_baseline(inp, ranks=[0], n_heads=case.Hq // case.Hkv)
 
     line = {
         "metric": METRIC,
@@ -231,42 +282,157 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(inp, n_heads):
-    """The fp64 CPU oracle, as it stands, on a bounded sample of the same workload:
-    rank 0's first ``n_heads`` query heads (with their KV heads), full sequence,
-    every layer type, forward and backward."""
-    import torch
+def _rocprof_name(full):
+    """Short name of a kernel as rocprofv3 prints it, matching the names the
+    library's per-kernel timer uses."""
+    import re
+    if "to_f16_kernel" in full:
+        return "attn_bwd_f16"
+    if "at::native" in full:
+        return "torch (buffer fill)"
+    m = re.search(r"uly::(\w+?)_kernel(<[^>]*>)?", full)
+    if not m:
+        return full
+    name, targs = m.group(1), m.group(2) or ""
+    if name == "permute":
+        return "a2a_pack" if "true" in targs else "a2a_unpack"
+    if name == "segments":
+        return "cu_seqlens"
+    if name in ("dq_reduce", "dkdv_reduce"):
+        return "attn_bwd_" + name
+    if name == "to_f16":
+        return "attn_bwd_f16"
+    if name in ("dsink_partial", "dsink_final"):
+        return "attn_bwd_" + name
+    return name
 
+
+def rocprof_summary(d, workload):
+    """Write profiles/<workload>_kernels.md from rocprofv3 CSV files and record
+    per-launch HBM traffic in profiles/traffic.json."""
+    import collections
+    import csv
+    import glob
+    from ulysses_inputs import CONFIGS
+    case = CONFIGS[workload]
+
+    def rows(sub, suffix):
+        fs = sorted(glob.glob(os.path.join(d, sub, "**", f"*{suffix}"), recursive=True))
+        if not fs:
+            raise SystemExit(f"no *{suffix} under {os.path.join(d, sub)}")
+        with open(fs[0]) as f:
+            return list(csv.DictReader(f))
+
+    def counters(sub):
+        agg = collections.defaultdict(lambda: collections.defaultdict(list))
+        for r in rows(sub, "counter_collection.csv"):
+            agg[_rocprof_name(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in agg.items()}
+
+    stats = rows("trace", "kernel_stats.csv")
+    sq, fe, wr = counters("sq"), counters("fetch"), counters("write")
+    with open(os.path.join(d, "commands.txt")) as f:
+        commands = [ln.rstrip() for ln in f if ln.strip()]
+
+    # scale factors: the pack kernel moves a known number of bytes per launch
+    # (Q, K, V in the forward and dO in the backward; each element read once
+    # and written once)
+    elem_q = case.B * case.S * case.Hq * case.D
+    elem_kv = case.B * case.S * case.Hkv * case.D
+    pack_bytes = 2 * (2 * elem_q + 2 * elem_kv) / 4
+    f_scale = pack_bytes / (fe["a2a_pack"]["FETCH_SIZE"] * 1024)
+    w_scale = pack_bytes / (wr["a2a_pack"]["WRITE_SIZE"] * 1024)
+
+    traffic = {}
+    for k in sorted(k for k in fe if not k.startswith("torch")):
+        if k in wr:
+            traffic[k] = {"fetch_kib": round(fe[k]["FETCH_SIZE"], 1),
+                          "write_kib": round(wr[k]["WRITE_SIZE"], 1),
+                          "bytes_per_launch": round(1024 * (fe[k]["FETCH_SIZE"] * f_scale +
+                                                            wr[k]["WRITE_SIZE"] * w_scale))}
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        rec = {}
+    if rec.get("source_sha256") != kernel_source_digest():
+        rec = {"source_sha256": kernel_source_digest(), "workloads": {}}
+    rec["note"] = ("HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per "
+                   "dispatch), each scaled by bytes/counter of the pack kernel in the same run")
+    rec["workloads"][case.name] = {"fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+                                   **traffic}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+        f.write("\n")
+
+    out = os.path.join(PROFILES, f"{case.name}_kernels.md")
+    with open(out, "w") as f:
+        f.write(f"# rocprofv3 per-kernel summary: simulated Ulysses step, workload {case.name}\n\n")
+        f.write(f"P={case.P}, B={case.B}, S={case.S}, Hq/Hkv={case.Hq}/{case.Hkv}, D={case.D}, "
+                f"layers {[v.name for v in case.variants]}, sink={case.sink}.\n\n")
+        f.write("Commands (run from /tmp with TMPDIR=/tmp; R = repository root):\n\n")
+        for c in commands:
+            f.write(f"    {c}\n")
+        f.write("\n## kernel trace (--kernel-trace --stats)\n\n")
+        f.write("| kernel | short name | calls | avg us | total us | % |\n|---|---|---|---|---|---|\n")
+        for r in stats:
+            f.write(f"| `{r['Name']}` | {_rocprof_name(r['Name'])} | {r['Calls']} | "
+                    f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['TotalDurationNs']) / 1e3:.1f} | "
+                    f"{float(r['Percentage']):.1f} |\n")
+        cols = sorted({c for v in sq.values() for c in v})
+        f.write("\n## counters, average per dispatch (FETCH_SIZE / WRITE_SIZE in KiB)\n\n")
+        f.write("| kernel | " + " | ".join(cols) + " | FETCH_SIZE | WRITE_SIZE | HBM MB/launch |\n")
+        f.write("|" + "---|" * (len(cols) + 4) + "\n")
+        for k in sorted(sq):
+            vals = " | ".join(f"{sq[k].get(c, float('nan')):.0f}" for c in cols)
+            t = traffic.get(k)
+            tail = (f"{t['fetch_kib']} | {t['write_kib']} | {t['bytes_per_launch'] / 1e6:.2f}"
+                    if t else " | | ")
+            f.write(f"| {k} | {vals} | {tail} |\n")
+        f.write(f"\nCounter scale (pack kernel, {pack_bytes / 1e6:.2f} MB read and written per "
+                f"launch): FETCH_SIZE x {f_scale:.4f}, WRITE_SIZE x {w_scale:.4f}.\n")
+    print(open(out).read())
+
+
+def cpu_baseline(inp, ranks, n_heads):
+    """The fp64 CPU oracle, as it stands, on a bounded sample of the same workload:
+    the first ``n_heads`` query heads (with their KV heads) of each rank in
+    ``ranks``, full sequence, every layer type, forward and backward."""
     import oracle
     from ulysses_inputs import seq_shards
     c = inp.case
     P, D = c.P, c.D
     G = c.Hq // c.Hkv
-    n_heads = max(G, (n_heads // G) * G)
+    n_heads = min(c.Hq // P, max(G, (n_heads // G) * G))
     nkv = n_heads // G
-    qh = oracle.pack(seq_shards(inp.q, P))[0][:, :, :n_heads].contiguous()
-    kh = oracle.pack(seq_shards(inp.k, P))[0][:, :, :nkv].contiguous()
-    vh = oracle.pack(seq_shards(inp.v, P))[0][:, :, :nkv].contiguous()
-    dh = oracle.pack(seq_shards(inp.dout, P))[0][:, :, :n_heads].contiguous()
-    sk = None if inp.sink is None else inp.sink[:n_heads].contiguous()
+    packed = [oracle.pack(seq_shards(x, P)) for x in (inp.q, inp.k, inp.v, inp.dout)]
     cu = None
     if inp.doc_lengths is not None:
         cu, _, _ = oracle.segments(oracle.gather_positions(seq_shards(inp.positions, P)))
     docs = docs_of(inp)
     flops = 0
-    log(f"cpu baseline: oracle on rank 0, {n_heads} query heads, {oracle.num_threads()} threads")
+    log(f"cpu baseline: oracle on ranks {ranks}, {n_heads} query heads each, "
+        f"{oracle.num_threads()} threads")
     t0 = time.perf_counter()
-    for v in c.variants:
-        kw = dict(sink=sk, cu=cu, causal=v.causal, window_left=v.window_left,
-                  window_right=v.window_right)
-        oracle.attn_fwd(qh, kh, vh, **kw)
-        oracle.attn_bwd(qh, kh, vh, dh, **kw)
-        flops += 12 * D * visible_pairs(docs, v.causal, v.window_left, v.window_right) * n_heads
+    for r in ranks:
+        qh = packed[0][r][:, :, :n_heads].contiguous()
+        kh = packed[1][r][:, :, :nkv].contiguous()
+        vh = packed[2][r][:, :, :nkv].contiguous()
+        dh = packed[3][r][:, :, :n_heads].contiguous()
+        sk = None if inp.sink is None else inp.sink[r * (c.Hq // P):][:n_heads].contiguous()
+        for v in c.variants:
+            kw = dict(sink=sk, cu=cu, causal=v.causal, window_left=v.window_left,
+                      window_right=v.window_right)
+            oracle.attn_fwd(qh, kh, vh, **kw)
+            oracle.attn_bwd(qh, kh, vh, dh, **kw)
+            flops += 12 * D * visible_pairs(docs, v.causal, v.window_left, v.window_right) * n_heads
     dt = time.perf_counter() - t0
+    whole = len(ranks) == P and n_heads == c.Hq // P
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle", "seconds": round(dt, 2),
-            "sample": (f"rank 0, {n_heads} of {c.hq} query heads ({nkv} KV head), full sequence "
-                       f"S={c.S}, layers {[v.name for v in c.variants]}, fwd+bwd in fp64")}
+            "sample": (f"{'the whole step: ' if whole else ''}ranks {ranks}, {n_heads} of "
+                       f"{c.Hq // P} query heads each ({nkv} KV head(s)), full sequence S={c.S}, "
+                       f"layers {[v.name for v in c.variants]}, attention fwd+bwd in fp64")}
 
 
 if __name__ == "__main__":

@@ -225,119 +225,6 @@ __device__ __forceinline__ void split_range(int n, int s, int ns, int& lo, int& 
   hi = (int)(((int64_t)n * (s + 1)) / ns);
 }
 
-// ---------------------------------------------------------------- LDS tiles
-//
-// Natural tile: kBK rows x D, row stride D + 8 elements (16 bytes of padding
-// keep the 16-byte A-operand reads of 32 consecutive rows on distinct banks).
-// Transposed tile: rows in groups of four, [kBK/4][D][4], with the 16-byte
-// slot (d/2) XOR-swizzled by (d/16) % 8 so that both the staging writes and
-// the operand reads hit distinct banks.
-
-template <int D>
-struct Tile {
-  static constexpr int kNatStride = D + 8;
-  static constexpr int kNatElems = kBK * kNatStride;
-  static constexpr int kTrElems = kBK * D;
-
-  __device__ static __forceinline__ int tr_slot(int d2) { return d2 ^ ((d2 >> 3) & 7); }
-
-  // byte offset of 8-byte (4 x bf16) slot [group g][d] in a transposed tile
-  __device__ static __forceinline__ int tr_off(int g, int d) {
-    return g * (D * 8) + tr_slot(d >> 1) * 16 + (d & 1) * 8;
-  }
-};
-
-// Staging of one kBK x D tile from global (row stride `ld` elements) through
-// registers into LDS, in both layouts.  Rows at or past `row_end` are zero.
-template <int D, int NT>
-struct TileLoader {
-  static constexpr int kChunks = kBK * D / 8;                // 16-byte chunks in a tile
-  static constexpr int kNat = (kChunks + NT - 1) / NT;      // per thread
-  static constexpr int kUnits = (kBK / 4) * (D / 8);         // 4 rows x 8 columns
-  static constexpr int kTr = (kUnits + NT - 1) / NT;
-
-  u32x4 nat[kNat];
-  u32x4 tr[kTr][4];
-
-  __device__ __forceinline__ void load_nat(const __bf16* base, int ld, int row0, int row_end, int tid) {
-#pragma unroll
-    for (int c = 0; c < kNat; ++c) {
-      const int ch = tid + c * NT;
-      const int r = ch / (D / 8), col = (ch % (D / 8)) * 8;
-      u32x4 x = {0, 0, 0, 0};
-      if ((kChunks % NT == 0 || ch < kChunks) && row0 + r < row_end)
-        x = *reinterpret_cast<const u32x4*>(base + (int64_t)(row0 + r) * ld + col);
-      nat[c] = x;
-    }
-  }
-  __device__ __forceinline__ void store_nat(__bf16* lds, int tid) const {
-#pragma unroll
-    for (int c = 0; c < kNat; ++c) {
-      const int ch = tid + c * NT;
-      if (kChunks % NT == 0 || ch < kChunks) {
-        const int r = ch / (D / 8), col = (ch % (D / 8)) * 8;
-        *reinterpret_cast<u32x4*>(lds + r * Tile<D>::kNatStride + col) = nat[c];
-      }
-    }
-  }
-  __device__ __forceinline__ void load_tr(const __bf16* base, int ld, int row0, int row_end, int tid) {
-#pragma unroll
-    for (int c = 0; c < kTr; ++c) {
-      const int u = tid + c * NT;
-      const int g = u / (D / 8), col = (u % (D / 8)) * 8;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        u32x4 x = {0, 0, 0, 0};
-        if ((kUnits % NT == 0 || u < kUnits) && row0 + 4 * g + r < row_end)
-          x = *reinterpret_cast<const u32x4*>(base + (int64_t)(row0 + 4 * g + r) * ld + col);
-        tr[c][r] = x;
-      }
-    }
-  }
-  // 4 rows x 8 columns -> 8 columns x 4 rows, two columns per 16-byte store
-  __device__ __forceinline__ void store_tr(__bf16* lds, int tid) const {
-    char* base = reinterpret_cast<char*>(lds);
-#pragma unroll
-    for (int c = 0; c < kTr; ++c) {
-      const int u = tid + c * NT;
-      if (kUnits % NT == 0 || u < kUnits) {
-        const int g = u / (D / 8), col = (u % (D / 8)) * 8;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {  // word w holds columns col+2w (low) and col+2w+1 (high)
-          u32x4 o;
-          o[0] = __builtin_amdgcn_perm(tr[c][1][w], tr[c][0][w], 0x05040100u);
-          o[1] = __builtin_amdgcn_perm(tr[c][3][w], tr[c][2][w], 0x05040100u);
-          o[2] = __builtin_amdgcn_perm(tr[c][1][w], tr[c][0][w], 0x07060302u);
-          o[3] = __builtin_amdgcn_perm(tr[c][3][w], tr[c][2][w], 0x07060302u);
-          const int d2 = (col >> 1) + w;
-          *reinterpret_cast<u32x4*>(base + g * (D * 8) + Tile<D>::tr_slot(d2) * 16) = o;
-        }
-      }
-    }
-  }
-};
-
-// A operand from a natural tile: rows row0 + (l % 32), columns 16 s + 8 hf ..
-template <int D>
-__device__ __forceinline__ bf16x8 nat_frag(const __bf16* lds, int row0, int s, int lane) {
-  const u32x4 x = *reinterpret_cast<const u32x4*>(
-      lds + (row0 + (lane & 31)) * Tile<D>::kNatStride + 16 * s + 8 * (lane >> 5));
-  return __builtin_bit_cast(bf16x8, x);
-}
-
-// A operand from a transposed tile for the 16-row step starting at row r0
-// (a multiple of 16): column d = d0 + (l % 32), rows in the slot order above.
-template <int D>
-__device__ __forceinline__ bf16x8 tr_frag(const __bf16* lds, int r0, int d0, int lane) {
-  const char* base = reinterpret_cast<const char*>(lds);
-  const int g = (r0 >> 2) + (lane >> 5);
-  const int d = d0 + (lane & 31);
-  const u32x2 lo = *reinterpret_cast<const u32x2*>(base + Tile<D>::tr_off(g, d));
-  const u32x2 hi = *reinterpret_cast<const u32x2*>(base + Tile<D>::tr_off(g + 2, d));
-  const u32x4 x = {lo[0], lo[1], hi[0], hi[1]};
-  return __builtin_bit_cast(bf16x8, x);
-}
-
 // B operand held in registers: row `row` (or zeros), columns 16 s + 8 hf ..
 template <int D, typename E>
 __device__ __forceinline__ void load_row_frags(bf16x8 (&f)[D / 16], const E* rowp, bool valid, int lane) {
@@ -366,20 +253,6 @@ __device__ __forceinline__ bf16x8 acc_frag_h(const f32x16& c, int ii) {
   x[2] = pack_f16x2(c[8 * ii + 4], c[8 * ii + 5]);
   x[3] = pack_f16x2(c[8 * ii + 6], c[8 * ii + 7]);
   return __builtin_bit_cast(bf16x8, x);
-}
-
-// Sum of eight bf16 values (v_dot2_f32_bf16 against ones): the row sum of
-// exactly the probabilities the P V product uses.
-__device__ __forceinline__ float sum_bf16x8(bf16x8 x) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const bf16x2 p = {x[2 * i], x[2 * i + 1]};
-    s = __builtin_amdgcn_fdot2_f32_bf16(p, one, s, false);
-  }
-  return s;
 }
 
 // Eight accumulator values (C rows 8(2ii) + 4hf + j and 8(2ii+1) + 4hf + j)
