@@ -160,7 +160,11 @@ size_t ulysses_attn_bwd_workspace_bytes(int B, int S, int hq, int hkv, int D);
  *     dsink_h = -sum_i exp(sink_h - LSE_i) * sum_d dout_i,d out_i,d
  *   workspace: device memory of at least ulysses_attn_bwd_workspace_bytes()
  *   bytes, 256-byte aligned, owned by the caller; its contents on entry do
- *   not matter and on return are unspecified.
+ *   not matter and on return are unspecified (it holds per-row statistics,
+ *   fp16 copies of q, k, v, dout and, on small problems, fp32 partial sums).
+ * Precision: the products run in fp16 (fp32 accumulation) on fp16 copies of
+ *   q, k, v and dout, which are exact for every bf16 value of magnitude up to
+ *   65504; larger magnitudes saturate to +-65504.
  * Errors: as ulysses_attn_fwd, plus ULY_ERR_CAPACITY (workspace too small)
  *   and ULY_ERR_NULL (sink and dsink not both NULL or both set).
  */
