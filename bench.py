@@ -219,7 +219,8 @@ def main():
         if k in kern:
             rows[k]["tflops"] = fl / (kern[k][1] * 1e-3) / 1e12
             rows[k]["frac_of_peak"] = rows[k]["tflops"] / PEAK_BF16_TFLOPS
-    # layout permutation: every element read once and written once
+    # layout permutation inside the step (every element read once and written
+    # once; the step's buffers may sit in the Infinity Cache)
     elem_q = case.B * case.S * case.Hq * case.D
     elem_kv = case.B * case.S * case.Hkv * case.D
     pack_bytes = 2 * 2 * (2 * elem_q + 2 * elem_kv)   # Q, dO (Hq) and K, V (Hkv), per layer
@@ -227,9 +228,9 @@ def main():
     nl = len(case.variants) * args.steps
     if "a2a_pack" in kern:
         rows["a2a_pack"]["gbps"] = pack_bytes * nl / (kern["a2a_pack"][1] * 1e-3) / 1e9
-        rows["a2a_pack"]["frac_of_peak"] = rows["a2a_pack"]["gbps"] / PEAK_HBM_GBPS
     if "a2a_unpack" in kern:
         rows["a2a_unpack"]["gbps"] = unpack_bytes * nl / (kern["a2a_unpack"][1] * 1e-3) / 1e9
+    perm = measure_permutation(case, b, dev)
     attn_ms = sum(v[1] for k, v in kern.items() if k.startswith("attn_"))
     attn_tflops = step_flops * args.steps / (attn_ms * 1e-3) / 1e12
 
@@ -272,14 +273,54 @@ def main():
         "execution": "hip_graph" if graph is not None else "eager",
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "attn_tflops": round(attn_tflops, 2),
-        "pack_gbps": round(rows.get("a2a_pack", {}).get("gbps", 0.0), 1),
-        "pack_frac_of_hbm": round(rows.get("a2a_pack", {}).get("frac_of_peak", 0.0), 4),
+        "pack_gbps": perm["pack_gbps"],
+        "pack_frac_of_hbm": round(perm["pack_gbps"] / PEAK_HBM_GBPS, 4),
+        "unpack_gbps": perm["unpack_gbps"],
+        "permutation": perm,
         "kernels": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in r.items()}
                     for k, r in rows.items()},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def measure_permutation(case, b, dev, launches=40):
+    """HBM throughput of the layout permutation on its own: Q, K and V packed
+    in one launch (and dQ, dK, dV unpacked in one), back to back, rotating over
+    enough buffer sets that the 256 MB Infinity Cache cannot hold them; one
+    HIP event pair around all launches."""
+    import math
+
+    import torch
+
+    import ulysses_sequence_attention_rank_amd as uly
+    P = case.P
+    seq0 = [b.q_seq, b.k_seq, b.v_seq]
+    set_bytes = sum(t.numel() * t.element_size() for t in seq0)  # read once, written once
+    n_sets = max(1, math.ceil(1.5 * 2 ** 30 / (2 * set_bytes)))
+    seqs = [seq0] + [[t.clone() for t in seq0] for _ in range(n_sets - 1)]
+    heads = [[torch.empty((P, t.shape[1], t.shape[2] * P, t.shape[3] // P, t.shape[4]),
+                          dtype=t.dtype, device=dev) for t in ss] for ss in seqs]
+    out = {"tensors": "Q, K, V in one launch", "launches": launches, "buffer_sets": n_sets,
+           "bytes_per_launch": 2 * set_bytes}
+    for name, fn, src, dst in (("pack", uly.a2a_pack_multi_into, seqs, heads),
+                               ("unpack", uly.a2a_unpack_multi_into, heads, seqs)):
+        for i in range(n_sets):
+            fn(src[i], dst[i], P)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(launches):
+            fn(src[i % n_sets], dst[i % n_sets], P)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / launches
+        out[f"{name}_us_per_launch"] = round(1e3 * ms, 2)
+        out[f"{name}_gbps"] = round(2 * set_bytes / (ms * 1e-3) / 1e9, 1)
+    del seqs[1:], heads
+    torch.cuda.empty_cache()
+    return out
 
 
 def _rocprof_name(full):

@@ -75,6 +75,20 @@ int ulysses_a2a_pack(const void* seq_shards, void* head_shards, int P, int B, in
 int ulysses_a2a_unpack(const void* head_shards, void* seq_shards, int P, int B, int S, int H,
                        int D, int elem_bytes, void* stream);
 
+/* The same permutation for n (1..4) tensors of one exchange in one launch
+ * (the forward's all-to-all carries Q, K and V together, the backward's dQ, dK
+ * and dV: [accelerate#4209] reply on the four all-to-all call sites).
+ * seq_shards, head_shards and H are HOST arrays of n entries: device
+ * pointers, and the head count of each tensor (K and V have Hkv heads under
+ * GQA); P, B, S, D and elem_bytes are shared.  Each tensor is checked as in
+ * ulysses_a2a_pack; no destination may overlap a source or another
+ * destination.  Errors: as above, ULY_ERR_UNSUPPORTED for n outside 1..4 or
+ * overlapping buffers, ULY_ERR_NULL for a NULL array. */
+int ulysses_a2a_pack_multi(int n, const void* const* seq_shards, void* const* head_shards,
+                           const int* H, int P, int B, int S, int D, int elem_bytes, void* stream);
+int ulysses_a2a_unpack_multi(int n, const void* const* head_shards, void* const* seq_shards,
+                             const int* H, int P, int B, int S, int D, int elem_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * cu_seqlens / max_len from the gathered position_ids ([accelerate#4209],
  * comment on the flash-attention kwargs: a padding-free collator's

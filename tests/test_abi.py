@@ -31,7 +31,8 @@ def declared():
 
 
 def test_header_declares_the_boundary():
-    assert declared() == {"ulysses_a2a_pack", "ulysses_a2a_unpack",
+    assert declared() == {"ulysses_a2a_pack", "ulysses_a2a_unpack", "ulysses_a2a_pack_multi",
+                          "ulysses_a2a_unpack_multi",
                           "ulysses_cu_seqlens_from_positions", "ulysses_attn_fwd",
                           "ulysses_attn_fwd_workspace_bytes",
                           "ulysses_attn_bwd_workspace_bytes", "ulysses_attn_bwd",
@@ -63,6 +64,24 @@ def test_pack_argument_errors(lib):
     assert f(_p(A), _p(A + 64), 2, 1, 8, 4, 4, 2, None) == UNSUP     # overlap
     assert b"overlap" in lib.ulysses_last_error()
     assert lib.ulysses_a2a_unpack(_p(A), _p(2 * A), 2, 1, 8, 3, 4, 2, None) == HEADS
+
+
+def test_pack_multi_argument_errors(lib):
+    def call(n=2, srcs=(A, 3 * A), dsts=(2 * A, 4 * A), H=(4, 2), P=2, S=8, D=2, eb=2, fn=None):
+        VP = ctypes.c_void_p * max(n, 1)
+        src = VP(*[ctypes.c_void_p(x) for x in srcs][:max(n, 1)])
+        dst = VP(*[ctypes.c_void_p(x) for x in dsts][:max(n, 1)])
+        hh = (ctypes.c_int * max(n, 1))(*H[:max(n, 1)])
+        f = fn or lib.ulysses_a2a_pack_multi
+        return f(n, src, dst, hh, P, 1, S, D, eb, None)
+    assert call(n=0) == UNSUP
+    assert call(n=5, srcs=(A,) * 5, dsts=(2 * A,) * 5, H=(2,) * 5) == UNSUP
+    assert call(H=(4, 3)) == HEADS                    # 3 heads over 2 ranks
+    assert call(dsts=(2 * A, 2 * A)) == UNSUP         # two destinations overlap
+    assert call(dsts=(2 * A, 3 * A)) == UNSUP         # a destination overlaps a source
+    assert call(S=7) == SHAPE
+    assert lib.ulysses_a2a_pack_multi(1, None, None, None, 2, 1, 8, 2, 2, None) == NULL
+    assert call(fn=lib.ulysses_a2a_unpack_multi, n=0) == UNSUP
 
 
 def test_segments_argument_errors(lib):

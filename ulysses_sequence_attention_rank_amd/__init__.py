@@ -18,7 +18,7 @@ import torch
 
 __all__ = [
     "UlyssesError", "lib_path", "load", "a2a_pack", "a2a_unpack", "a2a_pack_into",
-    "a2a_unpack_into", "cu_seqlens_from_positions", "attn_fwd", "attn_bwd",
+    "a2a_unpack_into", "a2a_pack_multi_into", "a2a_unpack_multi_into", "cu_seqlens_from_positions", "attn_fwd", "attn_bwd",
     "attn_fwd_workspace_bytes", "attn_bwd_workspace_bytes", "profile_start", "profile_stop", "profile_report",
 ]
 
@@ -30,7 +30,8 @@ _STATUS = {0: "ULY_OK", -1: "ULY_ERR_NULL", -2: "ULY_ERR_SHAPE", -3: "ULY_ERR_HE
            -4: "ULY_ERR_UNSUPPORTED", -5: "ULY_ERR_CAPACITY", -6: "ULY_ERR_ALIGN",
            -7: "ULY_ERR_HIP"}
 
-EXPORTS = ("ulysses_a2a_pack", "ulysses_a2a_unpack", "ulysses_cu_seqlens_from_positions",
+EXPORTS = ("ulysses_a2a_pack", "ulysses_a2a_unpack", "ulysses_a2a_pack_multi",
+           "ulysses_a2a_unpack_multi", "ulysses_cu_seqlens_from_positions",
            "ulysses_attn_fwd", "ulysses_attn_fwd_workspace_bytes", "ulysses_attn_bwd_workspace_bytes", "ulysses_attn_bwd",
            "ulysses_profile_start", "ulysses_profile_stop", "ulysses_profile_report",
            "ulysses_last_error")
@@ -58,6 +59,8 @@ def load():
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.ulysses_a2a_pack.argtypes = [vp, vp] + [i32] * 6 + [vp]
     lib.ulysses_a2a_unpack.argtypes = [vp, vp] + [i32] * 6 + [vp]
+    lib.ulysses_a2a_pack_multi.argtypes = [i32, vp, vp, vp] + [i32] * 5 + [vp]
+    lib.ulysses_a2a_unpack_multi.argtypes = [i32, vp, vp, vp] + [i32] * 5 + [vp]
     lib.ulysses_cu_seqlens_from_positions.argtypes = [vp, i32, i32, i32, i32, vp, i32, vp, vp, vp]
     lib.ulysses_attn_fwd.argtypes = [vp] * 9 + [sz] + [i32] * 5 + [f32] + [i32] * 3 + [vp]
     lib.ulysses_attn_fwd_workspace_bytes.argtypes = [i32] * 5
@@ -157,6 +160,40 @@ def a2a_unpack(head: torch.Tensor) -> torch.Tensor:
     P, B, S, hp, D = head.shape
     seq = torch.empty((P, B, S // P, hp * P, D), dtype=head.dtype, device=head.device)
     return a2a_unpack_into(head, seq, P)
+
+
+def _multi(fn_name, srcs, dsts, P, seq_side_is_src):
+    n = len(srcs)
+    if n != len(dsts) or not 1 <= n <= 4:
+        raise ValueError(f"{fn_name}: 1..4 source/destination pairs")
+    for i, (a, b) in enumerate(zip(srcs, dsts)):
+        _dev(a, f"src{i}"), _dev(b, f"dst{i}")
+        if a.numel() != b.numel() or a.dtype != b.dtype or a.dtype != srcs[0].dtype:
+            raise ValueError(f"{fn_name}: shape/dtype mismatch at tensor {i}")
+    seqs = srcs if seq_side_is_src else dsts
+    Pp, B, Sl, _, D = seqs[0].shape
+    if Pp != P or any(t.shape[0] != P or t.shape[1] != B or t.shape[2] != Sl or t.shape[4] != D
+                      for t in seqs):
+        raise ValueError(f"{fn_name}: tensors disagree on P, B, S/P or D")
+    VP = ctypes.c_void_p * n
+    src_arr = VP(*[t.data_ptr() for t in srcs])
+    dst_arr = VP(*[t.data_ptr() for t in dsts])
+    H = (ctypes.c_int * n)(*[t.shape[3] for t in seqs])
+    _check(getattr(load(), fn_name)(n, src_arr, dst_arr, H, P, B, Sl * P, D, srcs[0].element_size(),
+                                    _stream(srcs[0].device)), fn_name)
+
+
+def a2a_pack_multi_into(seqs, heads, P: int):
+    """Pack up to four tensors of one exchange (e.g. Q, K, V) in one launch:
+    ``seqs[i]`` ``[P, B, S/P, H_i, D]`` -> ``heads[i]`` ``[P, B, S, H_i/P, D]``."""
+    _multi("ulysses_a2a_pack_multi", list(seqs), list(heads), P, True)
+    return heads
+
+
+def a2a_unpack_multi_into(heads, seqs, P: int):
+    """Inverse of ``a2a_pack_multi_into`` (e.g. dQ, dK, dV in one launch)."""
+    _multi("ulysses_a2a_unpack_multi", list(heads), list(seqs), P, False)
+    return seqs
 
 
 # ---------------------------------------------------------------- segments

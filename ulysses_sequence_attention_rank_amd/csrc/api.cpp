@@ -216,7 +216,8 @@ int ulysses_a2a_pack(const void* seq_shards, void* head_shards, int P, int B, in
                      int elem_bytes, void* stream) {
   int rc = check_permute(seq_shards, head_shards, P, B, S, H, D, elem_bytes);
   if (rc) return rc;
-  return hip_status(uly::permute_launch(true, seq_shards, head_shards, P, B, S, H, D, elem_bytes,
+  void* dst = head_shards;
+  return hip_status(uly::permute_launch(true, 1, &seq_shards, &dst, &H, P, B, S, D, elem_bytes,
                                         (hipStream_t)stream),
                     "ulysses_a2a_pack launch");
 }
@@ -225,9 +226,45 @@ int ulysses_a2a_unpack(const void* head_shards, void* seq_shards, int P, int B, 
                        int D, int elem_bytes, void* stream) {
   int rc = check_permute(head_shards, seq_shards, P, B, S, H, D, elem_bytes);
   if (rc) return rc;
-  return hip_status(uly::permute_launch(false, head_shards, seq_shards, P, B, S, H, D, elem_bytes,
+  void* dst = seq_shards;
+  return hip_status(uly::permute_launch(false, 1, &head_shards, &dst, &H, P, B, S, D, elem_bytes,
                                         (hipStream_t)stream),
                     "ulysses_a2a_unpack launch");
+}
+
+static int permute_multi(bool pack, int n, const void* const* src, void* const* dst, const int* H,
+                         int P, int B, int S, int D, int elem_bytes, void* stream, const char* what) {
+  if (!src || !dst || !H) return fail(ULY_ERR_NULL, "NULL src/dst/H array");
+  if (n < 1 || n > 4) return fail(ULY_ERR_UNSUPPORTED, "n=%d tensors not in 1..4", n);
+  for (int i = 0; i < n; ++i) {
+    int rc = check_permute(src[i], dst[i], P, B, S, H[i], D, elem_bytes);
+    if (rc) return rc;
+  }
+  // no destination may overlap any source or another destination
+  for (int i = 0; i < n; ++i)
+    for (int j = 0; j < n; ++j) {
+      const uintptr_t ei = (uintptr_t)B * S * H[i] * D * elem_bytes, ej = (uintptr_t)B * S * H[j] * D * elem_bytes;
+      const uintptr_t d0 = (uintptr_t)dst[i], s0 = (uintptr_t)src[j], d1 = (uintptr_t)dst[j];
+      if (d0 < s0 + ej && s0 < d0 + ei)
+        return fail(ULY_ERR_UNSUPPORTED, "destination %d overlaps source %d", i, j);
+      if (i != j && d0 < d1 + ej && d1 < d0 + ei)
+        return fail(ULY_ERR_UNSUPPORTED, "destinations %d and %d overlap", i, j);
+    }
+  return hip_status(uly::permute_launch(pack, n, src, dst, H, P, B, S, D, elem_bytes,
+                                        (hipStream_t)stream),
+                    what);
+}
+
+int ulysses_a2a_pack_multi(int n, const void* const* seq_shards, void* const* head_shards,
+                           const int* H, int P, int B, int S, int D, int elem_bytes, void* stream) {
+  return permute_multi(true, n, seq_shards, head_shards, H, P, B, S, D, elem_bytes, stream,
+                       "ulysses_a2a_pack_multi launch");
+}
+
+int ulysses_a2a_unpack_multi(int n, const void* const* head_shards, void* const* seq_shards,
+                             const int* H, int P, int B, int S, int D, int elem_bytes, void* stream) {
+  return permute_multi(false, n, head_shards, seq_shards, H, P, B, S, D, elem_bytes, stream,
+                       "ulysses_a2a_unpack_multi launch");
 }
 
 int ulysses_cu_seqlens_from_positions(const void* pos_shards, int pos_bytes, int P, int B, int S,

@@ -1,4 +1,5 @@
-// Layout permutation of the Ulysses all-to-all, all P simulated ranks at once.
+// Layout permutation of the Ulysses all-to-all, all P simulated ranks at once
+// (and up to four tensors of one exchange, e.g. Q, K, V, in one launch).
 //
 // pack:   seq [P][B][S/P][H][D] -> head [P][B][S][H/P][D]
 // unpack: head -> seq
@@ -13,12 +14,18 @@
 
 namespace uly {
 
+constexpr int kMaxTensors = 4;
+
+// Up to kMaxTensors tensors of equal P, B, S, D (each its own H) in one
+// launch: tensor i owns blocks [blk0[i], blk0[i+1]) of the grid.
 struct PermArgs {
-  const char* src;
-  char* dst;
-  u32 n_chunks;     // total vector chunks
-  u32 run_bytes;    // H/P * D * elem_bytes
-  FastDiv cpr;      // chunks per run
+  int n;
+  const char* src[kMaxTensors];
+  char* dst[kMaxTensors];
+  u32 n_chunks[kMaxTensors];   // vector chunks of the tensor
+  u32 run_bytes[kMaxTensors];  // H/P * D * elem_bytes
+  FastDiv cpr[kMaxTensors];    // chunks per run
+  u32 blk0[kMaxTensors + 1];
   FastDiv S, B, Sl, P;
 };
 
@@ -54,29 +61,37 @@ __device__ __forceinline__ u32 unpack_src_run(u32 run, const PermArgs& a) {
 template <int VW, bool PACK>
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(PermArgs a) {
   typedef typename VecT<VW>::T V;
+  // this block's tensor (uniform)
+  int ti = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxTensors; ++i)
+    if (i < a.n && blockIdx.x >= a.blk0[i]) ti = i;
+  const char* src = a.src[ti];
+  char* dst = a.dst[ti];
+  const u32 n_chunks = a.n_chunks[ti], run_bytes = a.run_bytes[ti];
+  const FastDiv cpr = a.cpr[ti];
   V val[kPermUnroll];
   uint64_t dst_off[kPermUnroll];
-  const u32 base = blockIdx.x * (kPermThreads * kPermUnroll) + threadIdx.x;
+  const u32 base = (blockIdx.x - a.blk0[ti]) * (kPermThreads * kPermUnroll) + threadIdx.x;
 #pragma unroll
   for (int u = 0; u < kPermUnroll; ++u) {
     const u32 i = base + u * kPermThreads;
     dst_off[u] = ~0ull;
-    if (i < a.n_chunks) {
-      const u32 run = fdiv(i, a.cpr), off = (i - run * a.cpr.d) * VW;
+    if (i < n_chunks) {
+      const u32 run = fdiv(i, cpr), off = (i - run * cpr.d) * VW;
       const u32 srun = PACK ? pack_src_run(run, a) : unpack_src_run(run, a);
-      val[u] = *reinterpret_cast<const V*>(a.src + (uint64_t)srun * a.run_bytes + off);
-      dst_off[u] = (uint64_t)run * a.run_bytes + off;
+      val[u] = *reinterpret_cast<const V*>(src + (uint64_t)srun * run_bytes + off);
+      dst_off[u] = (uint64_t)run * run_bytes + off;
     }
   }
 #pragma unroll
   for (int u = 0; u < kPermUnroll; ++u)
-    if (dst_off[u] != ~0ull) __builtin_nontemporal_store(val[u], reinterpret_cast<V*>(a.dst + dst_off[u]));
+    if (dst_off[u] != ~0ull) __builtin_nontemporal_store(val[u], reinterpret_cast<V*>(dst + dst_off[u]));
 }
 
 template <bool PACK>
 static hipError_t launch_perm(int vw, const PermArgs& a, hipStream_t st) {
-  const u32 per_block = kPermThreads * kPermUnroll;
-  const dim3 grid((a.n_chunks + per_block - 1) / per_block), block(kPermThreads);
+  const dim3 grid(a.blk0[a.n]), block(kPermThreads);
   ProfScope prof(PACK ? "a2a_pack" : "a2a_unpack", st);
   switch (vw) {
     case 16: hipLaunchKernelGGL((permute_kernel<16, PACK>), grid, block, 0, st, a); break;
@@ -88,23 +103,32 @@ static hipError_t launch_perm(int vw, const PermArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t permute_launch(bool pack, const void* src, void* dst, int P, int B, int S, int H, int D,
-                          int eb, hipStream_t st) {
-  const uint64_t run_bytes = (uint64_t)(H / P) * D * eb;
+hipError_t permute_launch(bool pack, int n, const void* const* src, void* const* dst, const int* H,
+                          int P, int B, int S, int D, int eb, hipStream_t st) {
+  // the widest vector every tensor's runs and pointers allow
   int vw = 16;
-  while (vw > 1 && (run_bytes % vw || ((uintptr_t)src % vw) || ((uintptr_t)dst % vw))) vw >>= 1;
-  PermArgs a;
-  a.src = (const char*)src;
-  a.dst = (char*)dst;
-  const uint64_t total = (uint64_t)P * B * S * run_bytes;
-  a.n_chunks = (u32)(total / vw);
-  a.run_bytes = (u32)run_bytes;
-  a.cpr = make_fastdiv((u32)(run_bytes / vw));
+  for (int i = 0; i < n; ++i) {
+    const uint64_t run_bytes = (uint64_t)(H[i] / P) * D * eb;
+    while (vw > 1 && (run_bytes % vw || ((uintptr_t)src[i] % vw) || ((uintptr_t)dst[i] % vw))) vw >>= 1;
+  }
+  PermArgs a = {};
+  a.n = n;
   a.S = make_fastdiv(S);
   a.B = make_fastdiv(B);
   a.Sl = make_fastdiv(S / P);
   a.P = make_fastdiv(P);
-  if (a.n_chunks == 0) return hipSuccess;
+  const u32 per_block = kPermThreads * kPermUnroll;
+  a.blk0[0] = 0;
+  for (int i = 0; i < n; ++i) {
+    const uint64_t run_bytes = (uint64_t)(H[i] / P) * D * eb;
+    a.src[i] = (const char*)src[i];
+    a.dst[i] = (char*)dst[i];
+    a.n_chunks[i] = (u32)((uint64_t)P * B * S * run_bytes / vw);
+    a.run_bytes[i] = (u32)run_bytes;
+    a.cpr[i] = make_fastdiv((u32)(run_bytes / vw));
+    a.blk0[i + 1] = a.blk0[i] + (a.n_chunks[i] + per_block - 1) / per_block;
+  }
+  if (a.blk0[n] == 0) return hipSuccess;
   return pack ? launch_perm<true>(vw, a, st) : launch_perm<false>(vw, a, st);
 }
 

@@ -17,8 +17,8 @@ from typing import Optional, Sequence
 
 import torch
 
-from . import (a2a_pack_into, a2a_unpack_into, attn_bwd, attn_bwd_workspace_bytes, attn_fwd,
-               attn_fwd_workspace_bytes, cu_seqlens_from_positions)
+from . import (a2a_pack_into, a2a_pack_multi_into, a2a_unpack_into, a2a_unpack_multi_into, attn_bwd,
+               attn_bwd_workspace_bytes, attn_fwd, attn_fwd_workspace_bytes, cu_seqlens_from_positions)
 
 
 @dataclasses.dataclass
@@ -102,9 +102,7 @@ def forward(b: StepBuffers, *, causal: bool, window_left: int = -1, window_right
     """Gather positions -> cu_seqlens, pack Q/K/V, attention per rank, unpack O."""
     ranks = range(b.P) if ranks is None else ranks
     cu_seqlens_from_positions(b.pos_seq, b.cu, b.n_seqs, b.max_len)
-    a2a_pack_into(b.q_seq, b.q_head, b.P)
-    a2a_pack_into(b.k_seq, b.k_head, b.P)
-    a2a_pack_into(b.v_seq, b.v_head, b.P)
+    a2a_pack_multi_into((b.q_seq, b.k_seq, b.v_seq), (b.q_head, b.k_head, b.v_head), b.P)
     hq = b.hq
     for r in ranks:
         sk = None if b.sink is None else b.sink[r * hq:(r + 1) * hq]
@@ -129,9 +127,7 @@ def backward(b: StepBuffers, *, causal: bool, window_left: int = -1, window_righ
                  window_left=window_left, window_right=window_right,
                  softmax_scale=softmax_scale, dq=b.dq_head[r], dk=b.dk_head[r],
                  dv=b.dv_head[r], dsink=ds, workspace=b.workspace)
-    a2a_unpack_into(b.dq_head, b.dq_seq, b.P)
-    a2a_unpack_into(b.dk_head, b.dk_seq, b.P)
-    a2a_unpack_into(b.dv_head, b.dv_seq, b.P)
+    a2a_unpack_multi_into((b.dq_head, b.dk_head, b.dv_head), (b.dq_seq, b.dk_seq, b.dv_seq), b.P)
 
 
 def step(b: StepBuffers, *, causal: bool, window_left: int = -1, window_right: int = -1,
