@@ -192,6 +192,31 @@ def main():
     elapsed = time.perf_counter() - t0
     ms_per_step = 1e3 * elapsed / args.steps
 
+    # the same step with the permutation folded into the attention kernels'
+    # addressing (fused layout): timed the same way
+    def fused_step():
+        for v in case.variants:
+            sim.step(b, causal=v.causal, window_left=v.window_left, window_right=v.window_right,
+                     fused=True)
+    fused_step()
+    fgraph = None
+    if not args.no_graph:
+        fgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(fgraph):
+            fused_step()
+        for _ in range(args.warmup):
+            fgraph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        if fgraph is not None:
+            fgraph.replay()
+        else:
+            fused_step()
+    torch.cuda.synchronize()
+    fused_ms = 1e3 * (time.perf_counter() - t0) / args.steps
+    del fgraph
+
     # per-kernel durations: the same steps launched eagerly, each kernel
     # bracketed by HIP events on the stream it runs on
     log(f"per-kernel timing over {args.steps} eager steps")
@@ -272,6 +297,10 @@ def main():
                    "sink": case.sink, "packed_docs": len(docs) if inp.doc_lengths else None},
         "execution": "hip_graph" if graph is not None else "eager",
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "fused_layout": {"ms_per_step": round(fused_ms, 4),
+                         "value": round(step_flops / (fused_ms * 1e-3) / 1e12, 2),
+                         "note": "attention reads Q/K/V and writes O/dQ/dK/dV in the sequence "
+                                 "shards in place: no pack/unpack launches"},
         "attn_tflops": round(attn_tflops, 2),
         "pack_gbps": perm["pack_gbps"],
         "pack_frac_of_hbm": round(perm["pack_gbps"] / PEAK_HBM_GBPS, 4),

@@ -156,6 +156,49 @@ int ulysses_attn_fwd(const void* q, const void* k, const void* v, void* out, flo
                      float softmax_scale, int causal, int window_left, int window_right,
                      void* stream);
 
+/* ------------------------------------------------------------------------
+ * The same two calls on tensors in other layouts, read and written in place:
+ * attention takes the rank's heads straight from the sequence shards and
+ * writes its outputs back into them, with no pack or unpack (the all-to-all's
+ * permutation folded into the kernels' addressing; [accelerate#4209] reply
+ * on the four all-to-all call sites for the [B, S/P, H, D] and the wrapper's
+ * [B, H, S/P, D] forms).
+ *
+ * A layout says where the D contiguous elements of (batch row b, token s,
+ * head h) start, counting elements (not bytes) from the tensor pointer:
+ *   s = r * (S / shards) + sl  ->  b*batch + r*shard + sl*token + h*head
+ * All query-side tensors (q, out, dout, dq) follow q_layout, all KV-side ones
+ * (k, v, dk, dv) kv_layout.  Strides are multiples of 8 elements (16-byte
+ * rows), token > 0, the others >= 0; shards divides S.  Examples, for the
+ * rank r of P holding heads [r*h, (r+1)*h) of H (h = hq or hkv):
+ *   head layout [B][S][h][D]:           shards=1, batch=S*h*D, token=h*D, head=D
+ *   sequence shards [P][B][S/P][H][D]:  pointer + r*h*D; shards=P,
+ *       shard=B*(S/P)*H*D, batch=(S/P)*H*D, token=H*D, head=D
+ *   wrapper form, P x [B][H][S/P][D]:   pointer + r*h*(S/P)*D; shards=P,
+ *       shard=B*H*(S/P)*D, batch=H*(S/P)*D, token=D, head=(S/P)*D
+ * LSE, dsink, workspace and everything else as in ulysses_attn_fwd/_bwd.
+ * Errors: as those calls, plus ULY_ERR_NULL (NULL layout), ULY_ERR_SHAPE
+ * (shards, negative strides), ULY_ERR_ALIGN (strides not multiples of 8).
+ * ---------------------------------------------------------------------- */
+typedef struct uly_layout {
+  int shards;
+  int64_t batch, shard, token, head;
+} uly_layout;
+
+int ulysses_attn_fwd_layout(const void* q, const void* k, const void* v, void* out, float* lse,
+                            const float* sink, const int32_t* cu_seqlens, const int32_t* n_seqs,
+                            void* workspace, size_t workspace_bytes, const uly_layout* q_layout,
+                            const uly_layout* kv_layout, int B, int S, int hq, int hkv, int D,
+                            float softmax_scale, int causal, int window_left, int window_right,
+                            void* stream);
+int ulysses_attn_bwd_layout(const void* q, const void* k, const void* v, const void* out,
+                            const void* dout, const float* lse, const float* sink,
+                            const int32_t* cu_seqlens, const int32_t* n_seqs, void* dq, void* dk,
+                            void* dv, float* dsink, void* workspace, size_t workspace_bytes,
+                            const uly_layout* q_layout, const uly_layout* kv_layout, int B, int S,
+                            int hq, int hkv, int D, float softmax_scale, int causal, int window_left,
+                            int window_right, void* stream);
+
 /* Bytes of device workspace ulysses_attn_fwd needs for these sizes: zero when
  * one pass of query tiles fills the GPU, else room for fp32 partial outputs of
  * the key-range splits that small problems are cut into (merged, with the

@@ -34,6 +34,7 @@ def test_header_declares_the_boundary():
     assert declared() == {"ulysses_a2a_pack", "ulysses_a2a_unpack", "ulysses_a2a_pack_multi",
                           "ulysses_a2a_unpack_multi",
                           "ulysses_cu_seqlens_from_positions", "ulysses_attn_fwd",
+                          "ulysses_attn_fwd_layout", "ulysses_attn_bwd_layout",
                           "ulysses_attn_fwd_workspace_bytes",
                           "ulysses_attn_bwd_workspace_bytes", "ulysses_attn_bwd",
                           "ulysses_profile_start", "ulysses_profile_stop",
@@ -126,6 +127,28 @@ def test_attn_fwd_workspace(lib):
     # a problem that fills the GPU in one pass needs none
     assert lib.ulysses_attn_fwd_workspace_bytes(1, 131072, 7, 1, 128) == 0
     assert lib.ulysses_attn_fwd_workspace_bytes(1, 4096, 6, 6, 96) == 0
+
+
+def test_layout_argument_errors(lib):
+    from ulysses_sequence_attention_rank_amd import Layout
+    ok_q, ok_k = Layout(1, 64 * 4 * 128, 0, 4 * 128, 128), Layout(1, 64 * 2 * 128, 0, 2 * 128, 128)
+
+    def fwd(lq=ok_q, lk=ok_k):
+        return lib.ulysses_attn_fwd_layout(
+            _p(A), _p(2 * A), _p(3 * A), _p(4 * A), _p(5 * A), None, None, None, None,
+            ctypes.c_size_t(0), None if lq is None else ctypes.byref(lq),
+            None if lk is None else ctypes.byref(lk), 1, 64, 4, 2, 128, ctypes.c_float(0.125), 1,
+            -1, -1, None)
+    assert fwd(lq=None) == NULL
+    assert fwd(lq=Layout(3, 0, 0, 512, 128)) == SHAPE      # 3 shards do not divide S=64
+    assert fwd(lk=Layout(1, 0, 0, 0, 128)) == SHAPE        # token stride 0
+    assert fwd(lk=Layout(1, 0, 0, 256, -128)) == SHAPE     # negative stride
+    assert fwd(lq=Layout(2, 0, 4, 512, 128)) == ALIGN      # shard stride not a multiple of 8
+    rc = lib.ulysses_attn_bwd_layout(
+        _p(A), _p(2 * A), _p(3 * A), _p(4 * A), _p(5 * A), _p(6 * A), None, None, None, _p(7 * A),
+        _p(8 * A), _p(9 * A), None, _p(10 * A), ctypes.c_size_t(1 << 30), ctypes.byref(ok_q), None,
+        1, 64, 4, 2, 128, ctypes.c_float(0.125), 1, -1, -1, None)
+    assert rc == NULL
 
 
 def test_attn_bwd_argument_errors(lib):

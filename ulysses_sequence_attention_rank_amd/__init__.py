@@ -19,7 +19,7 @@ import torch
 __all__ = [
     "UlyssesError", "lib_path", "load", "a2a_pack", "a2a_unpack", "a2a_pack_into",
     "a2a_unpack_into", "a2a_pack_multi_into", "a2a_unpack_multi_into", "cu_seqlens_from_positions", "attn_fwd", "attn_bwd",
-    "attn_fwd_workspace_bytes", "attn_bwd_workspace_bytes", "profile_start", "profile_stop", "profile_report",
+    "attn_fwd_workspace_bytes", "attn_bwd_workspace_bytes", "Layout", "view_layout", "profile_start", "profile_stop", "profile_report",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -32,7 +32,8 @@ _STATUS = {0: "ULY_OK", -1: "ULY_ERR_NULL", -2: "ULY_ERR_SHAPE", -3: "ULY_ERR_HE
 
 EXPORTS = ("ulysses_a2a_pack", "ulysses_a2a_unpack", "ulysses_a2a_pack_multi",
            "ulysses_a2a_unpack_multi", "ulysses_cu_seqlens_from_positions",
-           "ulysses_attn_fwd", "ulysses_attn_fwd_workspace_bytes", "ulysses_attn_bwd_workspace_bytes", "ulysses_attn_bwd",
+           "ulysses_attn_fwd", "ulysses_attn_fwd_layout", "ulysses_attn_bwd_layout",
+           "ulysses_attn_fwd_workspace_bytes", "ulysses_attn_bwd_workspace_bytes", "ulysses_attn_bwd",
            "ulysses_profile_start", "ulysses_profile_stop", "ulysses_profile_report",
            "ulysses_last_error")
 
@@ -64,6 +65,8 @@ def load():
     lib.ulysses_cu_seqlens_from_positions.argtypes = [vp, i32, i32, i32, i32, vp, i32, vp, vp, vp]
     lib.ulysses_attn_fwd.argtypes = [vp] * 9 + [sz] + [i32] * 5 + [f32] + [i32] * 3 + [vp]
     lib.ulysses_attn_fwd_workspace_bytes.argtypes = [i32] * 5
+    lib.ulysses_attn_fwd_layout.argtypes = [vp] * 9 + [sz, vp, vp] + [i32] * 5 + [f32] + [i32] * 3 + [vp]
+    lib.ulysses_attn_bwd_layout.argtypes = [vp] * 14 + [sz, vp, vp] + [i32] * 5 + [f32] + [i32] * 3 + [vp]
     lib.ulysses_attn_fwd_workspace_bytes.restype = sz
     lib.ulysses_attn_bwd_workspace_bytes.argtypes = [i32] * 5
     lib.ulysses_attn_bwd_workspace_bytes.restype = sz
@@ -93,10 +96,10 @@ def _stream(device: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _dev(t: torch.Tensor, name: str, dtype=None):
+def _dev(t: torch.Tensor, name: str, dtype=None, strided: bool = False):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
-    if not t.is_contiguous():
+    if not strided and not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
@@ -222,12 +225,48 @@ def cu_seqlens_from_positions(pos_shards: torch.Tensor, cu: Optional[torch.Tenso
 
 # --------------------------------------------------------------- attention
 
+class Layout(ctypes.Structure):
+    """``uly_layout``: element (b, s, h, :) at b*batch + r*shard + sl*token + h*head,
+    s = r * (S / shards) + sl."""
+    _fields_ = [("shards", ctypes.c_int), ("batch", ctypes.c_int64), ("shard", ctypes.c_int64),
+                ("token", ctypes.c_int64), ("head", ctypes.c_int64)]
+
+
+def view_layout(t: torch.Tensor):
+    """Sizes and layout of a strided view: 4-D ``[B, S, h, D]`` or 5-D
+    ``[P, B, S/P, h, D]`` (P sequence shards), last dimension contiguous.
+    Returns (B, S, h, D, Layout)."""
+    if t.stride(-1) != 1:
+        raise ValueError("the head dimension D must be contiguous")
+    st = t.stride()
+    if t.dim() == 4:
+        B, S, h, D = t.shape
+        return B, S, h, D, Layout(1, st[0], 0, st[1], st[2])
+    if t.dim() == 5:
+        P, B, Sl, h, D = t.shape
+        return B, P * Sl, h, D, Layout(P, st[1], st[0], st[2], st[3])
+    raise ValueError("expected a [B, S, h, D] or [P, B, S/P, h, D] view")
+
+
+def _is_head_layout(t):
+    return t.dim() == 4 and t.is_contiguous()
+
+
+def _same_view(a, b, what):
+    if a.shape != b.shape or a.stride() != b.stride():
+        raise ValueError(f"{what} must have the same shape and strides")
+
+
+def _like(t):
+    return torch.empty_strided(t.shape, t.stride(), dtype=t.dtype, device=t.device)
+
+
 def _shapes(q, k):
-    B, S, hq, D = q.shape
-    Bk, Sk, hkv, Dk = k.shape
+    B, S, hq, D, lq = view_layout(q)
+    Bk, Sk, hkv, Dk, lk = view_layout(k)
     if (Bk, Sk, Dk) != (B, S, D):
         raise ValueError("q and k/v shapes disagree")
-    return B, S, hq, hkv, D
+    return B, S, hq, hkv, D, lq, lk
 
 
 def attn_fwd_workspace_bytes(B, S, hq, hkv, D) -> int:
@@ -236,15 +275,21 @@ def attn_fwd_workspace_bytes(B, S, hq, hkv, D) -> int:
 
 def attn_fwd(q, k, v, *, sink=None, cu_seqlens=None, n_seqs=None, causal=True, window_left=-1,
              window_right=-1, softmax_scale=None, out=None, lse=None, workspace=None):
-    """One rank's attention: q ``[B, S, hq, D]``, k/v ``[B, S, hkv, D]`` bf16.
-    Returns (out bf16 ``[B, S, hq, D]``, lse fp32 ``[B, hq, S]``)."""
+    """One rank's attention: q ``[B, S, hq, D]``, k/v ``[B, S, hkv, D]`` bf16, or
+    strided views of the rank's heads in another layout (``view_layout``: e.g.
+    ``seq[:, :, :, r*hq:(r+1)*hq]`` of the sequence shards ``[P, B, S/P, H, D]``),
+    read in place; ``out`` then has q's shape and strides.
+    Returns (out, lse fp32 ``[B, hq, S]``)."""
     for name, t in (("q", q), ("k", k), ("v", v)):
-        _dev(t, name, torch.bfloat16)
-    B, S, hq, hkv, D = _shapes(q, k)
+        _dev(t, name, torch.bfloat16, strided=True)
+    B, S, hq, hkv, D, lq, lk = _shapes(q, k)
+    _same_view(k, v, "k and v")
     if softmax_scale is None:
         softmax_scale = D ** -0.5
     if out is None:
-        out = torch.empty_like(q)
+        out = _like(q)
+    _same_view(q, out, "q and out")
+    _dev(out, "out", torch.bfloat16, strided=True)
     if lse is None:
         lse = torch.empty((B, hq, S), dtype=torch.float32, device=q.device)
     if sink is not None:
@@ -252,10 +297,11 @@ def attn_fwd(q, k, v, *, sink=None, cu_seqlens=None, n_seqs=None, causal=True, w
     if workspace is None:
         need = attn_fwd_workspace_bytes(B, S, hq, hkv, D)
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
-    _check(load().ulysses_attn_fwd(
+    _check(load().ulysses_attn_fwd_layout(
         _p(q), _p(k), _p(v), _p(out), _p(lse), _p(sink), _p(cu_seqlens), _p(n_seqs), _p(workspace),
-        0 if workspace is None else workspace.numel(), B, S, hq, hkv, D, float(softmax_scale), int(bool(causal)), int(window_left), int(window_right),
-        _stream(q.device)), "ulysses_attn_fwd")
+        0 if workspace is None else workspace.numel(), ctypes.byref(lq), ctypes.byref(lk), B, S, hq,
+        hkv, D, float(softmax_scale), int(bool(causal)), int(window_left), int(window_right),
+        _stream(q.device)), "ulysses_attn_fwd_layout")
     return out, lse
 
 
@@ -266,25 +312,31 @@ def attn_bwd_workspace_bytes(B, S, hq, hkv, D) -> int:
 def attn_bwd(q, k, v, out, dout, lse, *, sink=None, cu_seqlens=None, n_seqs=None, causal=True,
              window_left=-1, window_right=-1, softmax_scale=None, dq=None, dk=None, dv=None,
              dsink=None, workspace=None):
-    """Backward of ``attn_fwd`` for the loss ``sum(out * dout)``.
+    """Backward of ``attn_fwd`` for the loss ``sum(out * dout)``; views as in
+    ``attn_fwd`` (out, dout, dq with q's strides, dk, dv with k's).
     Returns (dq, dk, dv, dsink or None)."""
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
-        _dev(t, name, torch.bfloat16)
+        _dev(t, name, torch.bfloat16, strided=True)
     _dev(lse, "lse", torch.float32)
-    B, S, hq, hkv, D = _shapes(q, k)
+    B, S, hq, hkv, D, lq, lk = _shapes(q, k)
     if softmax_scale is None:
         softmax_scale = D ** -0.5
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    dq = _like(q) if dq is None else dq
+    dk = _like(k) if dk is None else dk
+    dv = _like(v) if dv is None else dv
+    for a, b, what in ((q, out, "q and out"), (q, dout, "q and dout"), (q, dq, "q and dq"),
+                       (k, v, "k and v"), (k, dk, "k and dk"), (k, dv, "k and dv")):
+        _same_view(a, b, what)
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _dev(t, name, torch.bfloat16, strided=True)
     if sink is not None and dsink is None:
         dsink = torch.empty_like(sink)
     need = attn_bwd_workspace_bytes(B, S, hq, hkv, D)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    _check(load().ulysses_attn_bwd(
+    _check(load().ulysses_attn_bwd_layout(
         _p(q), _p(k), _p(v), _p(out), _p(dout), _p(lse), _p(sink), _p(cu_seqlens), _p(n_seqs),
-        _p(dq), _p(dk), _p(dv), _p(dsink), _p(workspace), workspace.numel(), B, S, hq, hkv, D,
-        float(softmax_scale), int(bool(causal)), int(window_left), int(window_right),
-        _stream(q.device)), "ulysses_attn_bwd")
+        _p(dq), _p(dk), _p(dv), _p(dsink), _p(workspace), workspace.numel(), ctypes.byref(lq),
+        ctypes.byref(lk), B, S, hq, hkv, D, float(softmax_scale), int(bool(causal)),
+        int(window_left), int(window_right), _stream(q.device)), "ulysses_attn_bwd_layout")
     return dq, dk, dv, (dsink if sink is not None else None)

@@ -76,6 +76,43 @@ int check_attn(const void* q, const void* k, const void* v, const int32_t* cu, c
   return ok();
 }
 
+// RowMap of the contiguous head layout [B][S][H][D].
+// RowMap of a uly_layout for a tensor of H heads (checked: shards divide S,
+// non-negative strides, 16-byte rows, every element addressable).
+int make_map(const uly_layout* L, int B, int S, int H, int D, const char* name, uly::RowMap& m) {
+  if (!L) return fail(ULY_ERR_NULL, "NULL %s layout", name);
+  if (L->shards < 1 || S % L->shards)
+    return fail(ULY_ERR_SHAPE, "%s layout: %d shards do not divide S=%d", name, L->shards, S);
+  if (L->batch < 0 || L->shard < 0 || L->token <= 0 || L->head < 0)
+    return fail(ULY_ERR_SHAPE, "%s layout: strides must be >= 0 (token > 0)", name);
+  if (L->batch % 8 || L->shard % 8 || L->token % 8 || L->head % 8)
+    return fail(ULY_ERR_ALIGN, "%s layout: strides must be multiples of 8 elements (16-byte rows)", name);
+  const int Sl = S / L->shards;
+  const double span = (double)(B - 1) * L->batch + (double)(L->shards - 1) * L->shard +
+                      (double)(Sl - 1) * L->token + (double)(H - 1) * L->head + D;
+  if (span >= 9.0e18) return fail(ULY_ERR_SHAPE, "%s layout: offsets exceed 64 bits", name);
+  m = uly::RowMap{};
+  m.batch = L->batch;
+  m.shard = L->shard;
+  m.token = L->token;
+  m.head = L->head;
+  m.S = uly::make_fastdiv(S);
+  m.Sl = uly::make_fastdiv(Sl);
+  m.uniform = (B == 1 || L->batch == (int64_t)S * L->token) &&
+              (L->shards == 1 || L->shard == (int64_t)Sl * L->token);
+  return ok();
+}
+
+uly_layout head_layout(int S, int H, int D) {
+  uly_layout L;
+  L.shards = 1;
+  L.batch = (int64_t)S * H * D;
+  L.shard = 0;
+  L.token = (int64_t)H * D;
+  L.head = D;
+  return L;
+}
+
 uly::AttnArgs make_args(const void* q, const void* k, const void* v, const float* sink,
                         const int32_t* cu, const int32_t* n_seqs, int B, int S, int hq, int hkv,
                         float scale, int causal, int wl, int wr) {
@@ -298,11 +335,12 @@ size_t ulysses_attn_fwd_workspace_bytes(int B, int S, int hq, int hkv, int D) {
   return align256((size_t)ns * rows * D * 4) + align256(2 * (size_t)ns * rows * 4);
 }
 
-int ulysses_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
-                     const float* sink, const int32_t* cu_seqlens, const int32_t* n_seqs,
-                     void* workspace, size_t workspace_bytes, int B, int S, int hq, int hkv, int D,
-                     float softmax_scale, int causal, int window_left, int window_right,
-                     void* stream) {
+int ulysses_attn_fwd_layout(const void* q, const void* k, const void* v, void* out, float* lse,
+                            const float* sink, const int32_t* cu_seqlens, const int32_t* n_seqs,
+                            void* workspace, size_t workspace_bytes, const uly_layout* q_layout,
+                            const uly_layout* kv_layout, int B, int S, int hq, int hkv, int D,
+                            float softmax_scale, int causal, int window_left, int window_right,
+                            void* stream) {
   int rc = check_attn(q, k, v, cu_seqlens, n_seqs, B, S, hq, hkv, D, softmax_scale, window_left,
                       window_right);
   if (rc) return rc;
@@ -317,6 +355,8 @@ int ulysses_attn_fwd(const void* q, const void* k, const void* v, void* out, flo
     return fail(ULY_ERR_ALIGN, "q/k/v/out need 16-byte alignment, lse/sink/cu 4-byte, workspace 256-byte");
   uly::AttnArgs a = make_args(q, k, v, sink, cu_seqlens, n_seqs, B, S, hq, hkv, softmax_scale,
                               causal, window_left, window_right);
+  if ((rc = make_map(q_layout, B, S, hq, D, "q", a.mq)) || (rc = make_map(kv_layout, B, S, hkv, D, "kv", a.mk)))
+    return rc;
   a.out = (__bf16*)out;
   a.lse = lse;
   if (need > 0) {
@@ -325,6 +365,17 @@ int ulysses_attn_fwd(const void* q, const void* k, const void* v, void* out, flo
     a.part_pdp = (float*)((char*)workspace + align256((size_t)a.nsplit * B * S * hq * D * 4));
   }
   return hip_status(uly::attn_fwd_launch(a, D, (hipStream_t)stream), "ulysses_attn_fwd launch");
+}
+
+int ulysses_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                     const float* sink, const int32_t* cu_seqlens, const int32_t* n_seqs,
+                     void* workspace, size_t workspace_bytes, int B, int S, int hq, int hkv, int D,
+                     float softmax_scale, int causal, int window_left, int window_right,
+                     void* stream) {
+  const uly_layout lq = head_layout(S, hq, D), lk = head_layout(S, hkv, D);
+  return ulysses_attn_fwd_layout(q, k, v, out, lse, sink, cu_seqlens, n_seqs, workspace,
+                                 workspace_bytes, &lq, &lk, B, S, hq, hkv, D, softmax_scale, causal,
+                                 window_left, window_right, stream);
 }
 
 size_t ulysses_attn_bwd_workspace_bytes(int B, int S, int hq, int hkv, int D) {
@@ -337,12 +388,13 @@ size_t ulysses_attn_bwd_workspace_bytes(int B, int S, int hq, int hkv, int D) {
          split_part_bytes(B, S, hq, hkv, D);
 }
 
-int ulysses_attn_bwd(const void* q, const void* k, const void* v, const void* out,
-                     const void* dout, const float* lse, const float* sink,
-                     const int32_t* cu_seqlens, const int32_t* n_seqs, void* dq, void* dk,
-                     void* dv, float* dsink, void* workspace, size_t workspace_bytes, int B, int S,
-                     int hq, int hkv, int D, float softmax_scale, int causal, int window_left,
-                     int window_right, void* stream) {
+int ulysses_attn_bwd_layout(const void* q, const void* k, const void* v, const void* out,
+                            const void* dout, const float* lse, const float* sink,
+                            const int32_t* cu_seqlens, const int32_t* n_seqs, void* dq, void* dk,
+                            void* dv, float* dsink, void* workspace, size_t workspace_bytes,
+                            const uly_layout* q_layout, const uly_layout* kv_layout, int B, int S,
+                            int hq, int hkv, int D, float softmax_scale, int causal, int window_left,
+                            int window_right, void* stream) {
   int rc = check_attn(q, k, v, cu_seqlens, n_seqs, B, S, hq, hkv, D, softmax_scale, window_left,
                       window_right);
   if (rc) return rc;
@@ -360,6 +412,8 @@ int ulysses_attn_bwd(const void* q, const void* k, const void* v, const void* ou
     return fail(ULY_ERR_ALIGN, "bf16 tensors need 16-byte alignment, workspace 256-byte");
   uly::AttnArgs a = make_args(q, k, v, sink, cu_seqlens, n_seqs, B, S, hq, hkv, softmax_scale,
                               causal, window_left, window_right);
+  if ((rc = make_map(q_layout, B, S, hq, D, "q", a.mq)) || (rc = make_map(kv_layout, B, S, hkv, D, "kv", a.mk)))
+    return rc;
   a.o = (const __bf16*)out;
   a.dout = (const __bf16*)dout;
   a.lse = const_cast<float*>(lse);
@@ -390,6 +444,18 @@ int ulysses_attn_bwd(const void* q, const void* k, const void* v, const void* ou
   }
   a.n_part = kDsinkParts;
   return hip_status(uly::attn_bwd_launch(a, D, (hipStream_t)stream), "ulysses_attn_bwd launch");
+}
+
+int ulysses_attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                     const void* dout, const float* lse, const float* sink,
+                     const int32_t* cu_seqlens, const int32_t* n_seqs, void* dq, void* dk,
+                     void* dv, float* dsink, void* workspace, size_t workspace_bytes, int B, int S,
+                     int hq, int hkv, int D, float softmax_scale, int causal, int window_left,
+                     int window_right, void* stream) {
+  const uly_layout lq = head_layout(S, hq, D), lk = head_layout(S, hkv, D);
+  return ulysses_attn_bwd_layout(q, k, v, out, dout, lse, sink, cu_seqlens, n_seqs, dq, dk, dv,
+                                 dsink, workspace, workspace_bytes, &lq, &lk, B, S, hq, hkv, D,
+                                 softmax_scale, causal, window_left, window_right, stream);
 }
 
 const char* ulysses_last_error(void) { return g_err; }

@@ -36,8 +36,10 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(AttnArgs a) {
   float acc = 0.f;
   const bool valid = row < a.T * a.hq;
   if (valid) {
-    const u32x4 x = *reinterpret_cast<const u32x4*>(a.dout + (int64_t)row * D + 8 * c);
-    const u32x4 y = *reinterpret_cast<const u32x4*>(a.o + (int64_t)row * D + 8 * c);
+    const int t = row / a.hq, hh = row - t * a.hq;
+    const int64_t src = row_of(a.mq, t) + (int64_t)hh * a.mq.head + 8 * c;
+    const u32x4 x = *reinterpret_cast<const u32x4*>(a.dout + src);
+    const u32x4 y = *reinterpret_cast<const u32x4*>(a.o + src);
     u32x4 h;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -57,13 +59,18 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(AttnArgs a) {
   }
 }
 
-// Exact fp16 copy of a bf16 array (n a multiple of 8): every bf16 value of
-// magnitude <= 65504 is an fp16 value (fp16 keeps 11 significant bits, bf16 8);
-// larger magnitudes saturate, values below 2^-14 round to fp16's subnormals.
-__global__ __launch_bounds__(256) void to_f16_kernel(const __bf16* src, _Float16* dst, int64_t n) {
+// Exact fp16 copy, in the head layout [T][H][D], of a bf16 tensor laid out
+// as `m` says: every bf16 value of magnitude <= 65504 is an fp16 value (fp16
+// keeps 11 significant bits, bf16 8); larger magnitudes saturate, values below
+// 2^-14 round to fp16's subnormals.  One 16-byte chunk per thread; hd8 = H*D/8.
+__global__ __launch_bounds__(256) void to_f16_kernel(const __bf16* src, RowMap m, FastDiv hd8,
+                                                     FastDiv d8, _Float16* dst, int64_t n) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
   if (i < n) {
-    const u32x4 x = *reinterpret_cast<const u32x4*>(src + i);
+    const u32 chunk = (u32)(i >> 3);
+    const u32 t = fdiv(chunk, hd8), rest = chunk - t * hd8.d;
+    const u32 hh = fdiv(rest, d8), c = rest - hh * d8.d;
+    const u32x4 x = *reinterpret_cast<const u32x4*>(src + row_of(m, (int)t) + (int64_t)hh * m.head + 8 * c);
     u32x4 h;
 #pragma unroll
     for (int w = 0; w < 4; ++w) h[w] = pack_f16x2(clamp_f16(bf16_lo(x[w])), clamp_f16(bf16_hi(x[w])));
@@ -221,7 +228,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(AttnArgs a) {
   }
   if (qvalid && want_pdp && hf == 0) a.pdp[lse_index(a, qrow, h)] = pdp;
   if (qvalid) {
-    __bf16* row = a.out + ((int64_t)qrow * a.hq + h) * D;
+    __bf16* row = a.out + row_of(a.mq, qrow) + (int64_t)h * a.mq.head;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -236,6 +243,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(AttnArgs a) {
 
 // dQ = scale * sum of the split partials (fixed order), to bf16; the same for
 // the rows' sum of P dP.
+template <int D>
 __global__ __launch_bounds__(256) void dq_reduce_kernel(AttnArgs a, int64_t n) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i < n) {
@@ -244,7 +252,8 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(AttnArgs a, int64_t n) {
     u32x2 w;
     w[0] = pack_bf16x2(q[0] * a.scale, q[1] * a.scale);
     w[1] = pack_bf16x2(q[2] * a.scale, q[3] * a.scale);
-    *reinterpret_cast<u32x2*>(a.out + i) = w;
+    const int rr = (int)(i / D), t = rr / a.hq, h = rr - t * a.hq;  // row rr = t * hq + h
+    *reinterpret_cast<u32x2*>(a.out + row_of(a.mq, t) + (int64_t)h * a.mq.head + (i - (int64_t)rr * D)) = w;
   }
   const int64_t rows = (int64_t)a.T * a.hq;
   const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -268,9 +277,13 @@ static hipError_t launch_bwd_t(const AttnArgs& args, hipStream_t st) {
   {
     ProfScope prof("attn_bwd_f16", st);
     const int64_t nq = (int64_t)a.T * a.hq * D, nkv = (int64_t)a.T * a.hkv * D;
-    hipLaunchKernelGGL(to_f16_kernel, dim3((nq / 8 + 255) / 256), dim3(256), 0, st, a.q, a.q16, nq);
-    hipLaunchKernelGGL(to_f16_kernel, dim3((nkv / 8 + 255) / 256), dim3(256), 0, st, a.k, a.k16, nkv);
-    hipLaunchKernelGGL(to_f16_kernel, dim3((nkv / 8 + 255) / 256), dim3(256), 0, st, a.v, a.v16, nkv);
+    const FastDiv d8 = make_fastdiv(D / 8), q8 = make_fastdiv(a.hq * D / 8), k8 = make_fastdiv(a.hkv * D / 8);
+    hipLaunchKernelGGL(to_f16_kernel, dim3((nq / 8 + 255) / 256), dim3(256), 0, st, a.q, a.mq, q8, d8,
+                       a.q16, nq);
+    hipLaunchKernelGGL(to_f16_kernel, dim3((nkv / 8 + 255) / 256), dim3(256), 0, st, a.k, a.mk, k8, d8,
+                       a.k16, nkv);
+    hipLaunchKernelGGL(to_f16_kernel, dim3((nkv / 8 + 255) / 256), dim3(256), 0, st, a.v, a.mk, k8, d8,
+                       a.v16, nkv);
   }
   dkdv_launch(a, D, st);
   {
@@ -287,7 +300,7 @@ static hipError_t launch_bwd_t(const AttnArgs& args, hipStream_t st) {
       ProfScope prof("attn_bwd_dq_reduce", st);
       const int64_t n = (int64_t)a.T * a.hq * D;
       const int64_t items = n / 4 > (int64_t)a.T * a.hq ? n / 4 : (int64_t)a.T * a.hq;
-      hipLaunchKernelGGL(dq_reduce_kernel, dim3((items + 255) / 256), dim3(256), 0, st, b, n);
+      hipLaunchKernelGGL(dq_reduce_kernel<D>, dim3((items + 255) / 256), dim3(256), 0, st, b, n);
     }
   }
   if (a.sink != nullptr) {

@@ -181,11 +181,13 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(AttnArgs a) {
     for (int e = 0; e < 16; ++e) {
       const int key = k0 + 32 * wave + 8 * (e >> 2) + 4 * hf + (e & 3);
       if (key < a.T) {
-        const int64_t off = ((int64_t)key * a.hkv + g) * D + 32 * nb + (lane & 31);
+        const int col = 32 * nb + (lane & 31);
         if (a.nsplit == 1) {
+          const int64_t off = row_of(a.mk, key) + (int64_t)g * a.mk.head + col;
           a.dk[off] = (__bf16)(dkacc[nb][e] * a.scale);
           a.dv[off] = (__bf16)dvacc[nb][e];
         } else {
+          const int64_t off = ((int64_t)key * a.hkv + g) * D + col;
           pk[off] = dkacc[nb][e];
           pv[off] = dvacc[nb][e];
         }
@@ -194,6 +196,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(AttnArgs a) {
 }
 
 // dK = scale * sum of the split partials, dV = sum (fixed order), to bf16.
+template <int D>
 __global__ __launch_bounds__(256) void dkdv_reduce_kernel(AttnArgs a, int64_t n) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= n) return;
@@ -207,8 +210,10 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(AttnArgs a, int64_t n)
   wk[1] = pack_bf16x2(k[2] * a.scale, k[3] * a.scale);
   wv[0] = pack_bf16x2(v[0], v[1]);
   wv[1] = pack_bf16x2(v[2], v[3]);
-  *reinterpret_cast<u32x2*>(a.dk + i) = wk;
-  *reinterpret_cast<u32x2*>(a.dv + i) = wv;
+  const int rr = (int)(i / D), t = rr / a.hkv, g = rr - t * a.hkv;  // row rr = t * hkv + g
+  const int64_t off = row_of(a.mk, t) + (int64_t)g * a.mk.head + (i - (int64_t)rr * D);
+  *reinterpret_cast<u32x2*>(a.dk + off) = wk;
+  *reinterpret_cast<u32x2*>(a.dv + off) = wv;
 }
 
 template <int D, int NW>
@@ -224,7 +229,7 @@ static void launch_dkdv_t(const AttnArgs& args, hipStream_t st) {
   if (b.nsplit > 1) {
     ProfScope prof("attn_bwd_dkdv_reduce", st);
     const int64_t n = (int64_t)b.T * b.hkv * D;
-    hipLaunchKernelGGL(dkdv_reduce_kernel, dim3((n / 4 + 255) / 256), dim3(256), 0, st, b, n);
+    hipLaunchKernelGGL(dkdv_reduce_kernel<D>, dim3((n / 4 + 255) / 256), dim3(256), 0, st, b, n);
   }
 }
 

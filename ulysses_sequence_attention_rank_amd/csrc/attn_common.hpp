@@ -21,6 +21,24 @@ namespace uly {
 
 constexpr int kBK = 64;  // keys (or queries) per LDS tile
 
+// Where the D contiguous elements of (token t of the flattened B*S, head h)
+// of a bf16 tensor start: with t = b*S + s and s = r*Sl + sl (sequence shard
+// r of Sl tokens), at b*batch + r*shard + sl*token + h*head elements.  The
+// head layout [B][S][H][D] and, for B = 1, the rank's heads of the
+// sequence-sharded [P][B][S/P][H][D] are `uniform`: t*token.
+struct RowMap {
+  int64_t batch, shard, token, head;
+  FastDiv S, Sl;
+  int uniform;
+};
+
+__device__ __forceinline__ int64_t row_of(const RowMap& m, int t) {
+  if (m.uniform) return (int64_t)t * m.token;
+  const u32 b = fdiv((u32)t, m.S), s = (u32)t - b * m.S.d;
+  const u32 r = fdiv(s, m.Sl), sl = s - r * m.Sl.d;
+  return (int64_t)b * m.batch + (int64_t)r * m.shard + (int64_t)sl * m.token;
+}
+
 struct AttnArgs {
   const __bf16* q;
   const __bf16* k;
@@ -45,6 +63,8 @@ struct AttnArgs {
   float* dsink;
   const int32_t* cu;
   const int32_t* n_seqs;
+  RowMap mq;  // q, out, dout, dq
+  RowMap mk;  // k, v, dk, dv
   int B, S, T, hq, hkv, G;
   float scale;       // softmax scale
   float scale_log2;  // softmax scale * log2(e)
@@ -193,6 +213,25 @@ __device__ __forceinline__ void tile_load_lds(char* lds, const E* g, int ld, int
     const int c = (pos % Swz<D>::kSlots) ^ Swz<D>::f(r);
     const int row = min(row0 + r, row_end - 1);
     const char* src = reinterpret_cast<const char*>(g) + ((int64_t)row * ld + c * 8) * 2;
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(lds + i * 1024), 16, 0, 0);
+  }
+}
+
+// The same for a bf16 tensor addressed through a RowMap (`base` already
+// offset to the head): rows row0 .. row0+R-1, clamped to row_end - 1.
+template <int D, int R, int NW, bool UNIFORM>
+__device__ __forceinline__ void tile_load_lds_map(char* lds, const __bf16* base, const RowMap& m,
+                                                  int row0, int row_end, int wave, int lane) {
+  constexpr int kInstr = R * D * 2 / 1024;
+  static_assert(kInstr % NW == 0, "tile must split evenly over the waves");
+#pragma unroll
+  for (int k = 0; k < kInstr / NW; ++k) {
+    const int i = wave + k * NW;
+    const int pos = i * 64 + lane;
+    const int r = pos / Swz<D>::kSlots;
+    const int c = (pos % Swz<D>::kSlots) ^ Swz<D>::f(r);
+    const int row = min(row0 + r, row_end - 1);
+    const __bf16* src = base + (UNIFORM ? (int64_t)row * m.token : row_of(m, row)) + c * 8;
     __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(lds + i * 1024), 16, 0, 0);
   }
 }

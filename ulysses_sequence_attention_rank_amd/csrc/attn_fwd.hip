@@ -17,7 +17,7 @@ namespace uly {
 
 constexpr float kRescaleLog2 = 8.0f;
 
-template <int D, int NW, int QB>
+template <int D, int NW, int QB, bool KV_UNIFORM>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnArgs a) {
   constexpr int BM = 32 * QB * NW, NB = D / 32, KS = D / 16;
   constexpr int TILE = kBK * D * 2;  // bytes of one K or V tile
@@ -40,7 +40,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnArgs a) {
     qvalid[qb] = qrow[qb] < a.T;
     klo[qb] = khi[qb] = 0;
     if (qvalid[qb]) key_interval(a, qrow[qb], klo[qb], khi[qb]);
-    load_row_frags<D>(qf[qb], a.q + ((int64_t)qrow[qb] * a.hq + h) * D, qvalid[qb], lane);
+    load_row_frags<D>(qf[qb], a.q + (qvalid[qb] ? row_of(a.mq, qrow[qb]) : 0) + (int64_t)h * a.mq.head,
+                      qvalid[qb], lane);
   }
   const int q_last = min(q0 + BM, a.T) - 1;
   int wg_lo, wg_hi, full_lo, full_hi;
@@ -59,15 +60,14 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnArgs a) {
       for (int e = 0; e < 16; ++e) oacc[qb][nb][e] = 0.f;
   }
 
-  const __bf16* kbase = a.k + (int64_t)g * D;
-  const __bf16* vbase = a.v + (int64_t)g * D;
-  const int ld = a.hkv * D;
+  const __bf16* kbase = a.k + (int64_t)g * a.mk.head;
+  const __bf16* vbase = a.v + (int64_t)g * a.mk.head;
   // this split's share of the key tiles
   int it_lo, it_hi;
   split_range((wg_hi - wg_lo + kBK - 1) / kBK, blockIdx.y, a.nsplit, it_lo, it_hi);
   if (it_lo < it_hi) {
-    tile_load_lds<D, kBK, NW>(smem, kbase, ld, wg_lo + it_lo * kBK, a.T, wave, lane);
-    tile_load_lds<D, kBK, NW>(smem + TILE, vbase, ld, wg_lo + it_lo * kBK, a.T, wave, lane);
+    tile_load_lds_map<D, kBK, NW, KV_UNIFORM>(smem, kbase, a.mk, wg_lo + it_lo * kBK, a.T, wave, lane);
+    tile_load_lds_map<D, kBK, NW, KV_UNIFORM>(smem + TILE, vbase, a.mk, wg_lo + it_lo * kBK, a.T, wave, lane);
   }
   const f32x16 zero = {};
 
@@ -78,8 +78,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnArgs a) {
     __syncthreads();                // everyone's have, and tile it-1 is no longer read
     if (it + 1 < it_hi) {
       char* nxt = smem + (cur ^ 1) * STAGE;
-      tile_load_lds<D, kBK, NW>(nxt, kbase, ld, k0 + kBK, a.T, wave, lane);
-      tile_load_lds<D, kBK, NW>(nxt + TILE, vbase, ld, k0 + kBK, a.T, wave, lane);
+      tile_load_lds_map<D, kBK, NW, KV_UNIFORM>(nxt, kbase, a.mk, k0 + kBK, a.T, wave, lane);
+      tile_load_lds_map<D, kBK, NW, KV_UNIFORM>(nxt + TILE, vbase, a.mk, k0 + kBK, a.T, wave, lane);
     }
     const char* kt = smem + cur * STAGE;
     const char* vt = kt + TILE;
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnArgs a) {
     const float oscale = (m_fin == -INFINITY || l_tot == 0.f || mr == -INFINITY)
                              ? 0.f : exp2f(mr - m_fin) / l_tot;
     if (qvalid[qb]) {
-      __bf16* orow = a.out + ((int64_t)qrow[qb] * a.hq + h) * D;
+      __bf16* orow = a.out + row_of(a.mq, qrow[qb]) + (int64_t)h * a.mq.head;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -246,7 +246,7 @@ __global__ __launch_bounds__(256) void attn_fwd_merge_kernel(AttnArgs a) {
   u32x2 w;
   w[0] = pack_bf16x2(o[0] * inv, o[1] * inv);
   w[1] = pack_bf16x2(o[2] * inv, o[3] * inv);
-  *reinterpret_cast<u32x2*>(a.out + r * D + c) = w;
+  *reinterpret_cast<u32x2*>(a.out + row_of(a.mq, t) + (int64_t)h * a.mq.head + c) = w;
   if (c == 0) a.lse[li] = z > 0.f ? (mf + __log2f(z)) * 0.6931471805599453f : -INFINITY;
 }
 
@@ -258,7 +258,10 @@ static hipError_t launch_fwd_t(const AttnArgs& args, hipStream_t st) {
   const int blocks = ((groups + kXcds - 1) / kXcds) * kXcds * a.G;
   {
     ProfScope prof("attn_fwd", st);
-    hipLaunchKernelGGL((attn_fwd_kernel<D, NW, QB>), dim3(blocks, a.nsplit), dim3(NW * 64), 0, st, a);
+    if (a.mk.uniform)
+      hipLaunchKernelGGL((attn_fwd_kernel<D, NW, QB, true>), dim3(blocks, a.nsplit), dim3(NW * 64), 0, st, a);
+    else
+      hipLaunchKernelGGL((attn_fwd_kernel<D, NW, QB, false>), dim3(blocks, a.nsplit), dim3(NW * 64), 0, st, a);
   }
   if (a.nsplit > 1) {
     ProfScope prof("attn_fwd_merge", st);

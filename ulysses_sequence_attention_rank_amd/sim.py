@@ -97,42 +97,66 @@ def allocate(q_seq, k_seq, v_seq, dout_seq, pos_seq, sink) -> StepBuffers:
     return b
 
 
+def _views(b: StepBuffers, r: int, fused: bool):
+    """Rank r's attention operands: its slices of the head-shard buffers, or
+    (fused) strided views of its heads in the sequence shards themselves."""
+    hq, hkv = b.hq, b.hkv
+    if not fused:
+        return dict(q=b.q_head[r], k=b.k_head[r], v=b.v_head[r], o=b.o_head[r], do=b.do_head[r],
+                    dq=b.dq_head[r], dk=b.dk_head[r], dv=b.dv_head[r])
+    qs, ks = slice(r * hq, (r + 1) * hq), slice(r * hkv, (r + 1) * hkv)
+    return dict(q=b.q_seq[:, :, :, qs], k=b.k_seq[:, :, :, ks], v=b.v_seq[:, :, :, ks],
+                o=b.o_seq[:, :, :, qs], do=b.dout_seq[:, :, :, qs], dq=b.dq_seq[:, :, :, qs],
+                dk=b.dk_seq[:, :, :, ks], dv=b.dv_seq[:, :, :, ks])
+
+
 def forward(b: StepBuffers, *, causal: bool, window_left: int = -1, window_right: int = -1,
-            ranks: Optional[Sequence[int]] = None, softmax_scale: Optional[float] = None):
-    """Gather positions -> cu_seqlens, pack Q/K/V, attention per rank, unpack O."""
+            ranks: Optional[Sequence[int]] = None, softmax_scale: Optional[float] = None,
+            fused: bool = False):
+    """Gather positions -> cu_seqlens, pack Q/K/V, attention per rank, unpack O.
+    ``fused``: attention reads Q/K/V and writes O in the sequence shards
+    directly (the permutation folded into its addressing), no pack/unpack."""
     ranks = range(b.P) if ranks is None else ranks
     cu_seqlens_from_positions(b.pos_seq, b.cu, b.n_seqs, b.max_len)
-    a2a_pack_multi_into((b.q_seq, b.k_seq, b.v_seq), (b.q_head, b.k_head, b.v_head), b.P)
+    if not fused:
+        a2a_pack_multi_into((b.q_seq, b.k_seq, b.v_seq), (b.q_head, b.k_head, b.v_head), b.P)
     hq = b.hq
     for r in ranks:
+        t = _views(b, r, fused)
         sk = None if b.sink is None else b.sink[r * hq:(r + 1) * hq]
-        attn_fwd(b.q_head[r], b.k_head[r], b.v_head[r], sink=sk, cu_seqlens=b.cu,
-                 n_seqs=b.n_seqs, causal=causal, window_left=window_left,
-                 window_right=window_right, softmax_scale=softmax_scale, out=b.o_head[r],
-                 lse=b.lse[r], workspace=b.workspace)
-    a2a_unpack_into(b.o_head, b.o_seq, b.P)
+        attn_fwd(t["q"], t["k"], t["v"], sink=sk, cu_seqlens=b.cu, n_seqs=b.n_seqs, causal=causal,
+                 window_left=window_left, window_right=window_right, softmax_scale=softmax_scale,
+                 out=t["o"], lse=b.lse[r], workspace=b.workspace)
+    if not fused:
+        a2a_unpack_into(b.o_head, b.o_seq, b.P)
 
 
 def backward(b: StepBuffers, *, causal: bool, window_left: int = -1, window_right: int = -1,
-             ranks: Optional[Sequence[int]] = None, softmax_scale: Optional[float] = None):
-    """Pack dO, attention backward per rank, unpack dQ/dK/dV."""
+             ranks: Optional[Sequence[int]] = None, softmax_scale: Optional[float] = None,
+             fused: bool = False):
+    """Pack dO, attention backward per rank, unpack dQ/dK/dV (``fused``: in
+    place on the sequence shards, as in ``forward``)."""
     ranks = range(b.P) if ranks is None else ranks
-    a2a_pack_into(b.dout_seq, b.do_head, b.P)
+    if not fused:
+        a2a_pack_into(b.dout_seq, b.do_head, b.P)
     hq = b.hq
     for r in ranks:
+        t = _views(b, r, fused)
         sk = None if b.sink is None else b.sink[r * hq:(r + 1) * hq]
         ds = None if b.dsink is None else b.dsink[r * hq:(r + 1) * hq]
-        attn_bwd(b.q_head[r], b.k_head[r], b.v_head[r], b.o_head[r], b.do_head[r], b.lse[r],
-                 sink=sk, cu_seqlens=b.cu, n_seqs=b.n_seqs, causal=causal,
-                 window_left=window_left, window_right=window_right,
-                 softmax_scale=softmax_scale, dq=b.dq_head[r], dk=b.dk_head[r],
-                 dv=b.dv_head[r], dsink=ds, workspace=b.workspace)
-    a2a_unpack_multi_into((b.dq_head, b.dk_head, b.dv_head), (b.dq_seq, b.dk_seq, b.dv_seq), b.P)
+        attn_bwd(t["q"], t["k"], t["v"], t["o"], t["do"], b.lse[r], sink=sk, cu_seqlens=b.cu,
+                 n_seqs=b.n_seqs, causal=causal, window_left=window_left,
+                 window_right=window_right, softmax_scale=softmax_scale, dq=t["dq"], dk=t["dk"],
+                 dv=t["dv"], dsink=ds, workspace=b.workspace)
+    if not fused:
+        a2a_unpack_multi_into((b.dq_head, b.dk_head, b.dv_head), (b.dq_seq, b.dk_seq, b.dv_seq),
+                              b.P)
 
 
 def step(b: StepBuffers, *, causal: bool, window_left: int = -1, window_right: int = -1,
-         ranks: Optional[Sequence[int]] = None, softmax_scale: Optional[float] = None):
+         ranks: Optional[Sequence[int]] = None, softmax_scale: Optional[float] = None,
+         fused: bool = False):
     forward(b, causal=causal, window_left=window_left, window_right=window_right, ranks=ranks,
-            softmax_scale=softmax_scale)
+            softmax_scale=softmax_scale, fused=fused)
     backward(b, causal=causal, window_left=window_left, window_right=window_right, ranks=ranks,
-             softmax_scale=softmax_scale)
+             softmax_scale=softmax_scale, fused=fused)
