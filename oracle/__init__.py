@@ -56,6 +56,8 @@ def _get():
         i64, vp = ctypes.c_int64, ctypes.c_void_p
         lib.orc_pack.argtypes = [vp, vp] + [i64] * 6
         lib.orc_unpack.argtypes = [vp, vp] + [i64] * 6
+        lib.orc_pack_replicated.argtypes = [vp, vp] + [i64] * 6
+        lib.orc_reduce_replicated.argtypes = [vp, vp] + [i64] * 5
         lib.orc_gather_positions.argtypes = [vp, vp, i64, i64, i64]
         lib.orc_segments.argtypes = [vp, i64, i64, vp, i64, vp, vp]
         lib.orc_fwd.argtypes = [ctypes.POINTER(_Prob), vp, i64, vp, vp]
@@ -92,6 +94,32 @@ def unpack(head: torch.Tensor) -> torch.Tensor:
     rc = _get().orc_unpack(_ptr(head), _ptr(out), P, B, S, hp * P, D, head.element_size())
     if rc:
         raise ValueError(f"orc_unpack: {rc}")
+    return out
+
+
+def pack_replicated(seq: torch.Tensor) -> torch.Tensor:
+    """``[P, B, S/P, H, D]`` with H < P (P % H == 0) -> ``[P, B, S, 1, D]``: rank c
+    gets KV head c // (P // H)."""
+    P, B, Sl, H, D = seq.shape
+    seq = seq.contiguous()
+    out = torch.empty((P, B, Sl * P, 1, D), dtype=seq.dtype)
+    rc = _get().orc_pack_replicated(_ptr(seq), _ptr(out), P, B, Sl * P, H, D, seq.element_size())
+    if rc:
+        raise ValueError(f"orc_pack_replicated: {rc}")
+    return out
+
+
+def reduce_replicated(head: torch.Tensor, H: int) -> torch.Tensor:
+    """bf16 ``[P, B, S, 1, D]`` replica gradients -> ``[P, B, S/P, H, D]``: the sum of
+    each head's replicas in fp32, rank order, rounded once to bf16."""
+    P, B, S, one, D = head.shape
+    if head.dtype != torch.bfloat16 or one != 1:
+        raise ValueError("reduce_replicated: bf16 [P, B, S, 1, D]")
+    head = head.contiguous()
+    out = torch.empty((P, B, S // P, H, D), dtype=torch.bfloat16)
+    rc = _get().orc_reduce_replicated(_ptr(head), _ptr(out), P, B, S, H, D)
+    if rc:
+        raise ValueError(f"orc_reduce_replicated: {rc}")
     return out
 
 

@@ -16,6 +16,9 @@
  *    shards are numbered by where they sit in the sequence (same PR, the
  *    _prepare_sp_model comment); rank c receives the c-th contiguous chunk of
  *    heads ("scatter heads, gather sequence", PR body).
+ *  - orc_pack_replicated / orc_reduce_replicated: KV heads fewer than ranks,
+ *    each sent to the ranks whose query heads use it, and the sum of the
+ *    replicas' gradients (see the functions).
  *  - orc_gather_positions / orc_segments: concatenate the P position_ids
  *    shards in rank order, then a new document starts wherever the gathered
  *    position is 0 and at every batch-row start; cu_seqlens lists the starts
@@ -85,6 +88,69 @@ int orc_unpack(const void* head, void* seq, int64_t P, int64_t B, int64_t S, int
             const int64_t si = (((c * B + b) * S + t) * hp + hh) * D + d;
             const int64_t di = (((r * B + b) * Sl + s) * H + h) * D + d;
             memcpy(dst + di * eb, src + si * eb, (size_t)eb);
+          }
+  return 0;
+}
+
+/* KV heads when there are fewer of them than ranks (H < P, P % H == 0): the
+ * follow-up the accelerate PR leaves open (it requires H % sp_size == 0).
+ * Every head goes to the R = P / H ranks whose query heads use it under
+ * contiguous GQA groups: rank c holds query heads [c*Hq/P, (c+1)*Hq/P), which
+ * belong to KV head (c*Hq/P) / (Hq/H) = c / R.
+ * seq: [P][B][S/P][H][D]  ->  head: [P][B][S][1][D] */
+int orc_pack_replicated(const void* seq, void* head, int64_t P, int64_t B, int64_t S, int64_t H,
+                        int64_t D, int64_t eb) {
+  if (P <= 0 || H <= 0 || S % P || P % H) return -1;
+  const int64_t Sl = S / P, R = P / H;
+  const char* src = (const char*)seq;
+  char* dst = (char*)head;
+  for (int64_t c = 0; c < P; ++c)
+    for (int64_t b = 0; b < B; ++b)
+      for (int64_t t = 0; t < S; ++t)
+        for (int64_t d = 0; d < D; ++d) {
+          const int64_t r = t / Sl, s = t % Sl, h = c / R;
+          const int64_t si = (((r * B + b) * Sl + s) * H + h) * D + d;
+          const int64_t di = ((c * B + b) * S + t) * D + d;
+          memcpy(dst + di * eb, src + si * eb, (size_t)eb);
+        }
+  return 0;
+}
+
+/* bf16 bit pattern <-> float.  bf16 is the upper half of an IEEE binary32;
+ * rounding to it keeps the upper 16 bits, rounded to nearest, ties to even. */
+static float bf16_to_f32(uint16_t x) {
+  uint32_t u = (uint32_t)x << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+static uint16_t f32_to_bf16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (uint16_t)((u >> 16) | 0x40);
+  const uint32_t lsb = (u >> 16) & 1u;
+  u += 0x7fffu + lsb;
+  return (uint16_t)(u >> 16);
+}
+
+/* The gradient of that replication: head j of the sequence shards receives
+ * the sum of its R replicas' gradients, accumulated in fp32 in rank order and
+ * rounded once to bf16.  head: [P][B][S][1][D] bf16  ->  seq: [P][B][S/P][H][D] */
+int orc_reduce_replicated(const uint16_t* head, uint16_t* seq, int64_t P, int64_t B, int64_t S,
+                          int64_t H, int64_t D) {
+  if (P <= 0 || H <= 0 || S % P || P % H) return -1;
+  const int64_t Sl = S / P, R = P / H;
+  for (int64_t r = 0; r < P; ++r)
+    for (int64_t b = 0; b < B; ++b)
+      for (int64_t s = 0; s < Sl; ++s)
+        for (int64_t h = 0; h < H; ++h)
+          for (int64_t d = 0; d < D; ++d) {
+            float acc = 0.f;
+            for (int64_t j = 0; j < R; ++j) {
+              const int64_t c = h * R + j, t = r * Sl + s;
+              acc += bf16_to_f32(head[((c * B + b) * S + t) * D + d]);
+            }
+            seq[(((r * B + b) * Sl + s) * H + h) * D + d] = f32_to_bf16(acc);
           }
   return 0;
 }

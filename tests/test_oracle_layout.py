@@ -137,3 +137,47 @@ def test_local_shard_cu_seqlens_differ_from_gathered():
     local, _, _ = oracle.segments(shards[0])
     assert local.tolist() != good.tolist()
     assert int(local[-1]) == inp.case.S // 4 != int(good[-1])
+
+
+# ---------------------------------------------- KV heads fewer than ranks
+
+@pytest.mark.parametrize("P,H,B,S,D", [(4, 2, 1, 8, 3), (8, 1, 2, 16, 4), (6, 3, 1, 12, 2), (2, 2, 1, 4, 5)])
+def test_pack_replicated_matches_repeat_interleave(P, H, B, S, D):
+    """Rank c receives the KV head its query heads use: with the heads of the
+    full tensor repeated R = P/H times (contiguous GQA groups), rank c's share
+    of the repeated tensor is one head, number c."""
+    g = torch.Generator().manual_seed(1000 * P + H)
+    full = torch.randn((B, S, H, D), generator=g, dtype=torch.float64).to(torch.bfloat16)
+    seq = full.reshape(B, P, S // P, H, D).permute(1, 0, 2, 3, 4).contiguous()
+    rep = full.repeat_interleave(P // H, dim=2)            # [B, S, P, D]
+    want = rep.permute(2, 0, 1, 3).unsqueeze(3)            # [P, B, S, 1, D]
+    got = oracle.pack_replicated(seq)
+    assert torch.equal(got.view(torch.int16), want.contiguous().view(torch.int16))
+    if H == P:  # one head per rank: the plain pack
+        assert torch.equal(got.view(torch.int16), oracle.pack(seq).view(torch.int16))
+
+
+@pytest.mark.parametrize("P,H,B,S,D", [(4, 2, 1, 8, 3), (8, 1, 2, 16, 4), (6, 3, 1, 12, 2)])
+def test_reduce_replicated_is_the_rank_order_fp32_sum(P, H, B, S, D):
+    g = torch.Generator().manual_seed(77 * P + H)
+    head = (torch.randn((P, B, S, 1, D), generator=g, dtype=torch.float64) *
+            torch.exp(2 * torch.randn((P, B, S, 1, D), generator=g, dtype=torch.float64))).to(torch.bfloat16)
+    got = oracle.reduce_replicated(head, H)
+    R, Sl = P // H, S // P
+    acc = torch.zeros((H, B, S, D), dtype=torch.float32)
+    for j in range(R):                                     # rank order, fp32
+        acc = acc + head[j::R, :, :, 0].float()
+    want = acc.to(torch.bfloat16).permute(1, 2, 0, 3).reshape(B, P, Sl, H, D).permute(1, 0, 2, 3, 4)
+    assert torch.equal(got.view(torch.int16), want.contiguous().view(torch.int16))
+
+
+def test_reduce_replicated_closed_forms():
+    # equal replicas sum to R times the value (exact for powers of two); R = 1 is the plain unpack
+    P, H, B, S, D = 8, 2, 1, 8, 4
+    base = torch.randn((H, B, S, D), generator=torch.Generator().manual_seed(5)).to(torch.bfloat16)
+    head = base.repeat_interleave(P // H, dim=0).unsqueeze(3)   # [P, B, S, 1, D]
+    got = oracle.reduce_replicated(head, H)
+    want = (base.float() * 4).to(torch.bfloat16).permute(1, 2, 0, 3).reshape(B, P, S // P, H, D).permute(1, 0, 2, 3, 4)
+    assert torch.equal(got.view(torch.int16), want.contiguous().view(torch.int16))
+    x = torch.randn((4, 1, 8, 1, 3), generator=torch.Generator().manual_seed(6)).to(torch.bfloat16)
+    assert torch.equal(oracle.reduce_replicated(x, 4).view(torch.int16), oracle.unpack(x).view(torch.int16))
