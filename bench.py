@@ -113,7 +113,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD, choices=[1, 2, 3, 4, 5],
+    ap.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD, choices=[1, 2, 3, 4, 5, 6],
                     help="which of the five simulated workloads (default: the S=4096 one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=None,
@@ -250,12 +250,23 @@ def main():
     elem_kv = case.B * case.S * case.Hkv * case.D
     pack_bytes = 2 * 2 * (2 * elem_q + 2 * elem_kv)   # Q, dO (Hq) and K, V (Hkv), per layer
     unpack_bytes = 2 * 2 * (2 * elem_q + 2 * elem_kv)  # O, dQ (Hq) and dK, dV (Hkv)
+    if case.Hkv < case.P:
+        # K and V are read once and written P / Hkv times over (replicated); dK, dV
+        # are summed by their own kernel, so only O and dQ are unpacked
+        elem_rep = case.P * case.B * case.S * case.D
+        pack_bytes = 2 * (2 * 2 * elem_q + 2 * (elem_kv + elem_rep))
+        unpack_bytes = 2 * 2 * 2 * elem_q
     nl = len(case.variants) * args.steps
     if "a2a_pack" in kern:
         rows["a2a_pack"]["gbps"] = pack_bytes * nl / (kern["a2a_pack"][1] * 1e-3) / 1e9
     if "a2a_unpack" in kern:
         rows["a2a_unpack"]["gbps"] = unpack_bytes * nl / (kern["a2a_unpack"][1] * 1e-3) / 1e9
-    perm = measure_permutation(case, b, dev)
+    if case.Hkv < case.P:  # replicated KV heads: Q, K, V are not one permutation launch
+        perm = {"tensors": "in-step figures (replicated KV heads)",
+                "pack_gbps": round(rows.get("a2a_pack", {}).get("gbps", 0.0), 1),
+                "unpack_gbps": round(rows.get("a2a_unpack", {}).get("gbps", 0.0), 1)}
+    else:
+        perm = measure_permutation(case, b, dev)
     attn_ms = sum(v[1] for k, v in kern.items() if k.startswith("attn_"))
     attn_tflops = step_flops * args.steps / (attn_ms * 1e-3) / 1e12
 
@@ -473,9 +484,12 @@ def cpu_baseline(inp, ranks, n_heads):
     c = inp.case
     P, D = c.P, c.D
     G = c.Hq // c.Hkv
-    n_heads = min(c.Hq // P, max(G, (n_heads // G) * G))
-    nkv = n_heads // G
-    packed = [oracle.pack(seq_shards(x, P)) for x in (inp.q, inp.k, inp.v, inp.dout)]
+    hq = c.Hq // P
+    n_heads = min(hq, max(G, (n_heads // G) * G))
+    nkv = max(1, n_heads // G)
+    kv_pack = oracle.pack_replicated if c.Hkv < P else oracle.pack
+    packed = [oracle.pack(seq_shards(inp.q, P)), kv_pack(seq_shards(inp.k, P)),
+              kv_pack(seq_shards(inp.v, P)), oracle.pack(seq_shards(inp.dout, P))]
     cu = None
     if inp.doc_lengths is not None:
         cu, _, _ = oracle.segments(oracle.gather_positions(seq_shards(inp.positions, P)))

@@ -75,6 +75,26 @@ int ulysses_a2a_pack(const void* seq_shards, void* head_shards, int P, int B, in
 int ulysses_a2a_unpack(const void* head_shards, void* seq_shards, int P, int B, int S, int H,
                        int D, int elem_bytes, void* stream);
 
+/* KV heads fewer than ranks (the follow-up [accelerate#4209] leaves open: it
+ * requires the KV heads to be divisible by sp_size): with H < P and P % H == 0,
+ * each head goes to the R = P / H ranks
+ * whose query heads use it under contiguous GQA groups, rank c getting head
+ * c / R.
+ * ulysses_a2a_pack_replicated: seq_shards [P][B][S/P][H][D] -> head_shards
+ *   [P][B][S][1][D], head[c][b][r*S/P + s][0][d] = seq[r][b][s][c/R][d];
+ *   bit-exact, elem_bytes in {1, 2, 4, 8}.
+ * ulysses_a2a_reduce_replicated: its gradient: head_shards [P][B][S][1][D]
+ *   (in_elem_bytes 4: fp32, as ulysses_attn_bwd_layout_f32kv leaves the
+ *   replicas' dK/dV; or 2: bf16) -> seq_shards [P][B][S/P][H][D] bf16, each
+ *   element the fp32 sum of its R replicas in rank order, rounded once to
+ *   bf16 (D % 8 == 0, 16-byte aligned buffers).
+ * Errors: ULY_ERR_NULL, ULY_ERR_SHAPE (sizes, S % P), ULY_ERR_HEADS (H > P or
+ *   P % H), ULY_ERR_UNSUPPORTED (elem_bytes, D % 8, overlap), ULY_ERR_ALIGN. */
+int ulysses_a2a_pack_replicated(const void* seq_shards, void* head_shards, int P, int B, int S,
+                                int H, int D, int elem_bytes, void* stream);
+int ulysses_a2a_reduce_replicated(const void* head_shards, int in_elem_bytes, void* seq_shards,
+                                  int P, int B, int S, int H, int D, void* stream);
+
 /* The same permutation for n (1..4) tensors of one exchange in one launch
  * (the forward's all-to-all carries Q, K and V together, the backward's dQ, dK
  * and dV: [accelerate#4209] reply on the four all-to-all call sites).
@@ -198,6 +218,19 @@ int ulysses_attn_bwd_layout(const void* q, const void* k, const void* v, const v
                             const uly_layout* q_layout, const uly_layout* kv_layout, int B, int S,
                             int hq, int hkv, int D, float softmax_scale, int causal, int window_left,
                             int window_right, void* stream);
+
+/* As ulysses_attn_bwd_layout, except that dk and dv are fp32 (same layout,
+ * strides in elements) and not rounded: for KV gradients that are summed
+ * further, as the replicas of a KV head shared by several ranks are
+ * (ulysses_a2a_reduce_replicated), so that the sum is rounded only once. */
+int ulysses_attn_bwd_layout_f32kv(const void* q, const void* k, const void* v, const void* out,
+                                  const void* dout, const float* lse, const float* sink,
+                                  const int32_t* cu_seqlens, const int32_t* n_seqs, void* dq,
+                                  float* dk, float* dv, float* dsink, void* workspace,
+                                  size_t workspace_bytes, const uly_layout* q_layout,
+                                  const uly_layout* kv_layout, int B, int S, int hq, int hkv, int D,
+                                  float softmax_scale, int causal, int window_left,
+                                  int window_right, void* stream);
 
 /* Bytes of device workspace ulysses_attn_fwd needs for these sizes: zero when
  * one pass of query tiles fills the GPU, else room for fp32 partial outputs of

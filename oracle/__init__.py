@@ -58,6 +58,7 @@ def _get():
         lib.orc_unpack.argtypes = [vp, vp] + [i64] * 6
         lib.orc_pack_replicated.argtypes = [vp, vp] + [i64] * 6
         lib.orc_reduce_replicated.argtypes = [vp, vp] + [i64] * 5
+        lib.orc_reduce_replicated_f32.argtypes = [vp, vp] + [i64] * 5
         lib.orc_gather_positions.argtypes = [vp, vp, i64, i64, i64]
         lib.orc_segments.argtypes = [vp, i64, i64, vp, i64, vp, vp]
         lib.orc_fwd.argtypes = [ctypes.POINTER(_Prob), vp, i64, vp, vp]
@@ -110,14 +111,15 @@ def pack_replicated(seq: torch.Tensor) -> torch.Tensor:
 
 
 def reduce_replicated(head: torch.Tensor, H: int) -> torch.Tensor:
-    """bf16 ``[P, B, S, 1, D]`` replica gradients -> ``[P, B, S/P, H, D]``: the sum of
-    each head's replicas in fp32, rank order, rounded once to bf16."""
+    """bf16 or fp32 ``[P, B, S, 1, D]`` replica gradients -> bf16 ``[P, B, S/P, H, D]``:
+    the sum of each head's replicas in fp32, rank order, rounded once to bf16."""
     P, B, S, one, D = head.shape
-    if head.dtype != torch.bfloat16 or one != 1:
-        raise ValueError("reduce_replicated: bf16 [P, B, S, 1, D]")
+    if head.dtype not in (torch.bfloat16, torch.float32) or one != 1:
+        raise ValueError("reduce_replicated: bf16 or fp32 [P, B, S, 1, D]")
     head = head.contiguous()
     out = torch.empty((P, B, S // P, H, D), dtype=torch.bfloat16)
-    rc = _get().orc_reduce_replicated(_ptr(head), _ptr(out), P, B, S, H, D)
+    fn = _get().orc_reduce_replicated if head.dtype == torch.bfloat16 else _get().orc_reduce_replicated_f32
+    rc = fn(_ptr(head), _ptr(out), P, B, S, H, D)
     if rc:
         raise ValueError(f"orc_reduce_replicated: {rc}")
     return out

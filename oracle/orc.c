@@ -155,6 +155,25 @@ int orc_reduce_replicated(const uint16_t* head, uint16_t* seq, int64_t P, int64_
   return 0;
 }
 
+/* The same sum from fp32 replica gradients (kept unrounded by the backward):
+ * fp32 accumulation in rank order, one rounding to bf16.
+ * head: [P][B][S][1][D] fp32  ->  seq: [P][B][S/P][H][D] bf16 */
+int orc_reduce_replicated_f32(const float* head, uint16_t* seq, int64_t P, int64_t B, int64_t S,
+                              int64_t H, int64_t D) {
+  if (P <= 0 || H <= 0 || S % P || P % H) return -1;
+  const int64_t Sl = S / P, R = P / H;
+  for (int64_t r = 0; r < P; ++r)
+    for (int64_t b = 0; b < B; ++b)
+      for (int64_t s = 0; s < Sl; ++s)
+        for (int64_t h = 0; h < H; ++h)
+          for (int64_t d = 0; d < D; ++d) {
+            float acc = 0.f;
+            for (int64_t j = 0; j < R; ++j) acc += head[(((h * R + j) * B + b) * S + r * Sl + s) * D + d];
+            seq[(((r * B + b) * Sl + s) * H + h) * D + d] = f32_to_bf16(acc);
+          }
+  return 0;
+}
+
 /* --------------------------------------------------------------- segments */
 
 /* shards: [P][B][S/P] int64  ->  gathered: [B][S] int64 (concatenation in rank order) */

@@ -32,9 +32,11 @@ def declared():
 
 def test_header_declares_the_boundary():
     assert declared() == {"ulysses_a2a_pack", "ulysses_a2a_unpack", "ulysses_a2a_pack_multi",
-                          "ulysses_a2a_unpack_multi",
+                          "ulysses_a2a_unpack_multi", "ulysses_a2a_pack_replicated",
+                          "ulysses_a2a_reduce_replicated",
                           "ulysses_cu_seqlens_from_positions", "ulysses_attn_fwd",
                           "ulysses_attn_fwd_layout", "ulysses_attn_bwd_layout",
+                          "ulysses_attn_bwd_layout_f32kv",
                           "ulysses_attn_fwd_workspace_bytes",
                           "ulysses_attn_bwd_workspace_bytes", "ulysses_attn_bwd",
                           "ulysses_profile_start", "ulysses_profile_stop",
@@ -83,6 +85,18 @@ def test_pack_multi_argument_errors(lib):
     assert call(S=7) == SHAPE
     assert lib.ulysses_a2a_pack_multi(1, None, None, None, 2, 1, 8, 2, 2, None) == NULL
     assert call(fn=lib.ulysses_a2a_unpack_multi, n=0) == UNSUP
+
+
+def test_replicated_argument_errors(lib):
+    f, g = lib.ulysses_a2a_pack_replicated, lib.ulysses_a2a_reduce_replicated
+    assert f(_p(A), _p(2 * A), 4, 1, 8, 3, 8, 2, None) == HEADS     # 3 heads do not divide 4 ranks
+    assert f(_p(A), _p(2 * A), 4, 1, 8, 8, 8, 2, None) == HEADS     # not fewer heads than ranks
+    assert f(_p(A), _p(2 * A), 4, 1, 6, 2, 8, 2, None) == SHAPE     # S % P
+    assert f(None, _p(2 * A), 4, 1, 8, 2, 8, 2, None) == NULL
+    assert f(_p(A), _p(A + 64), 4, 1, 8, 2, 8, 2, None) == UNSUP    # overlap
+    assert g(_p(A), 2, _p(2 * A), 4, 1, 8, 2, 12, None) == UNSUP    # D % 8
+    assert g(_p(A + 2), 2, _p(2 * A), 4, 1, 8, 2, 8, None) == ALIGN
+    assert g(_p(A), 3, _p(2 * A), 4, 1, 8, 2, 8, None) == UNSUP      # in_elem_bytes
 
 
 def test_segments_argument_errors(lib):

@@ -165,3 +165,56 @@ def test_workload_parity(cfg, variant):
                 # rounding noise of L bf16 outputs and of delta grows like sqrt(L)
                 thr = 0.05 + 3e-3 * L ** 0.5
                 assert float(sdk.abs().max()) < thr, (d, float(sdk.abs().max()), thr)
+
+
+def test_workload_parity_replicated_kv():
+    """The packed S=32768 workload over 16 ranks: 8 KV heads for 16 ranks, each
+    replicated to 2.  Layout steps bit-exact (the replicated pack, and the
+    replicas' fp32 dK/dV summed and rounded once); every rank's attention on
+    sampled rows and keys; the summed dK/dV against the unsharded attention."""
+    cfg = 6
+    inp = _inputs(cfg)
+    c = inp.case
+    P, B, S, D, Hq, Hkv = c.P, c.B, c.S, c.D, c.Hq, c.Hkv
+    hq, R = c.hq, c.P // c.Hkv
+    variant = c.variants[0]
+    b = _device_step(cfg, variant)
+
+    say("layout: pack of Q, replicated pack of K/V, sums of the replicas' dK/dV")
+    qh = oracle.pack(seq_shards(inp.q, P))
+    kh = oracle.pack_replicated(seq_shards(inp.k, P))
+    vh = oracle.pack_replicated(seq_shards(inp.v, P))
+    dh = oracle.pack(seq_shards(inp.dout, P))
+    assert bits_equal(b.q_head, qh) and bits_equal(b.k_head, kh) and bits_equal(b.v_head, vh)
+    assert bits_equal(b.do_head, dh)
+    assert bits_equal(b.dk_seq, oracle.reduce_replicated(b.dk_head.cpu(), Hkv))
+    assert bits_equal(b.dv_seq, oracle.reduce_replicated(b.dv_head.cpu(), Hkv))
+
+    cu, n, mx = oracle.segments(oracle.gather_positions(seq_shards(inp.positions, P)))
+    assert torch.equal(b.cu[: n + 1].cpu(), cu)
+    kw = dict(cu=cu, causal=variant.causal, window_left=variant.window_left,
+              window_right=variant.window_right)
+    rows, keys = _sample_rows(cfg, cu, n, count=48), _sample_keys(cfg, cu, n, variant)
+    ridx, kidx = torch.tensor(rows), torch.tensor(keys)
+    flat = lambda t, H: t.reshape(B * S, H, D)
+    for r in (0, R - 1, P - 1):   # two replicas of KV head 0, and the last rank
+        say(f"rank {r}: oracle on {len(rows)} rows / {len(keys)} keys")
+        o, lse = oracle.attn_fwd(qh[r], kh[r], vh[r], rows=rows, **kw)
+        dq, _, _, _ = oracle.attn_bwd(qh[r], kh[r], vh[r], dh[r], qrows=rows, want_dkdv=False,
+                                      want_dsink=False, **kw)
+        _, dk, dv, _ = oracle.attn_bwd(qh[r], kh[r], vh[r], dh[r], krows=keys, want_dq=False,
+                                       want_dsink=False, **kw)
+        assert_close_tol(flat(b.o_head[r], hq)[ridx], o, f"rank{r} O")
+        assert_close_tol(flat(b.dq_head[r], hq)[ridx], dq, f"rank{r} dQ")
+        assert_close_tol(flat(b.dk_head[r], 1)[kidx], dk, f"rank{r} dK (fp32 replica)")
+        assert_close_tol(flat(b.dv_head[r], 1)[kidx], dv, f"rank{r} dV (fp32 replica)")
+
+    say("summed dK/dV of KV head 0 against the unsharded attention of its query heads")
+    G = Hq // Hkv
+    _, dk0, dv0, _ = oracle.attn_bwd(inp.q[:, :, :G], inp.k[:, :, :1], inp.v[:, :, :1],
+                                     inp.dout[:, :, :G], krows=keys, want_dq=False,
+                                     want_dsink=False, **kw)
+    dk_full = b.dk_seq.permute(1, 0, 2, 3, 4).reshape(B * S, Hkv, D)[:, :1]
+    dv_full = b.dv_seq.permute(1, 0, 2, 3, 4).reshape(B * S, Hkv, D)[:, :1]
+    assert_close_tol(dk_full[kidx], dk0, "summed dK")
+    assert_close_tol(dv_full[kidx], dv0, "summed dV")

@@ -48,3 +48,35 @@ def test_multi_pack_unpack_bit_exact(row):
         assert torch.equal(got, want)          # the oracle's permutation, bit for bit
         assert bits_equal(s1, h)               # one launch per tensor == one launch for all
         assert bits_equal(b, x.to(dev))        # unpack(pack(x)) == x
+
+
+REP_CASES = [
+    # id, P, B, S, H (KV heads, fewer than P), D, dtype
+    ("rep4_bf16", 8, 1, 32, 2, 128, torch.bfloat16),
+    ("rep2_b2_fp32", 4, 2, 12, 2, 64, torch.float32),
+    ("rep8_one_head", 8, 1, 16, 1, 8, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("row", REP_CASES, ids=[c[0] for c in REP_CASES])
+def test_replicated_pack_and_gradient_sum_bit_exact(row):
+    import ulysses_sequence_attention_rank_amd as uly
+    name, P, B, S, H, D, dtype = row
+    g = torch.Generator().manual_seed(zlib.crc32(name.encode()))
+    seq = _rand((P, B, S // P, H, D), dtype, g)
+    dev = torch.device("cuda", 0)
+    head = torch.empty((P, B, S, 1, D), dtype=dtype, device=dev)
+    say(f"replicated pack {name}")
+    uly.a2a_pack_replicated_into(seq.to(dev), head, P)
+    torch.cuda.synchronize()
+    want = oracle.pack_replicated(seq)
+    assert bits_equal(head, want)
+    if dtype == torch.bfloat16:
+        for gdt in (torch.bfloat16, torch.float32):   # replica gradients as stored
+            grads = (torch.randn((P, B, S, 1, D), generator=g) *
+                     torch.exp(2 * torch.randn((P, B, S, 1, D), generator=g))).to(gdt)
+            out = torch.empty((P, B, S // P, H, D), dtype=torch.bfloat16, device=dev)
+            say(f"replica gradient sum {name} {gdt}")
+            uly.a2a_reduce_replicated_into(grads.to(dev), out, P)
+            torch.cuda.synchronize()
+            assert bits_equal(out, oracle.reduce_replicated(grads, H))

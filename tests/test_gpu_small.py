@@ -28,6 +28,9 @@ CASES = [
     ("gqa7_causal_d128", 2, 1, 192, 14, 2, 128, True, -1, -1, False, None),
     ("gqa8_sink_swa_d64", 2, 1, 384, 16, 2, 64, True, 127, -1, True, None),
     ("tiny_s2", 2, 1, 2, 2, 2, 64, True, -1, -1, True, None),
+    # fewer KV heads than ranks: each KV head replicated to P / Hkv ranks
+    ("kvrep4_causal_sink_d128", 8, 1, 256, 16, 2, 128, True, -1, -1, True, None),
+    ("kvrep2_varlen_b2_swa_d64", 4, 2, 160, 8, 2, 64, True, 33, -1, False, [[90, 70], [1, 159]]),
 ]
 
 
@@ -53,7 +56,9 @@ def test_small_step_matches_oracle(row):
     inp, b = _run(row)
     # the layout steps are bit-exact against the oracle's permutation
     assert bits_equal(b.q_head, oracle.pack(seq_shards(inp.q, P)))
-    assert bits_equal(b.k_head, oracle.pack(seq_shards(inp.k, P)))
+    kpack = oracle.pack_replicated if Hkv < P else oracle.pack
+    assert bits_equal(b.k_head, kpack(seq_shards(inp.k, P)))
+    assert bits_equal(b.v_head, kpack(seq_shards(inp.v, P)))
     # cu_seqlens rebuilt from the gathered positions, bit-exact
     cu, n, mx = oracle.segments(oracle.gather_positions(seq_shards(inp.positions, P)))
     assert int(b.n_seqs.item()) == n and int(b.max_len.item()) == mx

@@ -157,11 +157,12 @@ def test_pack_replicated_matches_repeat_interleave(P, H, B, S, D):
         assert torch.equal(got.view(torch.int16), oracle.pack(seq).view(torch.int16))
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("P,H,B,S,D", [(4, 2, 1, 8, 3), (8, 1, 2, 16, 4), (6, 3, 1, 12, 2)])
-def test_reduce_replicated_is_the_rank_order_fp32_sum(P, H, B, S, D):
+def test_reduce_replicated_is_the_rank_order_fp32_sum(P, H, B, S, D, dtype):
     g = torch.Generator().manual_seed(77 * P + H)
     head = (torch.randn((P, B, S, 1, D), generator=g, dtype=torch.float64) *
-            torch.exp(2 * torch.randn((P, B, S, 1, D), generator=g, dtype=torch.float64))).to(torch.bfloat16)
+            torch.exp(2 * torch.randn((P, B, S, 1, D), generator=g, dtype=torch.float64))).to(dtype)
     got = oracle.reduce_replicated(head, H)
     R, Sl = P // H, S // P
     acc = torch.zeros((H, B, S, D), dtype=torch.float32)

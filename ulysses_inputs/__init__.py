@@ -62,7 +62,8 @@ class Case:
 
     @property
     def hkv(self) -> int:
-        return self.Hkv // self.P
+        """KV heads a rank holds (one, replicated, when there are fewer KV heads than ranks)."""
+        return max(1, self.Hkv // self.P)
 
     @property
     def scale(self) -> float:
@@ -83,6 +84,10 @@ CONFIGS = {
             variants=(Variant("swa128", True, 127, -1), CAUSAL), sink=True),
     5: Case("s131072_gqa28x4_d128_causal", 5, P=4, B=1, S=131072, Hq=28, Hkv=4, D=128,
             variants=(CAUSAL,)),
+    # the packed workload over 16 ranks: 8 KV heads for 16 ranks, so each KV
+    # head is replicated to 2 ranks (same seed, documents and tensors as 3)
+    6: Case("s32768_varlen_gqa32x8_d128_p16_kvrep", 3, P=16, B=1, S=32768, Hq=32, Hkv=8, D=128,
+            variants=(CAUSAL,), doc_len_range=(512, 8192)),
 }
 
 

@@ -18,7 +18,8 @@ import torch
 
 __all__ = [
     "UlyssesError", "lib_path", "load", "a2a_pack", "a2a_unpack", "a2a_pack_into",
-    "a2a_unpack_into", "a2a_pack_multi_into", "a2a_unpack_multi_into", "cu_seqlens_from_positions", "attn_fwd", "attn_bwd",
+    "a2a_unpack_into", "a2a_pack_multi_into", "a2a_unpack_multi_into", "a2a_pack_replicated_into",
+    "a2a_reduce_replicated_into", "cu_seqlens_from_positions", "attn_fwd", "attn_bwd",
     "attn_fwd_workspace_bytes", "attn_bwd_workspace_bytes", "Layout", "view_layout", "profile_start", "profile_stop", "profile_report",
 ]
 
@@ -31,8 +32,10 @@ _STATUS = {0: "ULY_OK", -1: "ULY_ERR_NULL", -2: "ULY_ERR_SHAPE", -3: "ULY_ERR_HE
            -7: "ULY_ERR_HIP"}
 
 EXPORTS = ("ulysses_a2a_pack", "ulysses_a2a_unpack", "ulysses_a2a_pack_multi",
-           "ulysses_a2a_unpack_multi", "ulysses_cu_seqlens_from_positions",
+           "ulysses_a2a_unpack_multi", "ulysses_a2a_pack_replicated",
+           "ulysses_a2a_reduce_replicated", "ulysses_cu_seqlens_from_positions",
            "ulysses_attn_fwd", "ulysses_attn_fwd_layout", "ulysses_attn_bwd_layout",
+           "ulysses_attn_bwd_layout_f32kv",
            "ulysses_attn_fwd_workspace_bytes", "ulysses_attn_bwd_workspace_bytes", "ulysses_attn_bwd",
            "ulysses_profile_start", "ulysses_profile_stop", "ulysses_profile_report",
            "ulysses_last_error")
@@ -61,12 +64,15 @@ def load():
     lib.ulysses_a2a_pack.argtypes = [vp, vp] + [i32] * 6 + [vp]
     lib.ulysses_a2a_unpack.argtypes = [vp, vp] + [i32] * 6 + [vp]
     lib.ulysses_a2a_pack_multi.argtypes = [i32, vp, vp, vp] + [i32] * 5 + [vp]
+    lib.ulysses_a2a_pack_replicated.argtypes = [vp, vp] + [i32] * 6 + [vp]
+    lib.ulysses_a2a_reduce_replicated.argtypes = [vp, i32, vp] + [i32] * 5 + [vp]
     lib.ulysses_a2a_unpack_multi.argtypes = [i32, vp, vp, vp] + [i32] * 5 + [vp]
     lib.ulysses_cu_seqlens_from_positions.argtypes = [vp, i32, i32, i32, i32, vp, i32, vp, vp, vp]
     lib.ulysses_attn_fwd.argtypes = [vp] * 9 + [sz] + [i32] * 5 + [f32] + [i32] * 3 + [vp]
     lib.ulysses_attn_fwd_workspace_bytes.argtypes = [i32] * 5
     lib.ulysses_attn_fwd_layout.argtypes = [vp] * 9 + [sz, vp, vp] + [i32] * 5 + [f32] + [i32] * 3 + [vp]
     lib.ulysses_attn_bwd_layout.argtypes = [vp] * 14 + [sz, vp, vp] + [i32] * 5 + [f32] + [i32] * 3 + [vp]
+    lib.ulysses_attn_bwd_layout_f32kv.argtypes = lib.ulysses_attn_bwd_layout.argtypes
     lib.ulysses_attn_fwd_workspace_bytes.restype = sz
     lib.ulysses_attn_bwd_workspace_bytes.argtypes = [i32] * 5
     lib.ulysses_attn_bwd_workspace_bytes.restype = sz
@@ -199,6 +205,35 @@ def a2a_unpack_multi_into(heads, seqs, P: int):
     return seqs
 
 
+def a2a_pack_replicated_into(seq: torch.Tensor, head: torch.Tensor, P: int):
+    """KV heads fewer than ranks: ``[P, B, S/P, H, D]`` (H < P, P % H == 0) ->
+    ``head`` ``[P, B, S, 1, D]``, rank c getting head c // (P // H)."""
+    _dev(seq, "seq"), _dev(head, "head")
+    Pp, B, Sl, H, D = seq.shape
+    if Pp != P or tuple(head.shape) != (P, B, Sl * P, 1, D) or head.dtype != seq.dtype:
+        raise ValueError("pack_replicated: shape/dtype mismatch")
+    _check(load().ulysses_a2a_pack_replicated(_p(seq), _p(head), P, B, Sl * P, H, D,
+                                              seq.element_size(), _stream(seq.device)),
+           "ulysses_a2a_pack_replicated")
+    return head
+
+
+def a2a_reduce_replicated_into(head: torch.Tensor, seq: torch.Tensor, P: int):
+    """Gradient of ``a2a_pack_replicated_into``: each of the H heads of the bf16
+    ``seq`` ``[P, B, S/P, H, D]`` gets the sum of its P // H replicas in ``head``
+    (fp32 or bf16), accumulated in fp32 and rounded once."""
+    _dev(head, "head"), _dev(seq, "seq", torch.bfloat16)
+    if head.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("reduce_replicated: head must be fp32 or bf16")
+    Pp, B, Sl, H, D = seq.shape
+    if Pp != P or tuple(head.shape) != (P, B, Sl * P, 1, D):
+        raise ValueError("reduce_replicated: shape mismatch")
+    _check(load().ulysses_a2a_reduce_replicated(_p(head), head.element_size(), _p(seq), P, B,
+                                                Sl * P, H, D, _stream(seq.device)),
+           "ulysses_a2a_reduce_replicated")
+    return seq
+
+
 # ---------------------------------------------------------------- segments
 
 def cu_seqlens_from_positions(pos_shards: torch.Tensor, cu: Optional[torch.Tensor] = None,
@@ -311,9 +346,10 @@ def attn_bwd_workspace_bytes(B, S, hq, hkv, D) -> int:
 
 def attn_bwd(q, k, v, out, dout, lse, *, sink=None, cu_seqlens=None, n_seqs=None, causal=True,
              window_left=-1, window_right=-1, softmax_scale=None, dq=None, dk=None, dv=None,
-             dsink=None, workspace=None):
+             dsink=None, workspace=None, kv_grad_fp32=False):
     """Backward of ``attn_fwd`` for the loss ``sum(out * dout)``; views as in
     ``attn_fwd`` (out, dout, dq with q's strides, dk, dv with k's).
+    ``kv_grad_fp32``: dk, dv are fp32 and unrounded (to be summed further).
     Returns (dq, dk, dv, dsink or None)."""
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
         _dev(t, name, torch.bfloat16, strided=True)
@@ -321,22 +357,27 @@ def attn_bwd(q, k, v, out, dout, lse, *, sink=None, cu_seqlens=None, n_seqs=None
     B, S, hq, hkv, D, lq, lk = _shapes(q, k)
     if softmax_scale is None:
         softmax_scale = D ** -0.5
+    kv_dtype = torch.float32 if kv_grad_fp32 else torch.bfloat16
     dq = _like(q) if dq is None else dq
-    dk = _like(k) if dk is None else dk
-    dv = _like(v) if dv is None else dv
+    if dk is None:
+        dk = torch.empty_strided(k.shape, k.stride(), dtype=kv_dtype, device=k.device)
+    if dv is None:
+        dv = torch.empty_strided(v.shape, v.stride(), dtype=kv_dtype, device=v.device)
     for a, b, what in ((q, out, "q and out"), (q, dout, "q and dout"), (q, dq, "q and dq"),
                        (k, v, "k and v"), (k, dk, "k and dk"), (k, dv, "k and dv")):
         _same_view(a, b, what)
-    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-        _dev(t, name, torch.bfloat16, strided=True)
+    _dev(dq, "dq", torch.bfloat16, strided=True)
+    for name, t in (("dk", dk), ("dv", dv)):
+        _dev(t, name, kv_dtype, strided=True)
     if sink is not None and dsink is None:
         dsink = torch.empty_like(sink)
     need = attn_bwd_workspace_bytes(B, S, hq, hkv, D)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    _check(load().ulysses_attn_bwd_layout(
+    fn = "ulysses_attn_bwd_layout_f32kv" if kv_grad_fp32 else "ulysses_attn_bwd_layout"
+    _check(getattr(load(), fn)(
         _p(q), _p(k), _p(v), _p(out), _p(dout), _p(lse), _p(sink), _p(cu_seqlens), _p(n_seqs),
         _p(dq), _p(dk), _p(dv), _p(dsink), _p(workspace), workspace.numel(), ctypes.byref(lq),
         ctypes.byref(lk), B, S, hq, hkv, D, float(softmax_scale), int(bool(causal)),
-        int(window_left), int(window_right), _stream(q.device)), "ulysses_attn_bwd_layout")
+        int(window_left), int(window_right), _stream(q.device)), fn)
     return dq, dk, dv, (dsink if sink is not None else None)

@@ -269,6 +269,53 @@ int ulysses_a2a_unpack(const void* head_shards, void* seq_shards, int P, int B, 
                     "ulysses_a2a_unpack launch");
 }
 
+int check_replicated(const void* a, const void* b, int P, int B, int S, int H, int D, int eb) {
+  if (!a || !b) return fail(ULY_ERR_NULL, "NULL tensor pointer");
+  if (P <= 0 || B <= 0 || S <= 0 || H <= 0 || D <= 0)
+    return fail(ULY_ERR_SHAPE, "sizes must be positive (P=%d B=%d S=%d H=%d D=%d)", P, B, S, H, D);
+  if (S % P) return fail(ULY_ERR_SHAPE, "S=%d is not divisible by P=%d", S, P);
+  if (H > P || P % H)
+    return fail(ULY_ERR_HEADS, "replication needs H=%d heads dividing P=%d ranks", H, P);
+  if (eb != 1 && eb != 2 && eb != 4 && eb != 8)
+    return fail(ULY_ERR_UNSUPPORTED, "elem_bytes=%d not in {1,2,4,8}", eb);
+  const int64_t elems = (int64_t)P * B * S * D;  // the replicated side, the larger
+  if (elems >= kMaxI32) return fail(ULY_ERR_SHAPE, "tensor of %lld elements exceeds 2^31 - 1",
+                                    (long long)elems);
+  if (!aligned(a, eb) || !aligned(b, eb))
+    return fail(ULY_ERR_ALIGN, "pointers must be aligned to elem_bytes=%d", eb);
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  const uintptr_t na = (uintptr_t)elems * eb, nb = (uintptr_t)B * S * H * D * eb;
+  if (a0 < b0 + nb && b0 < a0 + na) return fail(ULY_ERR_UNSUPPORTED, "the two buffers overlap");
+  return ok();
+}
+
+int ulysses_a2a_pack_replicated(const void* seq_shards, void* head_shards, int P, int B, int S,
+                                int H, int D, int elem_bytes, void* stream) {
+  int rc = check_replicated(head_shards, seq_shards, P, B, S, H, D, elem_bytes);
+  if (rc) return rc;
+  void* dst = head_shards;
+  return hip_status(uly::permute_launch(true, 1, &seq_shards, &dst, &H, P, B, S, D, elem_bytes,
+                                        (hipStream_t)stream),
+                    "ulysses_a2a_pack_replicated launch");
+}
+
+int ulysses_a2a_reduce_replicated(const void* head_shards, int in_elem_bytes, void* seq_shards,
+                                  int P, int B, int S, int H, int D, void* stream) {
+  if (in_elem_bytes != 2 && in_elem_bytes != 4)
+    return fail(ULY_ERR_UNSUPPORTED, "in_elem_bytes=%d not 2 (bf16) or 4 (fp32)", in_elem_bytes);
+  int rc = check_replicated(head_shards, seq_shards, P, B, S, H, D, 2);
+  if (rc) return rc;
+  if (D % 8) return fail(ULY_ERR_UNSUPPORTED, "D=%d is not a multiple of 8", D);
+  if (!aligned(head_shards, 16) || !aligned(seq_shards, 16))
+    return fail(ULY_ERR_ALIGN, "the gradient buffers need 16-byte alignment");
+  const uintptr_t a0 = (uintptr_t)head_shards, b0 = (uintptr_t)seq_shards;
+  const uintptr_t na = (uintptr_t)P * B * S * D * in_elem_bytes, nb = (uintptr_t)B * S * H * D * 2;
+  if (a0 < b0 + nb && b0 < a0 + na) return fail(ULY_ERR_UNSUPPORTED, "the two buffers overlap");
+  return hip_status(uly::reduce_replicated_launch(head_shards, in_elem_bytes == 4, seq_shards, P,
+                                                  B, S, H, D, (hipStream_t)stream),
+                    "ulysses_a2a_reduce_replicated launch");
+}
+
 static int permute_multi(bool pack, int n, const void* const* src, void* const* dst, const int* H,
                          int P, int B, int S, int D, int elem_bytes, void* stream, const char* what) {
   if (!src || !dst || !H) return fail(ULY_ERR_NULL, "NULL src/dst/H array");
@@ -388,13 +435,13 @@ size_t ulysses_attn_bwd_workspace_bytes(int B, int S, int hq, int hkv, int D) {
          split_part_bytes(B, S, hq, hkv, D);
 }
 
-int ulysses_attn_bwd_layout(const void* q, const void* k, const void* v, const void* out,
-                            const void* dout, const float* lse, const float* sink,
-                            const int32_t* cu_seqlens, const int32_t* n_seqs, void* dq, void* dk,
-                            void* dv, float* dsink, void* workspace, size_t workspace_bytes,
-                            const uly_layout* q_layout, const uly_layout* kv_layout, int B, int S,
-                            int hq, int hkv, int D, float softmax_scale, int causal, int window_left,
-                            int window_right, void* stream) {
+static int attn_bwd_impl(const void* q, const void* k, const void* v, const void* out,
+                         const void* dout, const float* lse, const float* sink,
+                         const int32_t* cu_seqlens, const int32_t* n_seqs, void* dq, void* dk,
+                         void* dv, float* dsink, void* workspace, size_t workspace_bytes,
+                         const uly_layout* q_layout, const uly_layout* kv_layout, int B, int S,
+                         int hq, int hkv, int D, float softmax_scale, int causal, int window_left,
+                         int window_right, void* stream, int dkv_f32) {
   int rc = check_attn(q, k, v, cu_seqlens, n_seqs, B, S, hq, hkv, D, softmax_scale, window_left,
                       window_right);
   if (rc) return rc;
@@ -420,6 +467,7 @@ int ulysses_attn_bwd_layout(const void* q, const void* k, const void* v, const v
   a.out = (__bf16*)dq;
   a.dk = (__bf16*)dk;
   a.dv = (__bf16*)dv;
+  a.dkv_f32 = dkv_f32;
   a.dsink = dsink;
   char* ws = (char*)workspace;
   const size_t rows = align256((size_t)B * S * hq * sizeof(float));
@@ -444,6 +492,31 @@ int ulysses_attn_bwd_layout(const void* q, const void* k, const void* v, const v
   }
   a.n_part = kDsinkParts;
   return hip_status(uly::attn_bwd_launch(a, D, (hipStream_t)stream), "ulysses_attn_bwd launch");
+}
+
+int ulysses_attn_bwd_layout(const void* q, const void* k, const void* v, const void* out,
+                            const void* dout, const float* lse, const float* sink,
+                            const int32_t* cu_seqlens, const int32_t* n_seqs, void* dq, void* dk,
+                            void* dv, float* dsink, void* workspace, size_t workspace_bytes,
+                            const uly_layout* q_layout, const uly_layout* kv_layout, int B, int S,
+                            int hq, int hkv, int D, float softmax_scale, int causal, int window_left,
+                            int window_right, void* stream) {
+  return attn_bwd_impl(q, k, v, out, dout, lse, sink, cu_seqlens, n_seqs, dq, dk, dv, dsink,
+                       workspace, workspace_bytes, q_layout, kv_layout, B, S, hq, hkv, D,
+                       softmax_scale, causal, window_left, window_right, stream, 0);
+}
+
+int ulysses_attn_bwd_layout_f32kv(const void* q, const void* k, const void* v, const void* out,
+                                  const void* dout, const float* lse, const float* sink,
+                                  const int32_t* cu_seqlens, const int32_t* n_seqs, void* dq,
+                                  float* dk, float* dv, float* dsink, void* workspace,
+                                  size_t workspace_bytes, const uly_layout* q_layout,
+                                  const uly_layout* kv_layout, int B, int S, int hq, int hkv, int D,
+                                  float softmax_scale, int causal, int window_left,
+                                  int window_right, void* stream) {
+  return attn_bwd_impl(q, k, v, out, dout, lse, sink, cu_seqlens, n_seqs, dq, dk, dv, dsink,
+                       workspace, workspace_bytes, q_layout, kv_layout, B, S, hq, hkv, D,
+                       softmax_scale, causal, window_left, window_right, stream, 1);
 }
 
 int ulysses_attn_bwd(const void* q, const void* k, const void* v, const void* out,

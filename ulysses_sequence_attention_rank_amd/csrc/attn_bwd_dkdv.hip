@@ -184,8 +184,13 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(AttnArgs a) {
         const int col = 32 * nb + (lane & 31);
         if (a.nsplit == 1) {
           const int64_t off = row_of(a.mk, key) + (int64_t)g * a.mk.head + col;
-          a.dk[off] = (__bf16)(dkacc[nb][e] * a.scale);
-          a.dv[off] = (__bf16)dvacc[nb][e];
+          if (a.dkv_f32) {
+            reinterpret_cast<float*>(a.dk)[off] = dkacc[nb][e] * a.scale;
+            reinterpret_cast<float*>(a.dv)[off] = dvacc[nb][e];
+          } else {
+            a.dk[off] = (__bf16)(dkacc[nb][e] * a.scale);
+            a.dv[off] = (__bf16)dvacc[nb][e];
+          }
         } else {
           const int64_t off = ((int64_t)key * a.hkv + g) * D + col;
           pk[off] = dkacc[nb][e];
@@ -195,7 +200,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(AttnArgs a) {
     }
 }
 
-// dK = scale * sum of the split partials, dV = sum (fixed order), to bf16.
+// dK = scale * sum of the split partials, dV = sum (fixed order), to bf16
+// (or fp32).
 template <int D>
 __global__ __launch_bounds__(256) void dkdv_reduce_kernel(AttnArgs a, int64_t n) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
@@ -205,13 +211,18 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(AttnArgs a, int64_t n)
     k += *reinterpret_cast<const f32x4*>(a.part + s * n + i);
     v += *reinterpret_cast<const f32x4*>(a.part + (a.nsplit + s) * n + i);
   }
+  const int rr = (int)(i / D), t = rr / a.hkv, g = rr - t * a.hkv;  // row rr = t * hkv + g
+  const int64_t off = row_of(a.mk, t) + (int64_t)g * a.mk.head + (i - (int64_t)rr * D);
+  if (a.dkv_f32) {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.dk) + off) = k * a.scale;
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.dv) + off) = v;
+    return;
+  }
   u32x2 wk, wv;
   wk[0] = pack_bf16x2(k[0] * a.scale, k[1] * a.scale);
   wk[1] = pack_bf16x2(k[2] * a.scale, k[3] * a.scale);
   wv[0] = pack_bf16x2(v[0], v[1]);
   wv[1] = pack_bf16x2(v[2], v[3]);
-  const int rr = (int)(i / D), t = rr / a.hkv, g = rr - t * a.hkv;  // row rr = t * hkv + g
-  const int64_t off = row_of(a.mk, t) + (int64_t)g * a.mk.head + (i - (int64_t)rr * D);
   *reinterpret_cast<u32x2*>(a.dk + off) = wk;
   *reinterpret_cast<u32x2*>(a.dv + off) = wv;
 }

@@ -46,8 +46,9 @@ struct AttnArgs {
   const __bf16* o;
   const __bf16* dout;
   __bf16* out;   // fwd: O; bwd dq kernel: dQ
-  __bf16* dk;
+  __bf16* dk;    // fp32 (float*) when dkv_f32
   __bf16* dv;
+  int dkv_f32;   // dK, dV written unrounded in fp32
   float* lse;    // fwd output / bwd input, [B][hq][S]
   float* delta;  // bwd: rowsum(dO * O) with the bf16 O, [B][hq][S]
   float* pdp;    // bwd: sum_j P_ij dP_ij = dO_i . O_i with the exact O, [B][hq][S]

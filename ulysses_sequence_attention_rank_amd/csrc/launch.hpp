@@ -11,6 +11,8 @@ struct AttnArgs;
 
 hipError_t permute_launch(bool pack, int n, const void* const* src, void* const* dst, const int* H,
                           int P, int B, int S, int D, int elem_bytes, hipStream_t st);
+hipError_t reduce_replicated_launch(const void* head, bool head_f32, void* seq, int P, int B, int S,
+                                    int H, int D, hipStream_t st);
 hipError_t segments_launch(const void* pos, int pos_bytes, int P, int B, int S, int32_t* cu,
                            int32_t* n_seqs, int32_t* max_len, hipStream_t st);
 hipError_t attn_fwd_launch(const AttnArgs& a, int D, hipStream_t st);

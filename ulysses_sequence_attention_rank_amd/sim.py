@@ -17,7 +17,8 @@ from typing import Optional, Sequence
 
 import torch
 
-from . import (a2a_pack_into, a2a_pack_multi_into, a2a_unpack_into, a2a_unpack_multi_into, attn_bwd,
+from . import (a2a_pack_into, a2a_pack_multi_into, a2a_pack_replicated_into,
+               a2a_reduce_replicated_into, a2a_unpack_into, a2a_unpack_multi_into, attn_bwd,
                attn_bwd_workspace_bytes, attn_fwd, attn_fwd_workspace_bytes, cu_seqlens_from_positions)
 
 
@@ -62,7 +63,12 @@ class StepBuffers:
 
     @property
     def hkv(self):
-        return self.Hkv // self.P
+        return max(1, self.Hkv // self.P)
+
+    @property
+    def replicated(self):
+        """Fewer KV heads than ranks: each KV head is sent to P // Hkv ranks."""
+        return self.Hkv < self.P
 
 
 def allocate(q_seq, k_seq, v_seq, dout_seq, pos_seq, sink) -> StepBuffers:
@@ -73,15 +79,19 @@ def allocate(q_seq, k_seq, v_seq, dout_seq, pos_seq, sink) -> StepBuffers:
     dev = q_seq.device
     bf = torch.bfloat16
     b = StepBuffers(P, B, S, Hq, Hkv, D, q_seq, k_seq, v_seq, dout_seq, pos_seq, sink)
-    hq, hkv = Hq // P, Hkv // P
+    hq, hkv = Hq // P, max(1, Hkv // P)
+    if Hkv < P and P % Hkv:
+        raise ValueError(f"Hkv={Hkv} KV heads neither divisible by nor dividing P={P}")
     b.q_head = torch.empty((P, B, S, hq, D), dtype=bf, device=dev)
     b.k_head = torch.empty((P, B, S, hkv, D), dtype=bf, device=dev)
     b.v_head = torch.empty_like(b.k_head)
     b.o_head = torch.empty_like(b.q_head)
     b.do_head = torch.empty_like(b.q_head)
     b.dq_head = torch.empty_like(b.q_head)
-    b.dk_head = torch.empty_like(b.k_head)
-    b.dv_head = torch.empty_like(b.k_head)
+    # replicated KV heads: each replica's dK/dV stays fp32 until their sum is rounded
+    kv_grad = torch.float32 if Hkv < P else bf
+    b.dk_head = torch.empty(b.k_head.shape, dtype=kv_grad, device=dev)
+    b.dv_head = torch.empty(b.k_head.shape, dtype=kv_grad, device=dev)
     b.lse = torch.empty((P, B, hq, S), dtype=torch.float32, device=dev)
     b.dsink = torch.empty(Hq, dtype=torch.float32, device=dev) if sink is not None else None
     b.o_seq = torch.empty_like(q_seq)
@@ -117,8 +127,13 @@ def forward(b: StepBuffers, *, causal: bool, window_left: int = -1, window_right
     ``fused``: attention reads Q/K/V and writes O in the sequence shards
     directly (the permutation folded into its addressing), no pack/unpack."""
     ranks = range(b.P) if ranks is None else ranks
+    fused = fused and not b.replicated  # replicas' dK/dV must be summed: head buffers
     cu_seqlens_from_positions(b.pos_seq, b.cu, b.n_seqs, b.max_len)
-    if not fused:
+    if b.replicated:
+        a2a_pack_into(b.q_seq, b.q_head, b.P)
+        a2a_pack_replicated_into(b.k_seq, b.k_head, b.P)
+        a2a_pack_replicated_into(b.v_seq, b.v_head, b.P)
+    elif not fused:
         a2a_pack_multi_into((b.q_seq, b.k_seq, b.v_seq), (b.q_head, b.k_head, b.v_head), b.P)
     hq = b.hq
     for r in ranks:
@@ -137,6 +152,7 @@ def backward(b: StepBuffers, *, causal: bool, window_left: int = -1, window_righ
     """Pack dO, attention backward per rank, unpack dQ/dK/dV (``fused``: in
     place on the sequence shards, as in ``forward``)."""
     ranks = range(b.P) if ranks is None else ranks
+    fused = fused and not b.replicated
     if not fused:
         a2a_pack_into(b.dout_seq, b.do_head, b.P)
     hq = b.hq
@@ -147,8 +163,12 @@ def backward(b: StepBuffers, *, causal: bool, window_left: int = -1, window_righ
         attn_bwd(t["q"], t["k"], t["v"], t["o"], t["do"], b.lse[r], sink=sk, cu_seqlens=b.cu,
                  n_seqs=b.n_seqs, causal=causal, window_left=window_left,
                  window_right=window_right, softmax_scale=softmax_scale, dq=t["dq"], dk=t["dk"],
-                 dv=t["dv"], dsink=ds, workspace=b.workspace)
-    if not fused:
+                 dv=t["dv"], dsink=ds, workspace=b.workspace, kv_grad_fp32=b.replicated)
+    if b.replicated:
+        a2a_unpack_into(b.dq_head, b.dq_seq, b.P)
+        a2a_reduce_replicated_into(b.dk_head, b.dk_seq, b.P)
+        a2a_reduce_replicated_into(b.dv_head, b.dv_seq, b.P)
+    elif not fused:
         a2a_unpack_multi_into((b.dq_head, b.dk_head, b.dv_head), (b.dq_seq, b.dk_seq, b.dv_seq),
                               b.P)
 
