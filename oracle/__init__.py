@@ -44,7 +44,8 @@ class _Prob(ctypes.Structure):
                 ("sink", ctypes.c_void_p), ("cu", ctypes.c_void_p), ("n", ctypes.c_int64),
                 ("B", ctypes.c_int64), ("S", ctypes.c_int64), ("hq", ctypes.c_int64),
                 ("hkv", ctypes.c_int64), ("D", ctypes.c_int64), ("scale", ctypes.c_double),
-                ("causal", ctypes.c_int64), ("wl", ctypes.c_int64), ("wr", ctypes.c_int64)]
+                ("causal", ctypes.c_int64), ("wl", ctypes.c_int64), ("wr", ctypes.c_int64),
+                ("k_lo", ctypes.c_int64), ("k_hi", ctypes.c_int64)]
 
 
 def _get():
@@ -154,15 +155,17 @@ def _f64(t: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
     return None if t is None else t.detach().to(torch.float64).contiguous()
 
 
-def _prob(q, k, v, sink, cu, causal, wl, wr, scale):
+def _prob(q, k, v, sink, cu, causal, wl, wr, scale, keys=None):
     B, S, hq, D = q.shape
     hkv = k.shape[2]
     keep = [q, k, v, sink, cu]
+    k_lo, k_hi = (0, S) if keys is None else keys
     pr = _Prob(q.data_ptr(), k.data_ptr(), v.data_ptr(),
                sink.data_ptr() if sink is not None else None,
                cu.data_ptr() if cu is not None else None,
                (cu.numel() - 1) if cu is not None else 0,
-               B, S, hq, hkv, D, float(scale), int(bool(causal)), int(wl), int(wr))
+               B, S, hq, hkv, D, float(scale), int(bool(causal)), int(wl), int(wr), int(k_lo),
+               int(k_hi))
     return pr, keep
 
 
@@ -174,13 +177,15 @@ def _rows(rows: Optional[Sequence[int]]):
 
 
 def attn_fwd(q, k, v, *, sink=None, cu=None, causal=True, window_left=-1, window_right=-1,
-             scale=None, rows=None):
+             scale=None, rows=None, keys=None):
     """Exact attention of one rank's heads.
 
     q ``[B, S, hq, D]``, k/v ``[B, S, hkv, D]`` (any float dtype, widened to
     fp64), sink ``[hq]`` or None, cu int32 ``[n+1]`` over the flattened B*S
     tokens or None (one document per batch row).  ``rows`` selects flattened
-    query rows (default: all).  Returns (O fp64 ``[nrows, hq, D]``, LSE fp64
+    query rows (default: all); ``keys = (lo, hi)`` restricts the keys to those
+    positions of each batch row (one KV chunk; rows that see none of them get
+    O = 0, LSE = -inf).  Returns (O fp64 ``[nrows, hq, D]``, LSE fp64
     ``[nrows, hq]``).
     """
     q, k, v, sink = _f64(q), _f64(k), _f64(v), _f64(sink)
@@ -188,7 +193,7 @@ def attn_fwd(q, k, v, *, sink=None, cu=None, causal=True, window_left=-1, window
     B, S, hq, D = q.shape
     if scale is None:
         scale = D ** -0.5
-    pr, keep = _prob(q, k, v, sink, cu, causal, window_left, window_right, scale)
+    pr, keep = _prob(q, k, v, sink, cu, causal, window_left, window_right, scale, keys)
     r = _rows(rows)
     nrows = B * S if r is None else r.numel()
     out = torch.zeros((nrows, hq, D), dtype=torch.float64)
@@ -196,6 +201,22 @@ def attn_fwd(q, k, v, *, sink=None, cu=None, causal=True, window_left=-1, window
     rc = _get().orc_fwd(ctypes.byref(pr), _ptr(r), nrows, _ptr(out), _ptr(lse))
     if rc:
         raise ValueError(f"orc_fwd: {rc}")
+    return out, lse
+
+
+def merge_chunks(outs, lses, sink=None):
+    """Exact combination of attention over disjoint KV chunks (fp64): with
+    L = log(sum_c e^{LSE_c} + e^{sink}), O = sum_c e^{LSE_c - L} O_c.
+    outs ``[n, hq, D]`` and lses ``[n, hq]`` per chunk; sink ``[hq]`` or None.
+    Rows with no key in any chunk and no sink get O = 0, LSE = -inf."""
+    L = torch.stack([x.to(torch.float64) for x in lses])           # [C, n, hq]
+    if sink is not None:
+        s = sink.to(torch.float64).reshape(1, 1, -1).expand(1, L.shape[1], L.shape[2])
+        L = torch.cat([L, s])
+    lse = torch.logsumexp(L, dim=0)
+    w = torch.exp(L[: len(outs)] - lse)                             # [C, n, hq]
+    w = torch.where(torch.isfinite(lse), w, torch.zeros_like(w))
+    out = sum(w[c].unsqueeze(-1) * outs[c].to(torch.float64) for c in range(len(outs)))
     return out, lse
 
 

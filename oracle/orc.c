@@ -26,7 +26,10 @@
  *    flash-attention kwargs: cu_seq_lens/max_length are dropped and rebuilt
  *    from the gathered position_ids, never taken from the local shard.
  *  - orc_fwd / orc_bwd: exact softmax attention of the rank's heads over the
- *    whole gathered sequence, with an explicit per-pair mask (same document,
+ *    whole gathered sequence (or over one chunk of key positions, the inner
+ *    step of a ring over KV chunks: the long-context-attention "unified
+ *    sequence parallel" combination of Ulysses with ring attention), with an
+ *    explicit per-pair mask (same document,
  *    causal, window (left, right) with -1 meaning unbounded, as in the
  *    flash_attn_func argument list of the long-context-attention issue
  *    "usage with pytorch FSDP"), GQA with contiguous head groups, and an
@@ -220,6 +223,9 @@ typedef struct {
   int64_t hq, hkv, D;
   double scale;
   int64_t causal, wl, wr;
+  /* keys restricted to positions [k_lo, k_hi) of each batch row (a KV chunk
+     of the ring inner step; 0 and S: every key) */
+  int64_t k_lo, k_hi;
 } orc_prob;
 
 /* Document index of every flattened token, and each document's first and
@@ -257,6 +263,7 @@ static void free_docs(orc_docs* dd) {
 /* The mask: key j is visible to query i. */
 static int allowed(const orc_prob* p, const orc_docs* dd, int64_t i, int64_t j) {
   if (dd->doc[i] != dd->doc[j] || dd->doc[i] < 0) return 0;
+  if (j % p->S < p->k_lo || j % p->S >= p->k_hi) return 0;
   if (p->causal && j > i) return 0;
   if (p->wl >= 0 && i - j > p->wl) return 0;
   if (p->wr >= 0 && j - i > p->wr) return 0;

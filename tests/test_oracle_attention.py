@@ -384,3 +384,54 @@ def test_hand_worked_golden():
                                    atol=1e-14, rtol=1e-14)
         torch.testing.assert_close(lse.reshape(-1), torch.tensor(ex["lse"], dtype=F64),
                                    atol=1e-14, rtol=1e-14)
+
+
+# ------------------------------------------- ring inner step: KV chunks + merge
+
+CHUNK_CASES = [
+    # seed, B, S, Hq, Hkv, D, causal, wl, docs, chunk bounds
+    (11, 1, 48, 4, 2, 8, True, -1, None, (0, 7, 20, 33, 48)),
+    (12, 2, 40, 2, 1, 4, False, -1, None, (0, 25, 40)),
+    (13, 1, 64, 4, 4, 8, True, 9, [[20, 1, 43]], (0, 16, 32, 48, 64)),
+]
+
+
+@pytest.mark.parametrize("case", CHUNK_CASES)
+def test_chunks_merged_equal_full_attention(case):
+    """Attention over disjoint KV chunks, combined by the exact LSE merge (the
+    sink entering once, in the merge), equals attention over every key."""
+    seed, B, S, Hq, Hkv, D, causal, wl, docs, bounds = case
+    inp = small_case(seed, P=1, B=B, S=S, Hq=Hq, Hkv=Hkv, D=D, sink=True, doc_lengths=docs)
+    cu = None
+    if docs is not None:
+        cu, _, _ = oracle.segments(inp.positions)
+    kw = dict(cu=cu, causal=causal, window_left=wl)
+    full_o, full_lse = oracle.attn_fwd(inp.q, inp.k, inp.v, sink=inp.sink, **kw)
+    parts = [oracle.attn_fwd(inp.q, inp.k, inp.v, keys=(lo, hi), **kw)
+             for lo, hi in zip(bounds[:-1], bounds[1:])]
+    o, lse = oracle.merge_chunks([p[0] for p in parts], [p[1] for p in parts], sink=inp.sink)
+    assert torch.allclose(o, full_o, atol=1e-12, rtol=0)
+    assert torch.allclose(lse, full_lse, atol=1e-12, rtol=0)
+    # without the sink: one chunk holding every key is the plain attention, exactly
+    o1, l1 = oracle.attn_fwd(inp.q, inp.k, inp.v, keys=(0, S), **kw)
+    o2, l2 = oracle.attn_fwd(inp.q, inp.k, inp.v, **kw)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    m1, n1 = oracle.merge_chunks([o1], [l1])
+    assert torch.allclose(m1, o1, atol=1e-15, rtol=0) and torch.allclose(n1, l1, atol=0, rtol=0)
+
+
+def test_single_key_chunk_closed_form():
+    """A chunk of one key j: rows that see j get O = v_j and LSE = scale q.k_j;
+    rows that do not (causal: i < j) get O = 0 and LSE = -inf."""
+    inp = small_case(21, P=1, B=1, S=16, Hq=2, Hkv=1, D=4)
+    j = 5
+    o, lse = oracle.attn_fwd(inp.q, inp.k, inp.v, causal=True, keys=(j, j + 1))
+    q, k, v = (x.double()[0] for x in (inp.q, inp.k, inp.v))
+    for i in range(16):
+        for h in range(2):
+            if i < j:
+                assert float(lse[i, h]) == float("-inf") and bool((o[i, h] == 0).all())
+            else:
+                assert torch.allclose(o[i, h], v[j, 0], atol=1e-14, rtol=0)
+                want = 0.5 * float((q[i, h] * k[j, 0]).sum())
+                assert abs(float(lse[i, h]) - want) < 1e-12
