@@ -117,9 +117,9 @@ def main():
                     help="which of the five simulated workloads (default: the S=4096 one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=None,
-                    help="query heads of rank 0 the CPU oracle baseline runs (default: every "
-                         "head of every rank, the whole step, for the S<=4096 workloads; one KV "
-                         "group of rank 0 for the S=32768 one; none for the larger ones)")
+                    help="query heads of rank 0 the CPU oracle baseline runs (default: all of "
+                         "rank 0's heads, every layer, for the S<=4096 workloads; one KV group of "
+                         "rank 0 for the S=32768 ones; none for the larger ones)")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches instead of a captured HIP graph of the step")
     ap.add_argument("--rocprof-summary", metavar="DIR",
@@ -281,12 +281,14 @@ def main():
                 "flops_per_launch": per_launch_flops,
                 "avg_launch_ms": round(kern[dom][1] / kern[dom][0], 5)}
 
+    ring = measure_ring(case, b, credit) if case.Hkv >= case.P else None
+
     cpu = None
     if not args.no_cpu_baseline:
         if args.cpu_heads is not None:
             cpu = cpu_baseline(inp, ranks=[0], n_heads=args.cpu_heads)
         elif case.S <= 4096:
-            cpu = cpu_baseline(inp, ranks=list(range(P)), n_heads=case.Hq // P)
+            cpu = cpu_baseline(inp, ranks=[0], n_heads=case.Hq // P)
         elif case.S <= 32768:
             cpu = cpu_baseline(inp, ranks=[0], n_heads=case.Hq // case.Hkv)
 
@@ -319,6 +321,7 @@ def main():
         "permutation": perm,
         "kernels": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in r.items()}
                     for k, r in rows.items()},
+        "ring_inner_step": ring,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
@@ -360,6 +363,61 @@ def measure_permutation(case, b, dev, launches=40):
         out[f"{name}_gbps"] = round(2 * set_bytes / (ms * 1e-3) / 1e9, 1)
     del seqs[1:], heads
     torch.cuda.empty_cache()
+    return out
+
+
+def measure_ring(case, b, credit, chunks=4, reps=5):
+    """Rank 0's forward as the inner step of a ring over KV chunks: attention
+    against each of `chunks` equal KV chunks, merged exactly as they arrive,
+    then finished (sink added, bf16 out), against the single forward over all
+    keys; every layer type, HIP events around `reps` repetitions."""
+    import torch
+
+    import ulysses_sequence_attention_rank_amd as uly
+    S, hq = case.S, case.hq
+    if S % chunks:
+        return None
+    sk = None if b.sink is None else b.sink[:hq]
+    q, k, v = b.q_head[0], b.k_head[0], b.v_head[0]
+    cu = b.cu if case.doc_len_range else None
+    n = b.n_seqs if case.doc_len_range else None
+    Sk = S // chunks
+    out = {"chunks": chunks, "layers": {}}
+    for var in case.variants:
+        kw = dict(causal=var.causal, window_left=var.window_left, window_right=var.window_right)
+        parts = [(torch.empty((case.B, S, hq, case.D), dtype=torch.float32, device=q.device),
+                  torch.empty((case.B, hq, S), dtype=torch.float32, device=q.device))
+                 for _ in range(2)]
+        acc_o, acc_l = (torch.empty_like(parts[0][0]), torch.empty_like(parts[0][1]))
+        fin_o = torch.empty_like(q)
+        fin_l = torch.empty_like(acc_l)
+
+        def ring():
+            for c in range(chunks):
+                dst = (acc_o, acc_l) if c == 0 else parts[c % 2]
+                uly.attn_fwd_chunk(q, k[:, c * Sk:(c + 1) * Sk], v[:, c * Sk:(c + 1) * Sk], c * Sk,
+                                   cu_seqlens=cu, n_seqs=n, out=dst[0], lse=dst[1],
+                                   workspace=b.workspace, **kw)
+                if c:
+                    uly.attn_merge(acc_o, acc_l, dst[0], dst[1])
+            uly.attn_merge_finish(acc_o, acc_l, sink=sk, out=fin_o, lse=fin_l)
+
+        def plain():
+            uly.attn_fwd(q, k, v, sink=sk, cu_seqlens=cu, n_seqs=n, out=b.o_head[0], lse=b.lse[0],
+                         workspace=b.workspace, **kw)
+        res = {}
+        for name, fn in (("ring", ring), ("single", plain)):
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            res[f"{name}_ms"] = round(e0.elapsed_time(e1) / reps, 4)
+        res["ring_fwd_tflops"] = round(credit[var.name]["attn_fwd"] / (res["ring_ms"] * 1e-3) / 1e12, 1)
+        out["layers"][var.name] = res
     return out
 
 

@@ -232,6 +232,45 @@ int ulysses_attn_bwd_layout_f32kv(const void* q, const void* k, const void* v, c
                                   float softmax_scale, int causal, int window_left,
                                   int window_right, void* stream);
 
+/* ------------------------------------------------------------------------
+ * The inner step of a ring over KV chunks, combined with Ulysses (the
+ * long-context-attention "unified sequence parallel" scheme: Ulysses heads
+ * inside, a ring over sequence chunks outside; the accelerate PR leaves ring
+ * attention to context parallelism).  The rank's queries, all S positions,
+ * meet one chunk of the keys at a time; exact per-chunk results are merged.
+ *
+ * ulysses_attn_fwd_chunk: attention of q ([B][S][hq][D] as q_layout says)
+ *   against keys at positions [k_start, k_start + Sk) of every batch row.
+ *   k_chunk, v_chunk hold only those Sk positions (kv_layout describes the
+ *   chunk tensors, e.g. [B][Sk][hkv][D]: shards=1, batch=Sk*hkv*D,
+ *   token=hkv*D, head=D).  Masks (documents, causal, windows) use the keys'
+ *   positions in the whole sequence.  out: fp32 [B][S][hq][D], normalised
+ *   over the chunk's keys; lse: fp32 [B][hq][S] over the chunk's keys.  Rows
+ *   that see no key of the chunk get O = 0, LSE = -inf.  No sink (it joins
+ *   once, in ulysses_attn_merge_finish).  Workspace as ulysses_attn_fwd.
+ * ulysses_attn_merge: acc := merge(acc, chunk), in place:
+ *   L = log(e^acc_lse + e^lse), acc_out = e^(acc_lse - L) acc_out + e^(lse - L) out,
+ *   acc_lse = L.  Start from the first chunk's result (or acc_lse = -inf).
+ * ulysses_attn_merge_finish: out (bf16 [B][S][hq][D]) and lse (fp32
+ *   [B][hq][S], not aliasing acc_lse) from the accumulator, the sink (fp32
+ *   [hq] or NULL) joining the denominator: L' = log(e^L + e^sink),
+ *   out = e^(L - L') acc_out.
+ * Buffers 16-byte aligned (out 8); D a multiple of 4 with D/4 dividing 256.
+ * Errors: ULY_ERR_NULL, ULY_ERR_SHAPE (sizes, chunk outside [0, S)),
+ *   ULY_ERR_UNSUPPORTED (D, aliasing), ULY_ERR_ALIGN, ULY_ERR_CAPACITY, and as
+ *   ulysses_attn_fwd_layout.
+ * ---------------------------------------------------------------------- */
+int ulysses_attn_fwd_chunk(const void* q, const void* k_chunk, const void* v_chunk, float* out,
+                           float* lse, const int32_t* cu_seqlens, const int32_t* n_seqs,
+                           void* workspace, size_t workspace_bytes, const uly_layout* q_layout,
+                           const uly_layout* kv_layout, int B, int S, int k_start, int Sk, int hq,
+                           int hkv, int D, float softmax_scale, int causal, int window_left,
+                           int window_right, void* stream);
+int ulysses_attn_merge(float* acc_out, float* acc_lse, const float* out, const float* lse, int B,
+                       int S, int hq, int D, void* stream);
+int ulysses_attn_merge_finish(const float* acc_out, const float* acc_lse, const float* sink,
+                              void* out, float* lse, int B, int S, int hq, int D, void* stream);
+
 /* Bytes of device workspace ulysses_attn_fwd needs for these sizes: zero when
  * one pass of query tiles fills the GPU, else room for fp32 partial outputs of
  * the key-range splits that small problems are cut into (merged, with the

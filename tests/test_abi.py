@@ -36,7 +36,8 @@ def test_header_declares_the_boundary():
                           "ulysses_a2a_reduce_replicated",
                           "ulysses_cu_seqlens_from_positions", "ulysses_attn_fwd",
                           "ulysses_attn_fwd_layout", "ulysses_attn_bwd_layout",
-                          "ulysses_attn_bwd_layout_f32kv",
+                          "ulysses_attn_bwd_layout_f32kv", "ulysses_attn_fwd_chunk",
+                          "ulysses_attn_merge", "ulysses_attn_merge_finish",
                           "ulysses_attn_fwd_workspace_bytes",
                           "ulysses_attn_bwd_workspace_bytes", "ulysses_attn_bwd",
                           "ulysses_profile_start", "ulysses_profile_stop",
@@ -163,6 +164,25 @@ def test_layout_argument_errors(lib):
         _p(8 * A), _p(9 * A), None, _p(10 * A), ctypes.c_size_t(1 << 30), ctypes.byref(ok_q), None,
         1, 64, 4, 2, 128, ctypes.c_float(0.125), 1, -1, -1, None)
     assert rc == NULL
+
+
+def test_chunk_and_merge_argument_errors(lib):
+    from ulysses_sequence_attention_rank_amd import Layout
+    lq, lk = Layout(1, 64 * 4 * 128, 0, 4 * 128, 128), Layout(1, 16 * 2 * 128, 0, 2 * 128, 128)
+
+    def chunk(k_start=0, Sk=16):
+        return lib.ulysses_attn_fwd_chunk(
+            _p(A), _p(2 * A), _p(3 * A), _p(4 * A), _p(5 * A), None, None, _p(6 * A),
+            ctypes.c_size_t(1 << 30), ctypes.byref(lq), ctypes.byref(lk), 1, 64, k_start, Sk, 4, 2,
+            128, ctypes.c_float(0.125), 1, -1, -1, None)
+    assert chunk(k_start=60, Sk=16) == SHAPE    # past the sequence end
+    assert chunk(k_start=-1) == SHAPE
+    assert chunk(Sk=0) == SHAPE
+    m = lib.ulysses_attn_merge
+    assert m(_p(A), _p(2 * A), _p(3 * A), _p(4 * A), 1, 8, 2, 12, None) == UNSUP   # D/4 = 3
+    assert m(None, _p(2 * A), _p(3 * A), _p(4 * A), 1, 8, 2, 64, None) == NULL
+    f = lib.ulysses_attn_merge_finish
+    assert f(_p(A), _p(2 * A), None, _p(3 * A), _p(2 * A), 1, 8, 2, 64, None) == UNSUP  # lse aliases
 
 
 def test_attn_bwd_argument_errors(lib):

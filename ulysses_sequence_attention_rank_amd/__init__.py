@@ -20,7 +20,8 @@ __all__ = [
     "UlyssesError", "lib_path", "load", "a2a_pack", "a2a_unpack", "a2a_pack_into",
     "a2a_unpack_into", "a2a_pack_multi_into", "a2a_unpack_multi_into", "a2a_pack_replicated_into",
     "a2a_reduce_replicated_into", "cu_seqlens_from_positions", "attn_fwd", "attn_bwd",
-    "attn_fwd_workspace_bytes", "attn_bwd_workspace_bytes", "Layout", "view_layout", "profile_start", "profile_stop", "profile_report",
+    "attn_fwd_workspace_bytes", "attn_bwd_workspace_bytes", "Layout", "view_layout",
+    "attn_fwd_chunk", "attn_merge", "attn_merge_finish", "profile_start", "profile_stop", "profile_report",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -35,7 +36,8 @@ EXPORTS = ("ulysses_a2a_pack", "ulysses_a2a_unpack", "ulysses_a2a_pack_multi",
            "ulysses_a2a_unpack_multi", "ulysses_a2a_pack_replicated",
            "ulysses_a2a_reduce_replicated", "ulysses_cu_seqlens_from_positions",
            "ulysses_attn_fwd", "ulysses_attn_fwd_layout", "ulysses_attn_bwd_layout",
-           "ulysses_attn_bwd_layout_f32kv",
+           "ulysses_attn_bwd_layout_f32kv", "ulysses_attn_fwd_chunk", "ulysses_attn_merge",
+           "ulysses_attn_merge_finish",
            "ulysses_attn_fwd_workspace_bytes", "ulysses_attn_bwd_workspace_bytes", "ulysses_attn_bwd",
            "ulysses_profile_start", "ulysses_profile_stop", "ulysses_profile_report",
            "ulysses_last_error")
@@ -73,6 +75,9 @@ def load():
     lib.ulysses_attn_fwd_layout.argtypes = [vp] * 9 + [sz, vp, vp] + [i32] * 5 + [f32] + [i32] * 3 + [vp]
     lib.ulysses_attn_bwd_layout.argtypes = [vp] * 14 + [sz, vp, vp] + [i32] * 5 + [f32] + [i32] * 3 + [vp]
     lib.ulysses_attn_bwd_layout_f32kv.argtypes = lib.ulysses_attn_bwd_layout.argtypes
+    lib.ulysses_attn_fwd_chunk.argtypes = [vp] * 8 + [sz, vp, vp] + [i32] * 7 + [f32] + [i32] * 3 + [vp]
+    lib.ulysses_attn_merge.argtypes = [vp] * 4 + [i32] * 4 + [vp]
+    lib.ulysses_attn_merge_finish.argtypes = [vp] * 5 + [i32] * 4 + [vp]
     lib.ulysses_attn_fwd_workspace_bytes.restype = sz
     lib.ulysses_attn_bwd_workspace_bytes.argtypes = [i32] * 5
     lib.ulysses_attn_bwd_workspace_bytes.restype = sz
@@ -337,6 +342,66 @@ def attn_fwd(q, k, v, *, sink=None, cu_seqlens=None, n_seqs=None, causal=True, w
         0 if workspace is None else workspace.numel(), ctypes.byref(lq), ctypes.byref(lk), B, S, hq,
         hkv, D, float(softmax_scale), int(bool(causal)), int(window_left), int(window_right),
         _stream(q.device)), "ulysses_attn_fwd_layout")
+    return out, lse
+
+
+def attn_fwd_chunk(q, k_chunk, v_chunk, k_start: int, *, cu_seqlens=None, n_seqs=None, causal=True,
+                   window_left=-1, window_right=-1, softmax_scale=None, out=None, lse=None,
+                   workspace=None):
+    """Attention of q (``[B, S, hq, D]`` or a strided view, as ``attn_fwd``)
+    against the keys at positions ``[k_start, k_start + Sk)`` of every batch
+    row, held in ``k_chunk``/``v_chunk`` ``[B, Sk, hkv, D]`` (views allowed).
+    Returns (out fp32 ``[B, S, hq, D]`` normalised over the chunk, lse fp32
+    ``[B, hq, S]``); rows seeing no key of the chunk get 0 and -inf."""
+    for name, t in (("q", q), ("k_chunk", k_chunk), ("v_chunk", v_chunk)):
+        _dev(t, name, torch.bfloat16, strided=True)
+    B, S, hq, D, lq = view_layout(q)
+    Bk, Sk, hkv, Dk, lk = view_layout(k_chunk)
+    if (Bk, Dk) != (B, D):
+        raise ValueError("q and the KV chunk disagree on B or D")
+    _same_view(k_chunk, v_chunk, "k_chunk and v_chunk")
+    if softmax_scale is None:
+        softmax_scale = D ** -0.5
+    if out is None:
+        out = torch.empty((B, S, hq, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, hq, S), dtype=torch.float32, device=q.device)
+    _dev(out, "out", torch.float32), _dev(lse, "lse", torch.float32)
+    if workspace is None:
+        need = attn_fwd_workspace_bytes(B, S, hq, hkv, D)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
+    _check(load().ulysses_attn_fwd_chunk(
+        _p(q), _p(k_chunk), _p(v_chunk), _p(out), _p(lse), _p(cu_seqlens), _p(n_seqs),
+        _p(workspace), 0 if workspace is None else workspace.numel(), ctypes.byref(lq),
+        ctypes.byref(lk), B, S, int(k_start), Sk, hq, hkv, D, float(softmax_scale),
+        int(bool(causal)), int(window_left), int(window_right), _stream(q.device)),
+        "ulysses_attn_fwd_chunk")
+    return out, lse
+
+
+def attn_merge(acc_out, acc_lse, out, lse):
+    """acc := exact merge of acc with one more chunk's (out, lse), in place."""
+    for name, t in (("acc_out", acc_out), ("acc_lse", acc_lse), ("out", out), ("lse", lse)):
+        _dev(t, name, torch.float32)
+    B, S, hq, D = acc_out.shape
+    if out.shape != acc_out.shape or acc_lse.shape != (B, hq, S) or lse.shape != (B, hq, S):
+        raise ValueError("attn_merge: shape mismatch")
+    _check(load().ulysses_attn_merge(_p(acc_out), _p(acc_lse), _p(out), _p(lse), B, S, hq, D,
+                                     _stream(out.device)), "ulysses_attn_merge")
+    return acc_out, acc_lse
+
+
+def attn_merge_finish(acc_out, acc_lse, *, sink=None, out=None, lse=None):
+    """Final bf16 O and LSE from the accumulator, the sink joining once."""
+    _dev(acc_out, "acc_out", torch.float32), _dev(acc_lse, "acc_lse", torch.float32)
+    B, S, hq, D = acc_out.shape
+    out = torch.empty((B, S, hq, D), dtype=torch.bfloat16, device=acc_out.device) if out is None else out
+    lse = torch.empty_like(acc_lse) if lse is None else lse
+    if sink is not None:
+        _dev(sink, "sink", torch.float32)
+    _check(load().ulysses_attn_merge_finish(_p(acc_out), _p(acc_lse), _p(sink), _p(out), _p(lse), B,
+                                            S, hq, D, _stream(acc_out.device)),
+           "ulysses_attn_merge_finish")
     return out, lse
 
 

@@ -100,6 +100,8 @@ int make_map(const uly_layout* L, int B, int S, int H, int D, const char* name, 
   m.Sl = uly::make_fastdiv(Sl);
   m.uniform = (B == 1 || L->batch == (int64_t)S * L->token) &&
               (L->shards == 1 || L->shard == (int64_t)Sl * L->token);
+  m.s0 = 0;
+  m.s_len = S;
   return ok();
 }
 
@@ -135,6 +137,11 @@ uly::AttnArgs make_args(const void* q, const void* k, const void* v, const float
   a.wl = wl;
   a.wr = wr;
   a.nsplit = 1;
+  a.k_lo_s = 0;
+  a.k_hi_s = S;
+  a.kt_lo = 0;
+  a.kt_hi = B * S;
+  a.o_f32 = 0;
   return a;
 }
 
@@ -423,6 +430,87 @@ int ulysses_attn_fwd(const void* q, const void* k, const void* v, void* out, flo
   return ulysses_attn_fwd_layout(q, k, v, out, lse, sink, cu_seqlens, n_seqs, workspace,
                                  workspace_bytes, &lq, &lk, B, S, hq, hkv, D, softmax_scale, causal,
                                  window_left, window_right, stream);
+}
+
+int ulysses_attn_fwd_chunk(const void* q, const void* k_chunk, const void* v_chunk, float* out,
+                           float* lse, const int32_t* cu_seqlens, const int32_t* n_seqs,
+                           void* workspace, size_t workspace_bytes, const uly_layout* q_layout,
+                           const uly_layout* kv_layout, int B, int S, int k_start, int Sk, int hq,
+                           int hkv, int D, float softmax_scale, int causal, int window_left,
+                           int window_right, void* stream) {
+  int rc = check_attn(q, k_chunk, v_chunk, cu_seqlens, n_seqs, B, S, hq, hkv, D, softmax_scale,
+                      window_left, window_right);
+  if (rc) return rc;
+  if (!out || !lse) return fail(ULY_ERR_NULL, "NULL out/lse");
+  if (k_start < 0 || Sk <= 0 || (int64_t)k_start + Sk > S)
+    return fail(ULY_ERR_SHAPE, "chunk [%d, %d) is not inside [0, S=%d)", k_start, k_start + Sk, S);
+  const size_t need = ulysses_attn_fwd_workspace_bytes(B, S, hq, hkv, D);
+  if (need > 0 && !workspace) return fail(ULY_ERR_NULL, "NULL workspace (%zu bytes needed)", need);
+  if (workspace_bytes < need)
+    return fail(ULY_ERR_CAPACITY, "workspace of %zu bytes < %zu needed", workspace_bytes, need);
+  if (!aligned(q, 16) || !aligned(k_chunk, 16) || !aligned(v_chunk, 16) || !aligned(out, 16) ||
+      !aligned(lse, 4) || !aligned(cu_seqlens, 4) || !aligned(n_seqs, 4) || !aligned(workspace, 256))
+    return fail(ULY_ERR_ALIGN, "q/k/v/out need 16-byte alignment, lse/cu 4-byte, workspace 256-byte");
+  uly::AttnArgs a = make_args(q, k_chunk, v_chunk, nullptr, cu_seqlens, n_seqs, B, S, hq, hkv,
+                              softmax_scale, causal, window_left, window_right);
+  if ((rc = make_map(q_layout, B, S, hq, D, "q", a.mq)) || (rc = make_map(kv_layout, B, Sk, hkv, D, "kv", a.mk)))
+    return rc;
+  // the chunk tensors hold positions [k_start, k_start + Sk) of each batch row
+  a.mk.S = uly::make_fastdiv(S);
+  a.mk.s0 = k_start;
+  a.mk.s_len = Sk;
+  if (B > 1) a.mk.uniform = 0;
+  a.k_lo_s = k_start;
+  a.k_hi_s = k_start + Sk;
+  if (a.mk.uniform) {  // B == 1: keep every tile row inside the chunk
+    a.kt_lo = k_start;
+    a.kt_hi = k_start + Sk;
+  }
+  a.out = (__bf16*)out;
+  a.lse = lse;
+  a.o_f32 = 1;
+  if (need > 0) {
+    a.nsplit = uly::fwd_splits(B, S, hq, uly::fwd_block_rows(B, S, hq, D));
+    a.part = (float*)workspace;
+    a.part_pdp = (float*)((char*)workspace + align256((size_t)a.nsplit * B * S * hq * D * 4));
+  }
+  return hip_status(uly::attn_fwd_launch(a, D, (hipStream_t)stream), "ulysses_attn_fwd_chunk launch");
+}
+
+static int check_merge(const void* a, const void* b, int B, int S, int hq, int D) {
+  if (!a || !b) return fail(ULY_ERR_NULL, "NULL pointer");
+  if (B <= 0 || S <= 0 || hq <= 0 || D <= 0)
+    return fail(ULY_ERR_SHAPE, "sizes must be positive (B=%d S=%d hq=%d D=%d)", B, S, hq, D);
+  if (D % 4 || 256 % (D / 4))
+    return fail(ULY_ERR_UNSUPPORTED, "D=%d: a multiple of 4 with D/4 dividing 256", D);
+  if ((int64_t)B * S * hq * D >= kMaxI32 * 8ll) return fail(ULY_ERR_SHAPE, "problem too large");
+  return ok();
+}
+
+int ulysses_attn_merge(float* acc_out, float* acc_lse, const float* out, const float* lse, int B,
+                       int S, int hq, int D, void* stream) {
+  int rc = check_merge(acc_out, out, B, S, hq, D);
+  if (rc) return rc;
+  if (!acc_lse || !lse) return fail(ULY_ERR_NULL, "NULL lse");
+  if (!aligned(acc_out, 16) || !aligned(out, 16) || !aligned(acc_lse, 4) || !aligned(lse, 4))
+    return fail(ULY_ERR_ALIGN, "outputs need 16-byte alignment, LSE 4-byte");
+  return hip_status(uly::attn_merge_launch(acc_out, acc_lse, out, lse, B, S, hq, D,
+                                           (hipStream_t)stream),
+                    "ulysses_attn_merge launch");
+}
+
+int ulysses_attn_merge_finish(const float* acc_out, const float* acc_lse, const float* sink,
+                              void* out, float* lse, int B, int S, int hq, int D, void* stream) {
+  int rc = check_merge(acc_out, out, B, S, hq, D);
+  if (rc) return rc;
+  if (!acc_lse || !lse) return fail(ULY_ERR_NULL, "NULL lse");
+  if (lse == acc_lse) return fail(ULY_ERR_UNSUPPORTED, "lse must not alias acc_lse");
+  if (!aligned(acc_out, 16) || !aligned(out, 8) || !aligned(acc_lse, 4) || !aligned(lse, 4) ||
+      !aligned(sink, 4))
+    return fail(ULY_ERR_ALIGN, "acc_out needs 16-byte alignment, out 8-byte, LSE/sink 4-byte");
+  return hip_status(uly::attn_merge_finish_launch(acc_out, acc_lse, sink, out, lse, B, S, hq, D,
+                                                  (hipStream_t)stream),
+                    "ulysses_attn_merge_finish launch");
 }
 
 size_t ulysses_attn_bwd_workspace_bytes(int B, int S, int hq, int hkv, int D) {

@@ -26,16 +26,22 @@ constexpr int kBK = 64;  // keys (or queries) per LDS tile
 // r of Sl tokens), at b*batch + r*shard + sl*token + h*head elements.  The
 // head layout [B][S][H][D] and, for B = 1, the rank's heads of the
 // sequence-sharded [P][B][S/P][H][D] are `uniform`: t*token.
+// A KV chunk (positions [s0, s0 + s_len) of every batch row, the inner step
+// of a ring over KV chunks) is addressed by its position s - s0, clamped
+// into the chunk (rows outside it are never visible; the clamp keeps their
+// loads inside the tensor).  Whole tensors: s0 = 0, s_len = S.
 struct RowMap {
   int64_t batch, shard, token, head;
   FastDiv S, Sl;
-  int uniform;
+  int uniform;  // row(t) = (t - s0) * token (the caller keeps t inside the chunk)
+  int s0, s_len;
 };
 
 __device__ __forceinline__ int64_t row_of(const RowMap& m, int t) {
-  if (m.uniform) return (int64_t)t * m.token;
-  const u32 b = fdiv((u32)t, m.S), s = (u32)t - b * m.S.d;
-  const u32 r = fdiv(s, m.Sl), sl = s - r * m.Sl.d;
+  if (m.uniform) return (int64_t)(t - m.s0) * m.token;
+  const u32 b = fdiv((u32)t, m.S);
+  const int sc = min(max((int)((u32)t - b * m.S.d) - m.s0, 0), m.s_len - 1);
+  const u32 r = fdiv((u32)sc, m.Sl), sl = (u32)sc - r * m.Sl.d;
   return (int64_t)b * m.batch + (int64_t)r * m.shard + (int64_t)sl * m.token;
 }
 
@@ -66,6 +72,10 @@ struct AttnArgs {
   const int32_t* n_seqs;
   RowMap mq;  // q, out, dout, dq
   RowMap mk;  // k, v, dk, dv
+  // keys restricted to positions [k_lo_s, k_hi_s) of each batch row (one KV
+  // chunk; 0 and S otherwise); K/V tile rows are clamped to [kt_lo, kt_hi)
+  int k_lo_s, k_hi_s, kt_lo, kt_hi;
+  int o_f32;  // forward: O written normalised in fp32, [T][hq][D] (chunk results)
   int B, S, T, hq, hkv, G;
   float scale;       // softmax scale
   float scale_log2;  // softmax scale * log2(e)
@@ -123,8 +133,9 @@ __device__ __forceinline__ void doc_bounds(const AttnArgs& a, int t, int& start,
 __device__ __forceinline__ void key_interval(const AttnArgs& a, int i, int& klo, int& khi) {
   int ds, de;
   doc_bounds(a, i, ds, de);
-  klo = ds;
-  khi = de;
+  const int b0 = (i / a.S) * a.S;  // the chunk's keys in query i's batch row
+  klo = max(ds, b0 + a.k_lo_s);
+  khi = min(de, b0 + a.k_hi_s);
   if (a.causal) khi = min(khi, i + 1);
   if (a.wl >= 0) klo = max(klo, i - a.wl);
   if (a.wr >= 0) khi = min(khi, i + a.wr + 1);
@@ -222,7 +233,8 @@ __device__ __forceinline__ void tile_load_lds(char* lds, const E* g, int ld, int
 // offset to the head): rows row0 .. row0+R-1, clamped to row_end - 1.
 template <int D, int R, int NW, bool UNIFORM>
 __device__ __forceinline__ void tile_load_lds_map(char* lds, const __bf16* base, const RowMap& m,
-                                                  int row0, int row_end, int wave, int lane) {
+                                                  int row0, int row_lo, int row_end, int wave,
+                                                  int lane) {
   constexpr int kInstr = R * D * 2 / 1024;
   static_assert(kInstr % NW == 0, "tile must split evenly over the waves");
 #pragma unroll
@@ -231,8 +243,8 @@ __device__ __forceinline__ void tile_load_lds_map(char* lds, const __bf16* base,
     const int pos = i * 64 + lane;
     const int r = pos / Swz<D>::kSlots;
     const int c = (pos % Swz<D>::kSlots) ^ Swz<D>::f(r);
-    const int row = min(row0 + r, row_end - 1);
-    const __bf16* src = base + (UNIFORM ? (int64_t)row * m.token : row_of(m, row)) + c * 8;
+    const int row = max(min(row0 + r, row_end - 1), row_lo);
+    const __bf16* src = base + (UNIFORM ? (int64_t)(row - m.s0) * m.token : row_of(m, row)) + c * 8;
     __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(lds + i * 1024), 16, 0, 0);
   }
 }

@@ -66,8 +66,10 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnArgs a) {
   int it_lo, it_hi;
   split_range((wg_hi - wg_lo + kBK - 1) / kBK, blockIdx.y, a.nsplit, it_lo, it_hi);
   if (it_lo < it_hi) {
-    tile_load_lds_map<D, kBK, NW, KV_UNIFORM>(smem, kbase, a.mk, wg_lo + it_lo * kBK, a.T, wave, lane);
-    tile_load_lds_map<D, kBK, NW, KV_UNIFORM>(smem + TILE, vbase, a.mk, wg_lo + it_lo * kBK, a.T, wave, lane);
+    tile_load_lds_map<D, kBK, NW, KV_UNIFORM>(smem, kbase, a.mk, wg_lo + it_lo * kBK, a.kt_lo, a.kt_hi,
+                                              wave, lane);
+    tile_load_lds_map<D, kBK, NW, KV_UNIFORM>(smem + TILE, vbase, a.mk, wg_lo + it_lo * kBK, a.kt_lo,
+                                              a.kt_hi, wave, lane);
   }
   const f32x16 zero = {};
 
@@ -78,8 +80,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnArgs a) {
     __syncthreads();                // everyone's have, and tile it-1 is no longer read
     if (it + 1 < it_hi) {
       char* nxt = smem + (cur ^ 1) * STAGE;
-      tile_load_lds_map<D, kBK, NW, KV_UNIFORM>(nxt, kbase, a.mk, k0 + kBK, a.T, wave, lane);
-      tile_load_lds_map<D, kBK, NW, KV_UNIFORM>(nxt + TILE, vbase, a.mk, k0 + kBK, a.T, wave, lane);
+      tile_load_lds_map<D, kBK, NW, KV_UNIFORM>(nxt, kbase, a.mk, k0 + kBK, a.kt_lo, a.kt_hi, wave, lane);
+      tile_load_lds_map<D, kBK, NW, KV_UNIFORM>(nxt + TILE, vbase, a.mk, k0 + kBK, a.kt_lo, a.kt_hi, wave,
+                                                lane);
     }
     const char* kt = smem + cur * STAGE;
     const char* vt = kt + TILE;
@@ -195,16 +198,28 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnArgs a) {
     const float oscale = (m_fin == -INFINITY || l_tot == 0.f || mr == -INFINITY)
                              ? 0.f : exp2f(mr - m_fin) / l_tot;
     if (qvalid[qb]) {
-      __bf16* orow = a.out + row_of(a.mq, qrow[qb]) + (int64_t)h * a.mq.head;
+      if (a.o_f32) {
+        float* orow = reinterpret_cast<float*>(a.out) + ((int64_t)qrow[qb] * a.hq + h) * D;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          u32x2 w;
-          w[0] = pack_bf16x2(oacc[qb][nb][4 * i + 0] * oscale, oacc[qb][nb][4 * i + 1] * oscale);
-          w[1] = pack_bf16x2(oacc[qb][nb][4 * i + 2] * oscale, oacc[qb][nb][4 * i + 3] * oscale);
-          *reinterpret_cast<u32x2*>(orow + 32 * nb + 8 * i + 4 * hf) = w;
-        }
+          for (int i = 0; i < 4; ++i) {
+            const f32x4 w = {oacc[qb][nb][4 * i + 0] * oscale, oacc[qb][nb][4 * i + 1] * oscale,
+                             oacc[qb][nb][4 * i + 2] * oscale, oacc[qb][nb][4 * i + 3] * oscale};
+            *reinterpret_cast<f32x4*>(orow + 32 * nb + 8 * i + 4 * hf) = w;
+          }
+      } else {
+        __bf16* orow = a.out + row_of(a.mq, qrow[qb]) + (int64_t)h * a.mq.head;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            u32x2 w;
+            w[0] = pack_bf16x2(oacc[qb][nb][4 * i + 0] * oscale, oacc[qb][nb][4 * i + 1] * oscale);
+            w[1] = pack_bf16x2(oacc[qb][nb][4 * i + 2] * oscale, oacc[qb][nb][4 * i + 3] * oscale);
+            *reinterpret_cast<u32x2*>(orow + 32 * nb + 8 * i + 4 * hf) = w;
+          }
+      }
       if (hf == 0) {
         const float lse = (m_fin == -INFINITY || l_tot == 0.f) ? -INFINITY
                           : (m_fin + __log2f(l_tot)) * 0.6931471805599453f;
@@ -243,10 +258,14 @@ __global__ __launch_bounds__(256) void attn_fwd_merge_kernel(AttnArgs a) {
     if (a.sink != nullptr) z += exp2f(s2 - mf);
   }
   const float inv = z > 0.f ? 1.f / z : 0.f;
-  u32x2 w;
-  w[0] = pack_bf16x2(o[0] * inv, o[1] * inv);
-  w[1] = pack_bf16x2(o[2] * inv, o[3] * inv);
-  *reinterpret_cast<u32x2*>(a.out + row_of(a.mq, t) + (int64_t)h * a.mq.head + c) = w;
+  if (a.o_f32) {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + r * D + c) = o * inv;
+  } else {
+    u32x2 w;
+    w[0] = pack_bf16x2(o[0] * inv, o[1] * inv);
+    w[1] = pack_bf16x2(o[2] * inv, o[3] * inv);
+    *reinterpret_cast<u32x2*>(a.out + row_of(a.mq, t) + (int64_t)h * a.mq.head + c) = w;
+  }
   if (c == 0) a.lse[li] = z > 0.f ? (mf + __log2f(z)) * 0.6931471805599453f : -INFINITY;
 }
 
@@ -273,6 +292,104 @@ static hipError_t launch_fwd_t(const AttnArgs& args, hipStream_t st) {
 
 // D=64: two query blocks per wave (halves the LDS operand traffic per
 // product) still fit two waves per SIMD; D=128 takes one block per wave.
+// ---------------------------------------------------------- chunk merge
+//
+// Exact combination of attention over two disjoint KV chunks (the ring inner
+// step): with L = log(e^La + e^Lb), O = e^(La - L) Oa + e^(Lb - L) Ob.  In
+// place on the accumulator (acc_o fp32 [T][hq][D], acc_lse [B][hq][S]).  One
+// thread per 4 columns; a (row, head) never spans two blocks, and its new LSE
+// is written after the block has read the old one.
+struct MergeArgs {
+  float* acc_o;
+  float* acc_lse;
+  const float* o;
+  const float* lse;
+  const float* sink;
+  __bf16* out;
+  float* lse_out;
+  int T, S, hq, D;
+};
+
+__device__ __forceinline__ int merge_lse_index(const MergeArgs& m, int t, int h) {
+  const int b = t / m.S;
+  return (b * m.hq + h) * m.S + (t - b * m.S);
+}
+
+__global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs m) {
+  const int64_t rows = (int64_t)m.T * m.hq;
+  const int64_t idx4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int q4 = m.D / 4;
+  const int64_t r = idx4 / q4;  // flattened (token, head) row
+  const int c = (int)(idx4 - r * q4) * 4;
+  float la = -INFINITY, lb = -INFINITY, l = -INFINITY;
+  int li = 0;
+  if (r < rows) {
+    const int t = (int)(r / m.hq), h = (int)(r - (int64_t)t * m.hq);
+    li = merge_lse_index(m, t, h);
+    la = m.acc_lse[li];
+    lb = m.lse[li];
+    const float mx = fmaxf(la, lb);
+    if (mx != -INFINITY) l = mx + log1pf(__expf(-fabsf(la - lb)));
+    const float wa = la == -INFINITY ? 0.f : __expf(la - l);
+    const float wb = lb == -INFINITY ? 0.f : __expf(lb - l);
+    f32x4* pa = reinterpret_cast<f32x4*>(m.acc_o + r * m.D + c);
+    const f32x4 ob = *reinterpret_cast<const f32x4*>(m.o + r * m.D + c);
+    *pa = *pa * wa + ob * wb;
+  }
+  __syncthreads();
+  if (r < rows && c == 0) m.acc_lse[li] = l;
+}
+
+// The accumulator's final form: the sink joins the denominator (L' =
+// log(e^L + e^sink), O' = e^(L - L') O), O rounded to bf16 [T][hq][D].
+__global__ __launch_bounds__(256) void attn_merge_finish_kernel(MergeArgs m) {
+  const int64_t rows = (int64_t)m.T * m.hq;
+  const int64_t idx4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int q4 = m.D / 4;
+  const int64_t r = idx4 / q4;
+  const int c = (int)(idx4 - r * q4) * 4;
+  if (r >= rows) return;
+  const int t = (int)(r / m.hq), h = (int)(r - (int64_t)t * m.hq);
+  const int li = merge_lse_index(m, t, h);
+  const float l = m.acc_lse[li];
+  float lf = l, w = l == -INFINITY ? 0.f : 1.f;
+  if (m.sink != nullptr) {
+    const float s = m.sink[h];
+    const float mx = fmaxf(l, s);
+    lf = mx + log1pf(__expf(-fabsf(l - s)));
+    w = l == -INFINITY ? 0.f : __expf(l - lf);
+  }
+  const f32x4 o = *reinterpret_cast<const f32x4*>(m.acc_o + r * m.D + c) * w;
+  u32x2 pk;
+  pk[0] = pack_bf16x2(o[0], o[1]);
+  pk[1] = pack_bf16x2(o[2], o[3]);
+  *reinterpret_cast<u32x2*>(m.out + r * m.D + c) = pk;
+  if (c == 0) m.lse_out[li] = lf;
+}
+
+hipError_t attn_merge_launch(float* acc_o, float* acc_lse, const float* o, const float* lse, int B,
+                             int S, int hq, int D, hipStream_t st) {
+  MergeArgs m = {acc_o, acc_lse, o, lse, nullptr, nullptr, nullptr, B * S, S, hq, D};
+  const int64_t items = (int64_t)B * S * hq * (D / 4);
+  if (items == 0) return hipSuccess;
+  ProfScope prof("attn_merge", st);
+  hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, st, m);
+  return hipGetLastError();
+}
+
+hipError_t attn_merge_finish_launch(const float* acc_o, const float* acc_lse, const float* sink,
+                                    void* out, float* lse, int B, int S, int hq, int D,
+                                    hipStream_t st) {
+  MergeArgs m = {const_cast<float*>(acc_o), const_cast<float*>(acc_lse), nullptr, nullptr, sink,
+                 (__bf16*)out, lse, B * S, S, hq, D};
+  const int64_t items = (int64_t)B * S * hq * (D / 4);
+  if (items == 0) return hipSuccess;
+  ProfScope prof("attn_merge_finish", st);
+  hipLaunchKernelGGL(attn_merge_finish_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, st,
+                     m);
+  return hipGetLastError();
+}
+
 hipError_t attn_fwd_launch(const AttnArgs& a, int D, hipStream_t st) {
   if (D == 128) return launch_fwd_t<128, 4, 1>(a, st);
   return fwd_block_rows(a.B, a.S, a.hq, D) == 256 ? launch_fwd_t<64, 4, 2>(a, st)

@@ -16,6 +16,11 @@ hipError_t reduce_replicated_launch(const void* head, bool head_f32, void* seq, 
 hipError_t segments_launch(const void* pos, int pos_bytes, int P, int B, int S, int32_t* cu,
                            int32_t* n_seqs, int32_t* max_len, hipStream_t st);
 hipError_t attn_fwd_launch(const AttnArgs& a, int D, hipStream_t st);
+hipError_t attn_merge_launch(float* acc_o, float* acc_lse, const float* o, const float* lse, int B,
+                             int S, int hq, int D, hipStream_t st);
+hipError_t attn_merge_finish_launch(const float* acc_o, const float* acc_lse, const float* sink,
+                                    void* out, float* lse, int B, int S, int hq, int D,
+                                    hipStream_t st);
 hipError_t attn_bwd_launch(const AttnArgs& a, int D, hipStream_t st);
 void dkdv_launch(const AttnArgs& a, int D, hipStream_t st);  // part of attn_bwd_launch
 
