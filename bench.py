@@ -473,14 +473,18 @@ def rocprof_summary(d, workload):
     with open(os.path.join(d, "commands.txt")) as f:
         commands = [ln.rstrip() for ln in f if ln.strip()]
 
-    # scale factors: the pack kernel moves a known number of bytes per launch
-    # (Q, K, V in the forward and dO in the backward; each element read once
-    # and written once)
-    elem_q = case.B * case.S * case.Hq * case.D
-    elem_kv = case.B * case.S * case.Hkv * case.D
-    pack_bytes = 2 * (2 * elem_q + 2 * elem_kv) / 4
-    f_scale = pack_bytes / (fe["a2a_pack"]["FETCH_SIZE"] * 1024)
-    w_scale = pack_bytes / (wr["a2a_pack"]["WRITE_SIZE"] * 1024)
+    # scale factors: every thread of the pack kernel (16-byte vectors, 4 per
+    # thread, grids a whole number of blocks for these shapes) reads 64 bytes
+    # and writes 64, so a dispatch moves Grid_Size * 64 bytes each way
+    def pack_scale(sub, counter):
+        known = got = 0.0
+        for r in rows(sub, "counter_collection.csv"):
+            if _rocprof_name(r["Kernel_Name"]) == "a2a_pack" and r["Counter_Name"] == counter:
+                known += float(r["Grid_Size"]) * 64
+                got += float(r["Counter_Value"]) * 1024
+        return known / got
+    f_scale, w_scale = pack_scale("fetch", "FETCH_SIZE"), pack_scale("write", "WRITE_SIZE")
+    pack_bytes = None
 
     traffic = {}
     for k in sorted(k for k in fe if not k.startswith("torch")):
@@ -528,8 +532,8 @@ def rocprof_summary(d, workload):
             tail = (f"{t['fetch_kib']} | {t['write_kib']} | {t['bytes_per_launch'] / 1e6:.2f}"
                     if t else " | | ")
             f.write(f"| {k} | {vals} | {tail} |\n")
-        f.write(f"\nCounter scale (pack kernel, {pack_bytes / 1e6:.2f} MB read and written per "
-                f"launch): FETCH_SIZE x {f_scale:.4f}, WRITE_SIZE x {w_scale:.4f}.\n")
+        f.write(f"\nCounter scale (pack kernel, Grid_Size x 64 bytes read and written per "
+                f"dispatch): FETCH_SIZE x {f_scale:.4f}, WRITE_SIZE x {w_scale:.4f}.\n")
     print(open(out).read())
 
 
