@@ -516,9 +516,10 @@ int ulysses_attn_merge_finish(const float* acc_out, const float* acc_lse, const 
 size_t ulysses_attn_bwd_workspace_bytes(int B, int S, int hq, int hkv, int D) {
   if (B <= 0 || S <= 0 || hq <= 0 || hkv <= 0 || D <= 0) return 0;
   // delta, sum_j P dP, LSE*log2(e) (each [B][hq][S] fp32), dsink partials [hq][parts],
-  // fp16 copies of q, dout ([B][S][hq][D]) and k, v ([B][S][hkv][D])
+  // fp16 copies of q, dout ([B*S + kPad][hq][D]) and k, v ([B*S + kPad][hkv][D])
   const size_t rows = align256((size_t)B * S * hq * sizeof(float));
-  const size_t qsz = align256((size_t)B * S * hq * D * 2), kvsz = align256((size_t)B * S * hkv * D * 2);
+  const size_t qsz = align256(((size_t)B * S + uly::kPad) * hq * D * 2),
+               kvsz = align256(((size_t)B * S + uly::kPad) * hkv * D * 2);
   return 3 * rows + align256((size_t)hq * kDsinkParts * sizeof(float)) + 2 * qsz + 2 * kvsz +
          split_part_bytes(B, S, hq, hkv, D);
 }
@@ -564,7 +565,8 @@ static int attn_bwd_impl(const void* q, const void* k, const void* v, const void
   a.lse2 = (float*)(ws + 2 * rows);
   a.dsink_part = (float*)(ws + 3 * rows);
   char* h16 = ws + 3 * rows + align256((size_t)hq * kDsinkParts * sizeof(float));
-  const size_t qsz = align256((size_t)B * S * hq * D * 2), kvsz = align256((size_t)B * S * hkv * D * 2);
+  const size_t qsz = align256(((size_t)B * S + uly::kPad) * hq * D * 2),
+               kvsz = align256(((size_t)B * S + uly::kPad) * hkv * D * 2);
   a.q16 = (_Float16*)h16;
   a.do16 = (_Float16*)(h16 + qsz);
   a.k16 = (_Float16*)(h16 + 2 * qsz);

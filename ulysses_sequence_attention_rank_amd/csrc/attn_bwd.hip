@@ -35,6 +35,10 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(AttnArgs a) {
   const int c = threadIdx.x % TPR;
   float acc = 0.f;
   const bool valid = row < a.T * a.hq;
+  if (!valid && row < (a.T + kPad) * a.hq) {  // the zero rows after the last token
+    const u32x4 z = {0, 0, 0, 0};
+    *reinterpret_cast<u32x4*>(a.do16 + (int64_t)row * D + 8 * c) = z;
+  }
   if (valid) {
     const int t = row / a.hq, hh = row - t * a.hq;
     const int64_t src = row_of(a.mq, t) + (int64_t)hh * a.mq.head + 8 * c;
@@ -63,9 +67,15 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(AttnArgs a) {
 // as `m` says: every bf16 value of magnitude <= 65504 is an fp16 value (fp16
 // keeps 11 significant bits, bf16 8); larger magnitudes saturate, values below
 // 2^-14 round to fp16's subnormals.  One 16-byte chunk per thread; hd8 = H*D/8.
+// Elements n .. n_pad - 1 (the kPad rows after the last token) are zero.
 __global__ __launch_bounds__(256) void to_f16_kernel(const __bf16* src, RowMap m, FastDiv hd8,
-                                                     FastDiv d8, _Float16* dst, int64_t n) {
+                                                     FastDiv d8, _Float16* dst, int64_t n,
+                                                     int64_t n_pad) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i >= n && i < n_pad) {
+    const u32x4 z = {0, 0, 0, 0};
+    *reinterpret_cast<u32x4*>(dst + i) = z;
+  }
   if (i < n) {
     const u32 chunk = (u32)(i >> 3);
     const u32 t = fdiv(chunk, hd8), rest = chunk - t * hd8.d;
@@ -157,12 +167,16 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(AttnArgs a) {
   const _Float16* kbase = a.k16 + (int64_t)g * D;
   const _Float16* vbase = a.v16 + (int64_t)g * D;
   const int ld = a.hkv * D;
+  // K and V tiles share row stride and swizzle: one set of per-lane offsets;
+  // rows up to wg_hi + 63 < T + kPad exist (zero past the last token)
+  const TileOffsets<D, kBK, NW> offs(ld, wave, lane);
   // this split's share of the key tiles
   int it_lo, it_hi;
   split_range((wg_hi - wg_lo + kBK - 1) / kBK, blockIdx.y, a.nsplit, it_lo, it_hi);
   if (it_lo < it_hi) {
-    tile_load_lds<D, kBK, NW>(smem, kbase, ld, wg_lo + it_lo * kBK, a.T, wave, lane);
-    tile_load_lds<D, kBK, NW>(smem + TILE, vbase, ld, wg_lo + it_lo * kBK, a.T, wave, lane);
+    const int64_t r0 = (int64_t)(wg_lo + it_lo * kBK) * ld;
+    offs.load(smem, kbase + r0, wave);
+    offs.load(smem + TILE, vbase + r0, wave);
   }
 
   for (int it = it_lo; it < it_hi; ++it) {
@@ -172,8 +186,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(AttnArgs a) {
     __syncthreads();
     if (it + 1 < it_hi) {
       char* nxt = smem + (cur ^ 1) * STAGE;
-      tile_load_lds<D, kBK, NW>(nxt, kbase, ld, k0 + kBK, a.T, wave, lane);
-      tile_load_lds<D, kBK, NW>(nxt + TILE, vbase, ld, k0 + kBK, a.T, wave, lane);
+      const int64_t r0 = (int64_t)(k0 + kBK) * ld;
+      offs.load(nxt, kbase + r0, wave);
+      offs.load(nxt + TILE, vbase + r0, wave);
     }
     const char* kt = smem + cur * STAGE;
     const char* vt = kt + TILE;
@@ -270,7 +285,7 @@ template <int D, int NW>
 static hipError_t launch_bwd_t(const AttnArgs& args, hipStream_t st) {
   AttnArgs a = args;
   {
-    const int rows = a.T * a.hq, rpb = 256 / (D / 8);
+    const int rows = (a.T + kPad) * a.hq, rpb = 256 / (D / 8);
     ProfScope prof("attn_bwd_pre", st);
     hipLaunchKernelGGL(attn_bwd_pre_kernel<D>, dim3((rows + rpb - 1) / rpb), dim3(256), 0, st, a);
   }
@@ -278,12 +293,13 @@ static hipError_t launch_bwd_t(const AttnArgs& args, hipStream_t st) {
     ProfScope prof("attn_bwd_f16", st);
     const int64_t nq = (int64_t)a.T * a.hq * D, nkv = (int64_t)a.T * a.hkv * D;
     const FastDiv d8 = make_fastdiv(D / 8), q8 = make_fastdiv(a.hq * D / 8), k8 = make_fastdiv(a.hkv * D / 8);
-    hipLaunchKernelGGL(to_f16_kernel, dim3((nq / 8 + 255) / 256), dim3(256), 0, st, a.q, a.mq, q8, d8,
-                       a.q16, nq);
-    hipLaunchKernelGGL(to_f16_kernel, dim3((nkv / 8 + 255) / 256), dim3(256), 0, st, a.k, a.mk, k8, d8,
-                       a.k16, nkv);
-    hipLaunchKernelGGL(to_f16_kernel, dim3((nkv / 8 + 255) / 256), dim3(256), 0, st, a.v, a.mk, k8, d8,
-                       a.v16, nkv);
+    const int64_t pq = nq + (int64_t)kPad * a.hq * D, pkv = nkv + (int64_t)kPad * a.hkv * D;
+    hipLaunchKernelGGL(to_f16_kernel, dim3((pq / 8 + 255) / 256), dim3(256), 0, st, a.q, a.mq, q8, d8,
+                       a.q16, nq, pq);
+    hipLaunchKernelGGL(to_f16_kernel, dim3((pkv / 8 + 255) / 256), dim3(256), 0, st, a.k, a.mk, k8, d8,
+                       a.k16, nkv, pkv);
+    hipLaunchKernelGGL(to_f16_kernel, dim3((pkv / 8 + 255) / 256), dim3(256), 0, st, a.v, a.mk, k8, d8,
+                       a.v16, nkv, pkv);
   }
   dkdv_launch(a, D, st);
   {

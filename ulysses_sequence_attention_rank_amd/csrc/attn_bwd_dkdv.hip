@@ -110,9 +110,21 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char st0[SM::kStage];
   __shared__ __attribute__((aligned(1024))) char st1[SM::kStage];
 
-  const int L = blockIdx.x;
-  if (L >= a.n_tiles * a.hkv) return;
-  const int kt = L / a.hkv, g = L % a.hkv;
+  // Unsplit (large) grids: key tiles of one KV head in bands per XCD, so
+  // neighbouring key tiles, which read mostly the same Q/dO tiles at about
+  // the same time, share an L2 (measured 4 % on a 131072-token causal head;
+  // on small split grids the plain order is faster).
+  int L = (int)blockIdx.x, g, kt;
+  if (a.nsplit == 1) {
+    L = xcd_band_item(L, a.n_tiles * a.hkv, 32);
+    if (L < 0) return;
+    g = L / a.n_tiles;
+    kt = L - g * a.n_tiles;
+  } else {
+    if (L >= a.n_tiles * a.hkv) return;
+    kt = L / a.hkv;
+    g = L - kt * a.hkv;
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hf = lane >> 5;
   const int k0 = kt * BN;
   const int krow = k0 + 32 * wave + (lane & 31);
@@ -141,34 +153,48 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(AttnArgs a) {
   const int ld = a.hq * D;
   const int nq = (wg_hi - wg_lo + kBK - 1) / kBK;  // query tiles per head
   const int n_iter = nq * a.G;
-  auto tile_q0 = [&](int it) { return wg_lo + (it % nq) * kBK; };
-  auto issue = [&](int it, char* buf) {
-    const int hh = it / nq, qa = wg_lo + (it - hh * nq) * kBK;
-    const int h = g * a.G + hh;
-    tile_load_lds<D, kBK, NW>(buf, a.q16 + (int64_t)h * D, ld, qa, a.T, wave, lane);
-    tile_load_lds<D, kBK, NW>(buf + SM::kTile, a.do16 + (int64_t)h * D, ld, qa, a.T, wave, lane);
+  // Q and dO tiles share row stride and swizzle: one set of per-lane offsets
+  const TileOffsets<D, kBK, NW> offs(ld, wave, lane);
+  int nh = 0, nt = 0;  // (head in the group, tile) of the next tile to issue
+  auto issue = [&](char* buf) {
+    const int qa = wg_lo + nt * kBK, h = g * a.G + nh;
+    const int64_t row0 = (int64_t)qa * a.hq + h;  // rows up to wg_hi + 63 < T + kPad exist
+    offs.load(buf, a.q16 + row0 * D, wave);
+    offs.load(buf + SM::kTile, a.do16 + row0 * D, wave);
     if (wave < 2) {
       const int idx = lse_index(a, min(qa + lane, a.T - 1), h);
       const float* src = wave == 0 ? a.lse2 + idx : a.delta + idx;
       __builtin_amdgcn_global_load_lds(src, (lds_void*)(buf + 2 * SM::kTile + wave * kBK * 4), 4, 0, 0);
     }
+    if (++nt == nq) {
+      nt = 0;
+      ++nh;
+    }
+    return qa;
   };
-  int it_end = n_iter;  // set to this split's end below
-  auto step = [&](int it, const char* buf, char* nxt) {
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile `it` have landed
-    __syncthreads();                // everyone's have, and the other stage is free
-    if (it + 1 < it_end) issue(it + 1, nxt);
-    dkdv_tile<D, NW>(a, buf, kvs, dkacc, dvacc, tile_q0(it), full_lo, full_hi, qlo, qhi, wave, lane);
+  auto compute = [&](const char* buf, int qa) {
+    dkdv_tile<D, NW>(a, buf, kvs, dkacc, dvacc, qa, full_lo, full_hi, qlo, qhi, wave, lane);
   };
 
   // this split's share of the (head, query tile) iterations
   int it_lo, it_hi;
   split_range(n_iter, blockIdx.y, a.nsplit, it_lo, it_hi);
-  it_end = it_hi;
-  if (it_lo < it_hi) issue(it_lo, st0);
+  if (it_lo < it_hi) {
+    nh = it_lo / nq;
+    nt = it_lo - nh * nq;
+  }
+  int qa0 = it_lo < it_hi ? issue(st0) : 0, qa1 = 0;
   for (int it = it_lo; it < it_hi; it += 2) {
-    step(it, st0, st1);
-    if (it + 1 < it_hi) step(it + 1, st1, st0);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile `it` have landed
+    __syncthreads();                // everyone's have, and stage 1 is free
+    if (it + 1 < it_hi) qa1 = issue(st1);
+    compute(st0, qa0);
+    if (it + 1 < it_hi) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (it + 2 < it_hi) qa0 = issue(st0);
+      compute(st1, qa1);
+    }
   }
 
   // dK, dV: lane holds column d = 32 nb + l % 32 of key rows 8 i + 4 hf + j
@@ -234,7 +260,9 @@ static void launch_dkdv_t(const AttnArgs& args, hipStream_t st) {
   b.nsplit = dkdv_splits(b.B, b.S, b.hkv);
   {
     ProfScope prof("attn_bwd_dkdv", st);
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, NW>), dim3(b.n_tiles * b.hkv, b.nsplit), dim3(NW * 64),
+    const int items = b.n_tiles * b.hkv;
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, NW>), dim3((items + kXcds - 1) / kXcds * kXcds, b.nsplit),
+                       dim3(NW * 64),
                        0, st, b);
   }
   if (b.nsplit > 1) {

@@ -19,7 +19,8 @@
 
 namespace uly {
 
-constexpr int kBK = 64;  // keys (or queries) per LDS tile
+constexpr int kBK = 64;   // keys (or queries) per LDS tile
+constexpr int kPad = 64;  // zero rows after the backward's fp16 copies
 
 // Where the D contiguous elements of (token t of the flattened B*S, head h)
 // of a bf16 tensor start: with t = b*S + s and s = r*Sl + sl (sequence shard
@@ -60,7 +61,9 @@ struct AttnArgs {
   float* pdp;    // bwd: sum_j P_ij dP_ij = dO_i . O_i with the exact O, [B][hq][S]
   float* lse2;   // bwd: LSE * log2(e) (+inf for rows without keys), [B][hq][S]
   // bwd: exact fp16 copies of q, k, v, dout (the backward's products run in
-  // fp16, whose 11-bit significand rounds P and dS 8x finer than bf16)
+  // fp16, whose 11-bit significand rounds P and dS 8x finer than bf16), each
+  // followed by kPad zero rows so that tiles starting anywhere below T can
+  // be loaded without clamping
   _Float16* q16;
   _Float16* k16;
   _Float16* v16;
@@ -159,6 +162,24 @@ __device__ __forceinline__ int lse_index(const AttnArgs& a, int t, int h) {
   return (b * a.hq + h) * a.S + (t - b * a.S);
 }
 
+// XCD-aware deal of n work items over a grid of 8 * ceil(n / 8) blocks:
+// blocks go round-robin to the 8 XCDs, and the j-th block of an XCD takes
+// the j-th item of that XCD's share, the shares interleaved in bands of W
+// consecutive items.  The W work-groups resident on an XCD at once then
+// work on neighbouring items and share what they stream through its L2.
+// The XCD order reverses every other band (a snake), so work that grows or
+// shrinks linearly along the items evens out over the XCDs (which cannot
+// take over each other's blocks).  Returns -1 for padding blocks.
+__device__ __forceinline__ int xcd_band_item(int b, int n, int W) {
+  const int n8 = (n + kXcds - 1) / kXcds;  // blocks per XCD
+  const int xcd = b % kXcds, j = b / kXcds;
+  const int band = j / W, within = j - band * W;
+  const int w = min(W, n8 - band * W);     // the last band may be narrower
+  const int slot = (band & 1) ? kXcds - 1 - xcd : xcd;
+  const int item = band * kXcds * W + slot * w + within;
+  return item < n ? item : -1;
+}
+
 // Work decode shared by the query-tile kernels.  Query tiles are ordered last
 // first (causal tiles near the end see the most keys); the G query heads of a
 // KV head that work on the same tile are put on one XCD (L2 shares their K/V).
@@ -248,6 +269,30 @@ __device__ __forceinline__ void tile_load_lds_map(char* lds, const __bf16* base,
     __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(lds + i * 1024), 16, 0, 0);
   }
 }
+
+// Per-lane byte offsets of a wave's direct-to-LDS loads of an R x D tile of
+// a matrix with row stride `ld` elements, relative to the tile's first row:
+// the same for every tile, so a loop computes them once and issues each load
+// as a uniform base plus this offset (the rows must exist: callers pad).
+template <int D, int R, int NW>
+struct TileOffsets {
+  static constexpr int kN = R * D * 2 / 1024 / NW;  // loads per wave
+  int off[kN];
+  __device__ __forceinline__ TileOffsets(int ld, int wave, int lane) {
+#pragma unroll
+    for (int k = 0; k < kN; ++k) {
+      const int pos = (wave + k * NW) * 64 + lane;
+      const int r = pos / Swz<D>::kSlots;
+      off[k] = (r * ld + (((pos % Swz<D>::kSlots) ^ Swz<D>::f(r)) << 3)) * 2;
+    }
+  }
+  __device__ __forceinline__ void load(char* lds, const void* tile0, int wave) const {
+#pragma unroll
+    for (int k = 0; k < kN; ++k)
+      __builtin_amdgcn_global_load_lds((const void*)(reinterpret_cast<const char*>(tile0) + off[k]),
+                                       (lds_void*)(lds + (wave + k * NW) * 1024), 16, 0, 0);
+  }
+};
 
 // natural operand: rows r0 + l%32, columns 16 s + 8 hf .. + 7
 template <int D>
