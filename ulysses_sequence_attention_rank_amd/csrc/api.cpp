@@ -98,8 +98,9 @@ int make_map(const uly_layout* L, int B, int S, int H, int D, const char* name, 
   m.head = L->head;
   m.S = uly::make_fastdiv(S);
   m.Sl = uly::make_fastdiv(Sl);
+  // one stride per token (and 64-row tiles addressable with 32-bit offsets)
   m.uniform = (B == 1 || L->batch == (int64_t)S * L->token) &&
-              (L->shards == 1 || L->shard == (int64_t)Sl * L->token);
+              (L->shards == 1 || L->shard == (int64_t)Sl * L->token) && L->token < (1 << 24);
   m.s0 = 0;
   m.s_len = S;
   return ok();

@@ -129,11 +129,16 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(AttnArgs a) {
   constexpr int BM = 32 * NW, NB = D / 32, KS = D / 16;
   constexpr int TILE = kBK * D * 2;
   constexpr int STAGE = 2 * TILE;  // K, then V
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  // distinct LDS objects per stage, each access naming one statically: the
+  // next tile's direct-to-LDS loads then provably miss the current tile's
+  // reads, and those reads do not wait for them
+  __shared__ __attribute__((aligned(1024))) char stage0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage1[STAGE];
 
   int qt, h;
   if (!decode_qtile(a, qt, h)) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hf = lane >> 5;
+  const int lane = threadIdx.x & 63, hf = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = h / a.G;
   const int q0 = qt * BM;
   const int qrow = q0 + 32 * wave + (lane & 31);
@@ -169,46 +174,52 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(AttnArgs a) {
   const int ld = a.hkv * D;
   // K and V tiles share row stride and swizzle: one set of per-lane offsets;
   // rows up to wg_hi + 63 < T + kPad exist (zero past the last token)
-  const TileOffsets<D, kBK, NW> offs(ld, wave, lane);
+  const BufTileLoader<D, kBK, NW> offs(ld, wave, lane);
+  SwzOffsets<D> so(lane);
   // this split's share of the key tiles
   int it_lo, it_hi;
   split_range((wg_hi - wg_lo + kBK - 1) / kBK, blockIdx.y, a.nsplit, it_lo, it_hi);
   if (it_lo < it_hi) {
     const int64_t r0 = (int64_t)(wg_lo + it_lo * kBK) * ld;
-    offs.load(smem, kbase + r0, wave);
-    offs.load(smem + TILE, vbase + r0, wave);
+    offs.load(stage0, kbase + r0, kBK, wave);
+    offs.load(stage0 + TILE, vbase + r0, kBK, wave);
   }
 
-  for (int it = it_lo; it < it_hi; ++it) {
-    const int cur = (it - it_lo) & 1;
+  // one key tile: `cur` holds tile `it`, tile it+1 goes to `nxt`
+  auto step = [&](int it, const char* cur, char* nxt) __attribute__((always_inline)) {
     const int k0 = wg_lo + it * kBK;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (it + 1 < it_hi) {
-      char* nxt = smem + (cur ^ 1) * STAGE;
       const int64_t r0 = (int64_t)(k0 + kBK) * ld;
-      offs.load(nxt, kbase + r0, wave);
-      offs.load(nxt + TILE, vbase + r0, wave);
+      offs.load(nxt, kbase + r0, kBK, wave);
+      offs.load(nxt + TILE, vbase + r0, kBK, wave);
     }
-    const char* kt = smem + cur * STAGE;
-    const char* vt = kt + TILE;
+    const char* kt = cur;
+    const char* vt = cur + TILE;
+    // one set of read offsets for both stages (two hoisted sets would not
+    // fit the register budget next to the accumulators)
+    so.refresh();
 
     const bool full = k0 >= full_lo && k0 + kBK <= full_hi;
+    // this lane's visible keys relative to its first key slot of the tile:
+    // slot e of block mb holds key offset 32 mb + 8 (e / 4) + e % 4
+    const int vis_lo = klo - (k0 + 4 * hf), vis_hi = khi - (k0 + 4 * hf);
     // one 32-key block at a time keeps two accumulators live, not four
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       f32x16 sacc, dpacc;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        sacc = mfma32h(swz_nat<D>(kt, 32 * mb, s, lane), qf[s], s == 0 ? zero : sacc);
-        dpacc = mfma32h(swz_nat<D>(vt, 32 * mb, s, lane), dof[s], s == 0 ? zero : dpacc);
+        sacc = mfma32h(so.nat_at(kt, 32 * mb, s), qf[s], s == 0 ? zero : sacc);
+        dpacc = mfma32h(so.nat_at(vt, 32 * mb, s), dof[s], s == 0 ? zero : dpacc);
       }
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], a.scale_log2, -lse2));
         if (!full) {
-          const int key = k0 + 32 * mb + 8 * (e >> 2) + 4 * hf + (e & 3);
-          if (key < klo || key >= khi) p = 0.f;
+          const int c = 32 * mb + 8 * (e >> 2) + (e & 3);
+          if (c < vis_lo || c >= vis_hi) p = 0.f;
         }
         if (want_pdp) pdp = __builtin_fmaf(p, dpacc[e], pdp);
         sacc[e] = p * (dpacc[e] - dlt);  // dS^T
@@ -219,9 +230,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(AttnArgs a) {
         const bf16x8 df = acc_frag_h(sacc, ii);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
-          dqacc[nb] = mfma32h(swz_tr<D>(kt, 32 * mb + 16 * ii, 32 * nb, lane), df, dqacc[nb]);
+          dqacc[nb] = mfma32h(so.tr_at(kt, 32 * mb + 16 * ii, nb), df, dqacc[nb]);
       }
     }
+  };
+  for (int it = it_lo; it < it_hi; it += 2) {
+    step(it, stage0, stage1);
+    if (it + 1 < it_hi) step(it + 1, stage1, stage0);
   }
 
   pdp = halves_sum(pdp);

@@ -270,6 +270,37 @@ __device__ __forceinline__ void tile_load_lds_map(char* lds, const __bf16* base,
   }
 }
 
+// Direct-to-LDS loads of R x D tiles whose rows lie `ld` elements apart,
+// through a buffer resource: the tile's first row is a wave-uniform base in
+// scalar registers and each lane's byte offset inside the tile is computed
+// once, so a load costs no vector instruction.  Rows at or beyond the
+// resource's bound read as zero, so a tile that runs past the matrix's last
+// row needs no clamping (callers mask those rows).  Needs 64 * ld < 2^24.
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+template <int D, int R, int NW>
+struct BufTileLoader {
+  static constexpr int kN = R * D * 2 / 1024 / NW;  // loads per wave
+  unsigned off[kN];
+  int row_bytes;
+  __device__ __forceinline__ BufTileLoader(int64_t ld, int wave, int lane) : row_bytes((int)ld * 2) {
+#pragma unroll
+    for (int k = 0; k < kN; ++k) {
+      const int pos = (wave + k * NW) * 64 + lane;
+      const int r = pos / Swz<D>::kSlots;
+      off[k] = (unsigned)(r * row_bytes + (((pos % Swz<D>::kSlots) ^ Swz<D>::f(r)) << 4));
+    }
+  }
+  // rows [0, rows) of the tile at `tile0` exist (rows >= 1); `wave` uniform
+  __device__ __forceinline__ void load(char* lds, const void* tile0, int rows, int wave) const {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(tile0), (short)0, min(rows, R) * row_bytes, kRsrcWord3);
+#pragma unroll
+    for (int k = 0; k < kN; ++k)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + (wave + k * NW) * 1024), 16, off[k],
+                                               0, 0, 0);
+  }
+};
+
 // Per-lane byte offsets of a wave's direct-to-LDS loads of an R x D tile of
 // a matrix with row stride `ld` elements, relative to the tile's first row:
 // the same for every tile, so a loop computes them once and issues each load
@@ -315,6 +346,50 @@ __device__ __forceinline__ bf16x8 swz_tr(const char* lds, int r0, int d0, int la
   const i16x8 x = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8, x);
 }
+
+// Per-lane byte offsets of the swz_nat / swz_tr reads, computed once: the
+// swizzle repeats every 16 rows, so for r0 a multiple of 16 the natural
+// operand of step s at rows r0 + l%32 lies at r0 * 2D + nat[s] and the
+// transposed operand of columns 32 nb at rows r0 .. r0+15 at r0 * 2D +
+// tr[nb][0] (rows +0..7) and r0 * 2D + tr[nb][1] (rows +8..15).  Kernels
+// with two LDS stages share one set between the stages, the stage base
+// folding into each read's immediate offset.
+template <int D>
+struct SwzOffsets {
+  int nat[D / 16];
+  int tr[D / 32][2];
+  __device__ __forceinline__ explicit SwzOffsets(int lane) {
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) nat[s] = Swz<D>::off(lane & 31, 2 * s + (lane >> 5));
+    const int j = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb) {
+      const int col = 32 * nb + 16 * (grp & 1) + 4 * (j & 3);
+      const int kb = 4 * (grp >> 1) + (j >> 2);
+      tr[nb][0] = Swz<D>::off(kb, col >> 3) + (col & 7) * 2;
+      tr[nb][1] = Swz<D>::off(kb + 8, col >> 3) + (col & 7) * 2;
+    }
+  }
+  // Makes the offsets opaque to the optimiser at this point, so that
+  // addresses derived from them are formed where they are used instead of
+  // being hoisted, one register each, out of an enclosing loop.
+  __device__ __forceinline__ void refresh() {
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) asm volatile("" : "+v"(nat[s]));
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb) asm volatile("" : "+v"(tr[nb][0]), "+v"(tr[nb][1]));
+  }
+  __device__ __forceinline__ bf16x8 nat_at(const char* lds, int r0, int s) const {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(lds + r0 * 2 * D + nat[s]));
+  }
+  __device__ __forceinline__ bf16x8 tr_at(const char* lds, int r0, int nb) const {
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds + r0 * 2 * D + tr[nb][0]));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds + r0 * 2 * D + tr[nb][1]));
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    const i16x8 x = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, x);
+  }
+};
 
 // Contiguous share [lo, hi) of n iterations for split s of ns.
 __device__ __forceinline__ void split_range(int n, int s, int ns, int& lo, int& hi) {

@@ -17,16 +17,41 @@ namespace uly {
 
 constexpr float kRescaleLog2 = 8.0f;
 
+// K and V tiles of the 64 keys from row0 into dst (V one tile after K):
+// uniformly strided rows through buffer loads (rows past kt_hi read as zero
+// and are masked), general layouts through per-row address maps with the
+// rows clamped to [kt_lo, kt_hi)
+template <int D, int NW, bool KV_UNIFORM>
+__device__ __forceinline__ void load_kv(char* dst, const AttnArgs& a, const BufTileLoader<D, kBK, NW>& kvl,
+                                        const __bf16* kbase, const __bf16* vbase, int row0, int wave,
+                                        int lane) {
+  constexpr int TILE = kBK * D * 2;
+  if constexpr (KV_UNIFORM) {
+    const int64_t o = (int64_t)(row0 - a.mk.s0) * a.mk.token;
+    kvl.load(dst, kbase + o, a.kt_hi - row0, wave);
+    kvl.load(dst + TILE, vbase + o, a.kt_hi - row0, wave);
+  } else {
+    tile_load_lds_map<D, kBK, NW, false>(dst, kbase, a.mk, row0, a.kt_lo, a.kt_hi, wave, lane);
+    tile_load_lds_map<D, kBK, NW, false>(dst + TILE, vbase, a.mk, row0, a.kt_lo, a.kt_hi, wave, lane);
+  }
+}
+
 template <int D, int NW, int QB, bool KV_UNIFORM>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnArgs a) {
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a) {
   constexpr int BM = 32 * QB * NW, NB = D / 32, KS = D / 16;
   constexpr int TILE = kBK * D * 2;  // bytes of one K or V tile
   constexpr int STAGE = 2 * TILE;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  // Two LDS stages as distinct objects: each access below names one of them
+  // statically, which lets the compiler see that the next tile's
+  // direct-to-LDS loads cannot alias the current tile's reads, so it does not
+  // make those reads wait for the loads.
+  __shared__ __attribute__((aligned(1024))) char stage0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage1[STAGE];
 
   int qt, h;
   if (!decode_qtile(a, qt, h)) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hf = lane >> 5;
+  const int lane = threadIdx.x & 63, hf = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = h / a.G;
   const int q0 = qt * BM;
 
@@ -65,27 +90,20 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnArgs a) {
   // this split's share of the key tiles
   int it_lo, it_hi;
   split_range((wg_hi - wg_lo + kBK - 1) / kBK, blockIdx.y, a.nsplit, it_lo, it_hi);
-  if (it_lo < it_hi) {
-    tile_load_lds_map<D, kBK, NW, KV_UNIFORM>(smem, kbase, a.mk, wg_lo + it_lo * kBK, a.kt_lo, a.kt_hi,
-                                              wave, lane);
-    tile_load_lds_map<D, kBK, NW, KV_UNIFORM>(smem + TILE, vbase, a.mk, wg_lo + it_lo * kBK, a.kt_lo,
-                                              a.kt_hi, wave, lane);
-  }
+  const BufTileLoader<D, kBK, NW> kvl(a.mk.token, wave, lane);
+  SwzOffsets<D> so(lane);
+  if (it_lo < it_hi) load_kv<D, NW, KV_UNIFORM>(stage0, a, kvl, kbase, vbase, wg_lo + it_lo * kBK, wave, lane);
   const f32x16 zero = {};
 
-  for (int it = it_lo; it < it_hi; ++it) {
-    const int cur = (it - it_lo) & 1;
+  // one key tile: `cur` holds tile `it`, tile it+1 goes to `nxt`
+  auto step = [&](int it, const char* cur, char* nxt) __attribute__((always_inline)) {
     const int k0 = wg_lo + it * kBK;
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile `it` have landed
     __syncthreads();                // everyone's have, and tile it-1 is no longer read
-    if (it + 1 < it_hi) {
-      char* nxt = smem + (cur ^ 1) * STAGE;
-      tile_load_lds_map<D, kBK, NW, KV_UNIFORM>(nxt, kbase, a.mk, k0 + kBK, a.kt_lo, a.kt_hi, wave, lane);
-      tile_load_lds_map<D, kBK, NW, KV_UNIFORM>(nxt + TILE, vbase, a.mk, k0 + kBK, a.kt_lo, a.kt_hi, wave,
-                                                lane);
-    }
-    const char* kt = smem + cur * STAGE;
-    const char* vt = kt + TILE;
+    if (it + 1 < it_hi) load_kv<D, NW, KV_UNIFORM>(nxt, a, kvl, kbase, vbase, k0 + kBK, wave, lane);
+    const char* kt = cur;
+    const char* vt = cur + TILE;
+    so.refresh();  // one set of read offsets serves both stages
 
     // S^T = K Q^T: each K operand read feeds QB products
     f32x16 sacc[QB][2];
@@ -93,7 +111,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnArgs a) {
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const bf16x8 kf = swz_nat<D>(kt, 32 * mb, s, lane);
+        const bf16x8 kf = so.nat_at(kt, 32 * mb, s);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) sacc[qb][mb] = mfma32(kf, qf[qb][s], s == 0 ? zero : sacc[qb][mb]);
       }
@@ -103,12 +121,15 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       if (!full) {
+        // this lane's visible keys relative to its first key slot of the
+        // tile: slot e of block mb holds key offset 32 mb + 8 (e / 4) + e % 4
+        const int vis_lo = klo[qb] - (k0 + 4 * hf), vis_hi = khi[qb] - (k0 + 4 * hf);
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            const int key = k0 + 32 * mb + 8 * (e >> 2) + 4 * hf + (e & 3);
-            if (key < klo[qb] || key >= khi[qb]) sacc[qb][mb][e] = -INFINITY;
+            const int c = 32 * mb + 8 * (e >> 2) + (e & 3);
+            if (c < vis_lo || c >= vis_hi) sacc[qb][mb][e] = -INFINITY;
           }
       }
       // online softmax in the log2 domain
@@ -152,10 +173,21 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnArgs a) {
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const bf16x8 vf = swz_tr<D>(vt, 16 * ks, 32 * nb, lane);
+        const bf16x8 vf = so.tr_at(vt, 16 * ks, nb);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) oacc[qb][nb] = mfma32(vf, pf[qb][ks], oacc[qb][nb]);
       }
+  };
+  if constexpr (QB == 1) {
+    for (int it = it_lo; it < it_hi; it += 2) {
+      step(it, stage0, stage1);
+      if (it + 1 < it_hi) step(it + 1, stage1, stage0);
+    }
+  } else {  // two query blocks: one copy of the body keeps them in registers
+    for (int it = it_lo; it < it_hi; ++it) {
+      const bool odd = (it - it_lo) & 1;
+      step(it, odd ? stage1 : stage0, odd ? stage0 : stage1);
+    }
   }
 
   if (a.nsplit > 1) {
