@@ -233,6 +233,28 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(AttnArgs a) {
           dqacc[nb] = mfma32h(so.tr_at(kt, 32 * mb + 16 * ii, nb), df, dqacc[nb]);
       }
     }
+    // keep 4 operand reads in flight ahead of the products (the default
+    // schedule issues each read just before its product and waits out the
+    // LDS latency every time): per 32-key block, S and dP (2 KS products,
+    // one read each), then dQ (2 NB products, two reads each)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      constexpr int PF = 4;
+      __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);  // LDS reads
+#pragma unroll
+      for (int i = 0; i < 2 * KS - PF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * NB - PF / 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, PF / 2, 0);
+    }
   };
   for (int it = it_lo; it < it_hi; it += 2) {
     step(it, stage0, stage1);

@@ -36,6 +36,108 @@ __device__ __forceinline__ void load_kv(char* dst, const AttnArgs& a, const BufT
   }
 }
 
+// S^T = K Q^T for one 64-key tile `kt`: each K operand read feeds QB products.
+template <int D, int QB>
+__device__ __forceinline__ void tile_scores(f32x16 (&sacc)[QB][2], const SwzOffsets<D>& so, const char* kt,
+                                            const bf16x8 (&qf)[QB][D / 16]) {
+  const f32x16 zero = {};
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      const bf16x8 kf = so.nat_at(kt, 32 * mb, s);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sacc[qb][mb] = mfma32(kf, qf[qb][s], s == 0 ? zero : sacc[qb][mb]);
+    }
+  if constexpr (QB == 1) {
+    // keep 8 operand reads in flight ahead of the products (the default
+    // schedule issues each read just before its product and waits out the
+    // LDS latency every time)
+    constexpr int PF = 8, N = 2 * (D / 16);
+    __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);  // LDS reads
+#pragma unroll
+    for (int i = 0; i < N - PF; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
+  }
+}
+
+// First half of the online softmax of one query block over one tile: the
+// mask (unless the tile is wholly visible; vis_lo / vis_hi are the lane's
+// visible keys relative to its first key slot, slot e of block mb holding
+// key offset 32 mb + 8 (e / 4) + e % 4), the tile's row max in the log2
+// domain, and the lazy rescale of the running state when that max exceeds
+// the reference max by more than 2^8.  Returns the max to subtract.
+template <int NB>
+__device__ __forceinline__ float softmax_max(f32x16 (&sacc)[2], bool full, int vis_lo, int vis_hi,
+                                             float scale_log2, float& m_run, float& l_run,
+                                             f32x16 (&oacc)[NB]) {
+  if (!full) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int c = 32 * mb + 8 * (e >> 2) + (e & 3);
+        if (c < vis_lo || c >= vis_hi) sacc[mb][e] = -INFINITY;
+      }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[mb][e]);
+  mx = halves_max(mx) * scale_log2;
+  const bool grow = mx > m_run + kRescaleLog2;
+  if (__any(grow)) {
+    const float m_new = grow ? mx : m_run;
+    const float alpha = grow ? exp2f(m_run - m_new) : 1.f;
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[nb][e] *= alpha;
+  }
+  return m_run == -INFINITY ? 0.f : m_run;
+}
+
+// Second half: the probabilities 2^(s scale_log2 - msub), their fp32 row sum
+// (the LSE it yields also sets dsink's sink probabilities) and their bf16 B
+// operands of O^T += V^T P^T.
+__device__ __forceinline__ void softmax_exp(f32x16 (&sacc)[2], float msub, float scale_log2, float& l_run,
+                                            bf16x8 (&pf)[4]) {
+  float lsum = 0.f;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mb][e], scale_log2, -msub));
+      sacc[mb][e] = p;
+      lsum += p;
+    }
+  l_run += lsum;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) pf[2 * mb + ii] = acc_frag(sacc[mb], ii);
+}
+
+// O^T += V^T P^T for one tile `vt`: each V operand read feeds QB products.
+template <int D, int QB>
+__device__ __forceinline__ void tile_pv(f32x16 (&oacc)[QB][D / 32], const SwzOffsets<D>& so, const char* vt,
+                                        const bf16x8 (&pf)[QB][4]) {
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb) {
+      const bf16x8 vf = so.tr_at(vt, 16 * ks, nb);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) oacc[qb][nb] = mfma32(vf, pf[qb][ks], oacc[qb][nb]);
+    }
+}
+
 template <int D, int NW, int QB, bool KV_UNIFORM>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a) {
   constexpr int BM = 32 * QB * NW, NB = D / 32, KS = D / 16;
@@ -92,92 +194,26 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a) {
   split_range((wg_hi - wg_lo + kBK - 1) / kBK, blockIdx.y, a.nsplit, it_lo, it_hi);
   const BufTileLoader<D, kBK, NW> kvl(a.mk.token, wave, lane);
   SwzOffsets<D> so(lane);
-  if (it_lo < it_hi) load_kv<D, NW, KV_UNIFORM>(stage0, a, kvl, kbase, vbase, wg_lo + it_lo * kBK, wave, lane);
-  const f32x16 zero = {};
-
-  // one key tile: `cur` holds tile `it`, tile it+1 goes to `nxt`
+  // one key tile: `cur` holds tile `it` (K, then V), tile it+1 goes to `nxt`
   auto step = [&](int it, const char* cur, char* nxt) __attribute__((always_inline)) {
     const int k0 = wg_lo + it * kBK;
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile `it` have landed
     __syncthreads();                // everyone's have, and tile it-1 is no longer read
     if (it + 1 < it_hi) load_kv<D, NW, KV_UNIFORM>(nxt, a, kvl, kbase, vbase, k0 + kBK, wave, lane);
-    const char* kt = cur;
-    const char* vt = cur + TILE;
     so.refresh();  // one set of read offsets serves both stages
-
-    // S^T = K Q^T: each K operand read feeds QB products
     f32x16 sacc[QB][2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const bf16x8 kf = so.nat_at(kt, 32 * mb, s);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) sacc[qb][mb] = mfma32(kf, qf[qb][s], s == 0 ? zero : sacc[qb][mb]);
-      }
-
+    tile_scores<D, QB>(sacc, so, cur, qf);
     const bool full = k0 >= full_lo && k0 + kBK <= full_hi;
     bf16x8 pf[QB][4];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      if (!full) {
-        // this lane's visible keys relative to its first key slot of the
-        // tile: slot e of block mb holds key offset 32 mb + 8 (e / 4) + e % 4
-        const int vis_lo = klo[qb] - (k0 + 4 * hf), vis_hi = khi[qb] - (k0 + 4 * hf);
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int c = 32 * mb + 8 * (e >> 2) + (e & 3);
-            if (c < vis_lo || c >= vis_hi) sacc[qb][mb][e] = -INFINITY;
-          }
-      }
-      // online softmax in the log2 domain
-      float mx = -INFINITY;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[qb][mb][e]);
-      mx = halves_max(mx) * a.scale_log2;
-      const bool grow = mx > m_run[qb] + kRescaleLog2;
-      if (__any(grow)) {
-        const float m_new = grow ? mx : m_run[qb];
-        const float alpha = grow ? exp2f(m_run[qb] - m_new) : 1.f;
-        m_run[qb] = m_new;
-        l_run[qb] *= alpha;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) oacc[qb][nb][e] *= alpha;
-      }
-      const float msub = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
-      // fp32 row sum: the LSE it yields also sets dsink's sink probabilities
-      float lsum = 0.f;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][mb][e], a.scale_log2, -msub));
-          sacc[qb][mb][e] = p;
-          lsum += p;
-        }
-      l_run[qb] += lsum;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int ii = 0; ii < 2; ++ii) pf[qb][2 * mb + ii] = acc_frag(sacc[qb][mb], ii);
+      const float msub = softmax_max<NB>(sacc[qb], full, klo[qb] - (k0 + 4 * hf), khi[qb] - (k0 + 4 * hf),
+                                         a.scale_log2, m_run[qb], l_run[qb], oacc[qb]);
+      softmax_exp(sacc[qb], msub, a.scale_log2, l_run[qb], pf[qb]);
     }
-
-    // O^T += V^T P^T: each V operand read feeds QB products
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const bf16x8 vf = so.tr_at(vt, 16 * ks, nb);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) oacc[qb][nb] = mfma32(vf, pf[qb][ks], oacc[qb][nb]);
-      }
+    tile_pv<D, QB>(oacc, so, cur + TILE, pf);
   };
+  if (it_lo < it_hi) load_kv<D, NW, KV_UNIFORM>(stage0, a, kvl, kbase, vbase, wg_lo + it_lo * kBK, wave, lane);
   if constexpr (QB == 1) {
     for (int it = it_lo; it < it_hi; it += 2) {
       step(it, stage0, stage1);
