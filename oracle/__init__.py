@@ -5,6 +5,8 @@ CPU-baseline leg of ``bench.py`` may import it; the product package never does.
 The arithmetic lives in ``orc.c`` (compiled with gcc, OpenMP over rows); this
 module only marshals torch tensors in and out through ctypes.
 
+The sequence-tiled gated MLP (fp64 torch CPU matmuls) is in ``oracle/mlp.py``.
+
 parity unpinned: none.  Every function is pinned by the CPU tests in
 ``tests/test_oracle_*.py`` (library special cases, finite differences, closed
 forms, brute force, a hand-worked example and invariants of the method).

@@ -24,11 +24,13 @@ script; the workloads below are the five simulated Ulysses configurations):
 from __future__ import annotations
 
 import dataclasses
+import math
 from typing import List, Optional, Sequence, Tuple
 
 import torch
 
-__all__ = ["Case", "CONFIGS", "config_case", "make_inputs", "doc_lengths_uniform",
+__all__ = ["Case", "CONFIGS", "config_case", "make_inputs", "doc_lengths_uniform", "MlpInputs",
+           "make_mlp_inputs",
            "positions_from_doc_lengths", "seq_shards"]
 
 
@@ -182,3 +184,31 @@ def small_case(seed: int, *, P: int, B: int, S: int, Hq: int, Hkv: int, D: int,
         pos = torch.arange(S, dtype=torch.int64).repeat(B, 1)
         flat = None
     return Inputs(case, q, k, v, dout, sk, pos, flat)
+
+
+# ------------------------------------------------------------ tiled MLP inputs
+#
+# The gated MLP of one rank's tokens: x [T][H], gate and up weights [I][H],
+# down weight [H][I], output gradient dy [T][H], all bf16 (fp32 normal draws
+# rounded to nearest even).  The weights are drawn with standard deviation
+# 1/sqrt(fan-in) (gate, up: H; down: I), so the projections have unit scale.
+@dataclasses.dataclass
+class MlpInputs:
+    x: torch.Tensor
+    w_gate: torch.Tensor
+    w_up: torch.Tensor
+    w_down: torch.Tensor
+    dy: torch.Tensor
+
+
+def make_mlp_inputs(seed: int, T: int, H: int, I: int, device=None) -> MlpInputs:
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(T, H, generator=g)
+    wg = torch.randn(I, H, generator=g) / math.sqrt(H)
+    wu = torch.randn(I, H, generator=g) / math.sqrt(H)
+    wd = torch.randn(H, I, generator=g) / math.sqrt(I)
+    dy = torch.randn(T, H, generator=g)
+    def cvt(t):
+        t = t.to(torch.bfloat16)
+        return t.to(device) if device is not None else t
+    return MlpInputs(cvt(x), cvt(wg), cvt(wu), cvt(wd), cvt(dy))
