@@ -116,6 +116,7 @@ def main():
     ap.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD, choices=[1, 2, 3, 4, 5, 6],
                     help="which of the five simulated workloads (default: the S=4096 one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mlp", action="store_true", help="skip the sequence-tiled MLP measurement")
     ap.add_argument("--cpu-heads", type=int, default=None,
                     help="query heads of rank 0 the CPU oracle baseline runs (default: all of "
                          "rank 0's heads, every layer, for the S<=4096 workloads; one KV group of "
@@ -282,6 +283,7 @@ def main():
                 "avg_launch_ms": round(kern[dom][1] / kern[dom][0], 5)}
 
     ring = measure_ring(case, b, credit) if case.Hkv >= case.P else None
+    mlp = None if args.no_mlp else measure_tiled_mlp(dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -322,6 +324,7 @@ def main():
         "kernels": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in r.items()}
                     for k, r in rows.items()},
         "ring_inner_step": ring,
+        "tiled_mlp": mlp,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
@@ -418,6 +421,55 @@ def measure_ring(case, b, credit, chunks=4, reps=5):
             res[f"{name}_ms"] = round(e0.elapsed_time(e1) / reps, 4)
         res["ring_fwd_tflops"] = round(credit[var.name]["attn_fwd"] / (res["ring_ms"] * 1e-3) / 1e12, 1)
         out["layers"][var.name] = res
+    return out
+
+
+def measure_tiled_mlp(dev, T=32768, H=2048, I=8192, tile=8192, reps=3):
+    """The sequence-tiled gated MLP of one rank: a Llama-3.2-1B-sized MLP
+    (hidden 2048, intermediate 8192) over the 32768 tokens a rank holds in the
+    S=131072, P=4 workload, in tiles of 8192 tokens.  Forward and backward
+    timed apart with HIP events over `reps` repetitions each; credited FLOPs
+    6 T H I (forward) and 12 T H I (backward; its recompute of the gate and up
+    projections, 4 T H I, is not credited), against the bf16 dense peak."""
+    import torch
+
+    import ulysses_sequence_attention_rank_amd as uly
+    from ulysses_inputs import make_mlp_inputs
+    m = make_mlp_inputs(2026, T, H, I, device=dev)
+    ws = torch.empty(uly.tiled_mlp_workspace_bytes(T, H, I, tile), dtype=torch.uint8, device=dev)
+    y = torch.empty_like(m.x)
+    dx = torch.empty_like(m.x)
+    dwg = torch.empty((I, H), dtype=torch.float32, device=dev)
+    dwu = torch.empty_like(dwg)
+    dwd = torch.empty((H, I), dtype=torch.float32, device=dev)
+    fwd = lambda: uly.tiled_mlp_fwd(m.x, m.w_gate, m.w_up, m.w_down, tile, y=y, workspace=ws)
+    bwd = lambda: uly.tiled_mlp_bwd(m.x, m.w_gate, m.w_up, m.w_down, m.dy, tile, dx=dx, dw_gate=dwg,
+                                    dw_up=dwu, dw_down=dwd, workspace=ws)
+    out = {"workload": f"T{T}_H{H}_I{I}_tile{tile}", "T": T, "H": H, "I": I, "tile": tile}
+    thi = float(T) * H * I
+    for name, fn, credit in (("fwd", fwd, 6 * thi), ("bwd", bwd, 12 * thi)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[f"{name}_ms"] = round(ms, 4)
+        out[f"{name}_tflops"] = round(credit / (ms * 1e-3) / 1e12, 1)
+    out["tflops"] = round(18 * thi / ((out["fwd_ms"] + out["bwd_ms"]) * 1e-3) / 1e12, 1)
+    out["frac_of_peak"] = round(out["tflops"] / PEAK_BF16_TFLOPS, 4)
+    # per-kernel times of one forward and one backward
+    uly.profile_start()
+    fwd()
+    bwd()
+    torch.cuda.synchronize()
+    uly.profile_stop()
+    rep = uly.profile_report()
+    out["kernels"] = {k: {"launches": v[0], "total_ms": round(v[1], 4)} for k, v in rep.items()
+                      if k.startswith("mlp")}
     return out
 
 

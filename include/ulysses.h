@@ -271,6 +271,36 @@ int ulysses_attn_merge(float* acc_out, float* acc_lse, const float* out, const f
 int ulysses_attn_merge_finish(const float* acc_out, const float* acc_lse, const float* sink,
                               void* out, float* lse, int B, int S, int hq, int D, void* stream);
 
+/* ------------------------------------------------------------------------
+ * The sequence-tiled MLP of one rank (the TiledMLP / SequenceTiledCompute
+ * features of the DeepSpeed pull request that ports Ulysses to HF models:
+ * the layer's MLP computed over the rank's tokens in tiles along the
+ * sequence, so that only one tile's activations exist at a time, and the
+ * weight gradients added once after the tiles).  The gated MLP of the
+ * Llama-family models:  y = (silu(x Wg^T) * (x Wu^T)) Wd^T.
+ *
+ * x, y, dy, dx: bf16 [T][H] (row-major, token-major); w_gate, w_up: bf16
+ * [I][H]; w_down: bf16 [H][I]; dw_gate, dw_up: fp32 [I][H]; dw_down: fp32
+ * [H][I].  `tile` tokens per tile (the last tile may be shorter).  H and I
+ * must be multiples of 128; T >= 1, tile >= 1.  The forward rounds the gated
+ * activation to bf16 before the down projection; the backward recomputes
+ * each tile's projections from x, rounds them and the gated derivatives to
+ * bf16, accumulates the weight gradients in fp32 over the tiles and
+ * overwrites dw_* with the sums.  The caller owns all buffers (16-byte
+ * aligned), including `workspace` (ulysses_tiled_mlp_workspace_bytes; one
+ * tile's activations).  Errors: ULY_ERR_NULL, ULY_ERR_SHAPE (sizes),
+ * ULY_ERR_UNSUPPORTED (H or I not a multiple of 128), ULY_ERR_ALIGN,
+ * ULY_ERR_CAPACITY (workspace), ULY_ERR_HIP.
+ * ---------------------------------------------------------------------- */
+size_t ulysses_tiled_mlp_workspace_bytes(int T, int H, int I, int tile);
+int ulysses_tiled_mlp_fwd(const void* x, const void* w_gate, const void* w_up, const void* w_down,
+                          void* y, int T, int H, int I, int tile, void* workspace,
+                          size_t workspace_bytes, void* stream);
+int ulysses_tiled_mlp_bwd(const void* x, const void* w_gate, const void* w_up, const void* w_down,
+                          const void* dy, void* dx, float* dw_gate, float* dw_up, float* dw_down,
+                          int T, int H, int I, int tile, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 /* Bytes of device workspace ulysses_attn_fwd needs for these sizes: zero when
  * one pass of query tiles fills the GPU, else room for fp32 partial outputs of
  * the key-range splits that small problems are cut into (merged, with the

@@ -27,7 +27,7 @@ from typing import Tuple
 
 import torch
 
-__all__ = ["tiled_mlp_fwd", "tiled_mlp_bwd", "silu", "silu_grad"]
+__all__ = ["tiled_mlp_fwd", "tiled_mlp_bwd", "weight_grad_entries", "silu", "silu_grad"]
 
 
 def _f64(t: torch.Tensor) -> torch.Tensor:
@@ -95,3 +95,34 @@ def tiled_mlp_bwd(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, w_d
         dwu += du.T @ xt
         dwd += dyt.T @ h
     return dx, dwg, dwu, dwd
+
+
+def weight_grad_entries(x, w_gate, w_up, w_down, dy, gate_up_idx, down_idx):
+    """Selected weight-gradient entries, each the plain sum over all tokens.
+
+    gate_up_idx: (i, h) pairs -> (dWg[i][h], dWu[i][h]) with dWg[i][h] =
+    sum_t dG[t][i] x[t][h], dG[t][i] = (dy[t] . Wd[:, i]) U[t][i] silu'(G[t][i]),
+    and dWu likewise with dU = (dy[t] . Wd[:, i]) silu(G[t][i]).
+    down_idx: (h, i) pairs -> dWd[h][i] = sum_t dy[t][h] silu(G[t][i]) U[t][i].
+    Only the columns i involved are formed (one matvec over the tokens each).
+    """
+    x, wg, wu, wd, dy = _f64(x), _f64(w_gate), _f64(w_up), _f64(w_down), _f64(dy)
+    cols = {}
+
+    def col(i):
+        if i not in cols:
+            g = x @ wg[i]
+            u = x @ wu[i]
+            dh = dy @ wd[:, i]
+            cols[i] = (g, u, dh)
+        return cols[i]
+
+    gate, up, down = [], [], []
+    for i, h in gate_up_idx:
+        g, u, dh = col(i)
+        gate.append(float((dh * u * silu_grad(g)) @ x[:, h]))
+        up.append(float((dh * silu(g)) @ x[:, h]))
+    for h, i in down_idx:
+        g, u, _ = col(i)
+        down.append(float((silu(g) * u) @ dy[:, h]))
+    return gate, up, down

@@ -40,6 +40,8 @@ def test_header_declares_the_boundary():
                           "ulysses_attn_merge", "ulysses_attn_merge_finish",
                           "ulysses_attn_fwd_workspace_bytes",
                           "ulysses_attn_bwd_workspace_bytes", "ulysses_attn_bwd",
+                          "ulysses_tiled_mlp_workspace_bytes", "ulysses_tiled_mlp_fwd",
+                          "ulysses_tiled_mlp_bwd",
                           "ulysses_profile_start", "ulysses_profile_stop",
                           "ulysses_profile_report", "ulysses_last_error"}
 
@@ -214,3 +216,24 @@ def test_python_binding_rejects_host_tensors():
     q = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         uly.attn_fwd(q, q, q)
+
+
+def test_tiled_mlp_argument_errors(lib):
+    ws = lib.ulysses_tiled_mlp_workspace_bytes(200, 128, 256, 128)
+    assert ws >= 128 * 256 * 2 * 5
+    assert lib.ulysses_tiled_mlp_workspace_bytes(0, 128, 256, 128) == 0
+    fwd = lambda T, H, I, tile, x=A, y=A, ws_ptr=A, ws_bytes=ws: lib.ulysses_tiled_mlp_fwd(
+        _p(x), _p(A), _p(A), _p(A), _p(y), T, H, I, tile, _p(ws_ptr), ws_bytes, None)
+    assert fwd(200, 128, 256, 128, x=0) == NULL
+    assert fwd(200, 128, 256, 128, y=0) == NULL
+    assert fwd(0, 128, 256, 128) == SHAPE
+    assert fwd(200, 128, 256, 0) == SHAPE
+    assert fwd(200, 96, 256, 128) == UNSUP
+    assert fwd(200, 128, 200, 128) == UNSUP
+    assert fwd(200, 128, 256, 128, ws_ptr=0) == NULL
+    assert fwd(200, 128, 256, 128, ws_bytes=ws - 1) == CAP
+    assert fwd(200, 128, 256, 128, x=A + 2) == ALIGN
+    bwd = lambda dw=A: lib.ulysses_tiled_mlp_bwd(_p(A), _p(A), _p(A), _p(A), _p(A), _p(A), _p(dw),
+                                                 _p(A), _p(A), 200, 128, 256, 128, _p(A), ws, None)
+    assert bwd(dw=0) == NULL
+    assert bwd(dw=A + 4) == ALIGN

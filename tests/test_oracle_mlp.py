@@ -117,3 +117,18 @@ def test_zero_input_and_zero_down_weight():
     assert torch.count_nonzero(y) == 0 and torch.count_nonzero(dx) == 0
     assert torch.count_nonzero(dwg) == 0 and torch.count_nonzero(dwu) == 0
     assert torch.count_nonzero(dwd) > 0   # dWd = dy^T h does not depend on Wd
+
+
+def test_weight_grad_entries_match_the_full_backward():
+    """The one-entry-at-a-time sums (used at full size) equal the tiled backward's entries."""
+    T, H, I = 9, 5, 7
+    m = make_mlp_inputs(5, T, H, I)
+    _, dwg, dwu, dwd = om.tiled_mlp_bwd(m.x, m.w_gate, m.w_up, m.w_down, m.dy, tile=4)
+    gu = [(0, 0), (6, 4), (3, 2)]
+    dn = [(0, 0), (4, 6), (2, 3)]
+    g, u, d = om.weight_grad_entries(m.x, m.w_gate, m.w_up, m.w_down, m.dy, gu, dn)
+    for (i, h), a, b in zip(gu, g, u):
+        assert a == pytest.approx(float(dwg[i, h]), rel=1e-12, abs=1e-13)
+        assert b == pytest.approx(float(dwu[i, h]), rel=1e-12, abs=1e-13)
+    for (h, i), c in zip(dn, d):
+        assert c == pytest.approx(float(dwd[h, i]), rel=1e-12, abs=1e-13)

@@ -39,6 +39,7 @@ EXPORTS = ("ulysses_a2a_pack", "ulysses_a2a_unpack", "ulysses_a2a_pack_multi",
            "ulysses_attn_bwd_layout_f32kv", "ulysses_attn_fwd_chunk", "ulysses_attn_merge",
            "ulysses_attn_merge_finish",
            "ulysses_attn_fwd_workspace_bytes", "ulysses_attn_bwd_workspace_bytes", "ulysses_attn_bwd",
+           "ulysses_tiled_mlp_workspace_bytes", "ulysses_tiled_mlp_fwd", "ulysses_tiled_mlp_bwd",
            "ulysses_profile_start", "ulysses_profile_stop", "ulysses_profile_report",
            "ulysses_last_error")
 
@@ -82,6 +83,10 @@ def load():
     lib.ulysses_attn_bwd_workspace_bytes.argtypes = [i32] * 5
     lib.ulysses_attn_bwd_workspace_bytes.restype = sz
     lib.ulysses_attn_bwd.argtypes = [vp] * 14 + [sz] + [i32] * 5 + [f32] + [i32] * 3 + [vp]
+    lib.ulysses_tiled_mlp_workspace_bytes.argtypes = [i32] * 4
+    lib.ulysses_tiled_mlp_workspace_bytes.restype = sz
+    lib.ulysses_tiled_mlp_fwd.argtypes = [vp] * 5 + [i32] * 4 + [vp, sz, vp]
+    lib.ulysses_tiled_mlp_bwd.argtypes = [vp] * 9 + [i32] * 4 + [vp, sz, vp]
     lib.ulysses_profile_start.argtypes = [i32]
     lib.ulysses_profile_stop.argtypes = []
     lib.ulysses_profile_report.argtypes = [ctypes.c_char_p, sz]
@@ -446,3 +451,59 @@ def attn_bwd(q, k, v, out, dout, lse, *, sink=None, cu_seqlens=None, n_seqs=None
         ctypes.byref(lk), B, S, hq, hkv, D, float(softmax_scale), int(bool(causal)),
         int(window_left), int(window_right), _stream(q.device)), fn)
     return dq, dk, dv, (dsink if sink is not None else None)
+
+
+# ------------------------------------------------------------ tiled MLP
+
+def tiled_mlp_workspace_bytes(T: int, H: int, I: int, tile: int) -> int:
+    return int(load().ulysses_tiled_mlp_workspace_bytes(T, H, I, tile))
+
+
+def _mlp_shapes(x, w_gate, w_up, w_down):
+    for name, t in (("x", x), ("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _dev(t, name, torch.bfloat16)
+    T, H = x.shape
+    I = w_gate.shape[0]
+    if w_gate.shape != (I, H) or w_up.shape != (I, H) or w_down.shape != (H, I):
+        raise ValueError("tiled MLP: weights must be [I, H], [I, H], [H, I] for x [T, H]")
+    return T, H, I
+
+
+def tiled_mlp_fwd(x, w_gate, w_up, w_down, tile: int, *, y=None, workspace=None):
+    """y = (silu(x Wg^T) * (x Wu^T)) Wd^T over the tokens of x ``[T, H]`` in tiles
+    of ``tile`` tokens (bf16; weights ``[I, H]``, ``[I, H]``, ``[H, I]``)."""
+    T, H, I = _mlp_shapes(x, w_gate, w_up, w_down)
+    y = torch.empty_like(x) if y is None else y
+    _dev(y, "y", torch.bfloat16)
+    if workspace is None:
+        workspace = torch.empty(tiled_mlp_workspace_bytes(T, H, I, tile), dtype=torch.uint8,
+                                device=x.device)
+    _check(load().ulysses_tiled_mlp_fwd(_p(x), _p(w_gate), _p(w_up), _p(w_down), _p(y), T, H, I,
+                                        int(tile), _p(workspace), workspace.numel(),
+                                        _stream(x.device)), "ulysses_tiled_mlp_fwd")
+    return y
+
+
+def tiled_mlp_bwd(x, w_gate, w_up, w_down, dy, tile: int, *, dx=None, dw_gate=None, dw_up=None,
+                  dw_down=None, workspace=None):
+    """Backward of ``tiled_mlp_fwd`` for the loss ``sum(y * dy)``: each tile's
+    activations recomputed from x, weight gradients summed in fp32 over the
+    tiles.  Returns (dx bf16 ``[T, H]``, dw_gate, dw_up fp32 ``[I, H]``,
+    dw_down fp32 ``[H, I]``)."""
+    T, H, I = _mlp_shapes(x, w_gate, w_up, w_down)
+    _dev(dy, "dy", torch.bfloat16)
+    dev = x.device
+    dx = torch.empty_like(x) if dx is None else dx
+    dw_gate = torch.empty((I, H), dtype=torch.float32, device=dev) if dw_gate is None else dw_gate
+    dw_up = torch.empty((I, H), dtype=torch.float32, device=dev) if dw_up is None else dw_up
+    dw_down = torch.empty((H, I), dtype=torch.float32, device=dev) if dw_down is None else dw_down
+    _dev(dx, "dx", torch.bfloat16)
+    for name, t in (("dw_gate", dw_gate), ("dw_up", dw_up), ("dw_down", dw_down)):
+        _dev(t, name, torch.float32)
+    if workspace is None:
+        workspace = torch.empty(tiled_mlp_workspace_bytes(T, H, I, tile), dtype=torch.uint8, device=dev)
+    _check(load().ulysses_tiled_mlp_bwd(_p(x), _p(w_gate), _p(w_up), _p(w_down), _p(dy), _p(dx),
+                                        _p(dw_gate), _p(dw_up), _p(dw_down), T, H, I, int(tile),
+                                        _p(workspace), workspace.numel(), _stream(dev)),
+           "ulysses_tiled_mlp_bwd")
+    return dx, dw_gate, dw_up, dw_down

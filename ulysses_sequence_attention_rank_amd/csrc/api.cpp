@@ -1,6 +1,7 @@
 // C ABI of the per-rank Ulysses hot path: argument checks, workspace layout
 // and kernel dispatch.  Declared (with the meaning of every argument) in
 // include/ulysses.h.
+#include <algorithm>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -275,6 +276,63 @@ int ulysses_a2a_unpack(const void* head_shards, void* seq_shards, int P, int B, 
   return hip_status(uly::permute_launch(false, 1, &head_shards, &dst, &H, P, B, S, D, elem_bytes,
                                         (hipStream_t)stream),
                     "ulysses_a2a_unpack launch");
+}
+
+// ---- sequence-tiled MLP
+size_t ulysses_tiled_mlp_workspace_bytes(int T, int H, int I, int tile) {
+  if (T <= 0 || H <= 0 || I <= 0 || tile <= 0) return 0;
+  const size_t rows = (size_t)std::min(T, tile);
+  // one tile's G, U, h (each [rows][I]) and dG | dU ([rows][2I]), bf16
+  return align256(rows * I * 2 * 5);
+}
+
+static int check_mlp(const void* x, const void* wg, const void* wu, const void* wd, int T, int H,
+                     int I, int tile, void* ws, size_t ws_bytes) {
+  if (!x || !wg || !wu || !wd) return fail(ULY_ERR_NULL, "NULL x or weight");
+  if (T <= 0 || H <= 0 || I <= 0 || tile <= 0)
+    return fail(ULY_ERR_SHAPE, "sizes must be positive (T=%d H=%d I=%d tile=%d)", T, H, I, tile);
+  if (H % 128 || I % 128)
+    return fail(ULY_ERR_UNSUPPORTED, "H=%d and I=%d must be multiples of 128", H, I);
+  if ((int64_t)T * H >= kMaxI32 * 8ll || (int64_t)I * H >= kMaxI32 * 8ll || I >= (1 << 22))
+    return fail(ULY_ERR_SHAPE, "problem too large");
+  const size_t need = ulysses_tiled_mlp_workspace_bytes(T, H, I, tile);
+  if (!ws) return fail(ULY_ERR_NULL, "NULL workspace (%zu bytes needed)", need);
+  if (ws_bytes < need) return fail(ULY_ERR_CAPACITY, "workspace of %zu bytes < %zu needed", ws_bytes, need);
+  if (!aligned(x, 16) || !aligned(wg, 16) || !aligned(wu, 16) || !aligned(wd, 16) || !aligned(ws, 256))
+    return fail(ULY_ERR_ALIGN, "tensors need 16-byte alignment, workspace 256-byte");
+  return ok();
+}
+
+int ulysses_tiled_mlp_fwd(const void* x, const void* w_gate, const void* w_up, const void* w_down,
+                          void* y, int T, int H, int I, int tile, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  int rc = check_mlp(x, w_gate, w_up, w_down, T, H, I, tile, workspace, workspace_bytes);
+  if (rc) return rc;
+  if (!y) return fail(ULY_ERR_NULL, "NULL y");
+  if (!aligned(y, 16)) return fail(ULY_ERR_ALIGN, "y needs 16-byte alignment");
+  uly::MlpArgs p = {};
+  p.x = (const __bf16*)x, p.wg = (const __bf16*)w_gate, p.wu = (const __bf16*)w_up;
+  p.wd = (const __bf16*)w_down, p.y = (__bf16*)y, p.ws = workspace;
+  p.T = T, p.H = H, p.I = I, p.tile = std::min(T, tile);
+  return hip_status(uly::mlp_fwd_launch(p, (hipStream_t)stream), "ulysses_tiled_mlp_fwd launch");
+}
+
+int ulysses_tiled_mlp_bwd(const void* x, const void* w_gate, const void* w_up, const void* w_down,
+                          const void* dy, void* dx, float* dw_gate, float* dw_up, float* dw_down,
+                          int T, int H, int I, int tile, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  int rc = check_mlp(x, w_gate, w_up, w_down, T, H, I, tile, workspace, workspace_bytes);
+  if (rc) return rc;
+  if (!dy || !dx || !dw_gate || !dw_up || !dw_down) return fail(ULY_ERR_NULL, "NULL dy, dx or dw");
+  if (!aligned(dy, 16) || !aligned(dx, 16) || !aligned(dw_gate, 16) || !aligned(dw_up, 16) ||
+      !aligned(dw_down, 16))
+    return fail(ULY_ERR_ALIGN, "tensors need 16-byte alignment");
+  uly::MlpArgs p = {};
+  p.x = (const __bf16*)x, p.wg = (const __bf16*)w_gate, p.wu = (const __bf16*)w_up;
+  p.wd = (const __bf16*)w_down, p.dy = (const __bf16*)dy, p.dx = (__bf16*)dx;
+  p.dwg = dw_gate, p.dwu = dw_up, p.dwd = dw_down, p.ws = workspace;
+  p.T = T, p.H = H, p.I = I, p.tile = std::min(T, tile);
+  return hip_status(uly::mlp_bwd_launch(p, (hipStream_t)stream), "ulysses_tiled_mlp_bwd launch");
 }
 
 int check_replicated(const void* a, const void* b, int P, int B, int S, int H, int D, int eb) {

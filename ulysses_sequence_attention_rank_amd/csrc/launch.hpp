@@ -24,6 +24,19 @@ hipError_t attn_merge_finish_launch(const float* acc_o, const float* acc_lse, co
 hipError_t attn_bwd_launch(const AttnArgs& a, int D, hipStream_t st);
 void dkdv_launch(const AttnArgs& a, int D, hipStream_t st);  // part of attn_bwd_launch
 
+// The sequence-tiled gated MLP (mlp.hip): x, dy, y, dx [T][H]; gate and up
+// weights [I][H], down weight [H][I] (bf16); weight gradients fp32; ws holds
+// one tile's activations (mlp_workspace_bytes).
+struct MlpArgs {
+  const __bf16 *x, *wg, *wu, *wd, *dy;
+  __bf16 *y, *dx;
+  float *dwg, *dwu, *dwd;
+  void* ws;
+  int T, H, I, tile;
+};
+hipError_t mlp_fwd_launch(const MlpArgs& p, hipStream_t st);
+hipError_t mlp_bwd_launch(const MlpArgs& p, hipStream_t st);
+
 // Number of splits of a reduction dimension for a kernel whose natural grid
 // has `wgs` work-groups of which `per_round` are resident at once on MI355X
 // (256 CUs times the work-groups a CU holds): the split count (at most 4, at
