@@ -477,8 +477,6 @@ def _rocprof_name(full):
     """Short name of a kernel as rocprofv3 prints it, matching the names the
     library's per-kernel timer uses."""
     import re
-    if "to_f16_kernel" in full:
-        return "attn_bwd_f16"
     if "at::native" in full:
         return "torch (buffer fill)"
     m = re.search(r"uly::(\w+?)_kernel(<[^>]*>)?", full)
@@ -491,8 +489,10 @@ def _rocprof_name(full):
         return "cu_seqlens"
     if name in ("dq_reduce", "dkdv_reduce"):
         return "attn_bwd_" + name
-    if name == "to_f16":
-        return "attn_bwd_f16"
+    if name == "mlp_gemm":  # the tiled MLP's products, by operand layouts and epilogue
+        return {"<false, false, 1>": "mlp_gate_up", "<false, false, 0>": "mlp_down",
+                "<false, false, 2>": "mlp_bwd_gate_up", "<false, true, 3>": "mlp_bwd_gated",
+                "<false, true, 0>": "mlp_bwd_dx", "<true, true, 4>": "mlp_bwd_dw"}.get(targs, name)
     if name in ("dsink_partial", "dsink_final"):
         return "attn_bwd_" + name
     return name

@@ -1,6 +1,6 @@
 // Attention backward of one Ulysses rank.
 //
-//   delta_i = sum_d dO_i,d O_i,d                         (attn_bwd_pre)
+//   delta_i = sum_d dO_i,d O_i,d                         (attn_bwd_prep)
 //   P_ij = exp(s_ij - LSE_i), dP_ij = dO_i . v_j, dS_ij = P_ij (dP_ij - delta_i)
 //   dK_j = scale sum_i dS_ij q_i, dV_j = sum_i P_ij dO_i  (attn_bwd_dkdv: one
 //          work-group owns 32*NW keys of one KV head and walks every query of
@@ -27,11 +27,12 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 // ------------------------------------------------------------- delta, dsink
 
-// One 16-byte chunk of dO and O per thread, D/8 threads per (row, head).
+// One 16-byte chunk of dO and O per thread, D/8 threads per (row, head);
+// `block` plays the role of the block index.
 template <int D>
-__global__ __launch_bounds__(256) void attn_bwd_pre_kernel(AttnArgs a) {
+__device__ __forceinline__ void pre_block(const AttnArgs& a, int block) {
   constexpr int TPR = D / 8;  // threads per row
-  const int row = blockIdx.x * (256 / TPR) + threadIdx.x / TPR;  // row = t * hq + h
+  const int row = block * (256 / TPR) + threadIdx.x / TPR;  // row = t * hq + h
   const int c = threadIdx.x % TPR;
   float acc = 0.f;
   const bool valid = row < a.T * a.hq;
@@ -68,10 +69,9 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(AttnArgs a) {
 // keeps 11 significant bits, bf16 8); larger magnitudes saturate, values below
 // 2^-14 round to fp16's subnormals.  One 16-byte chunk per thread; hd8 = H*D/8.
 // Elements n .. n_pad - 1 (the kPad rows after the last token) are zero.
-__global__ __launch_bounds__(256) void to_f16_kernel(const __bf16* src, RowMap m, FastDiv hd8,
-                                                     FastDiv d8, _Float16* dst, int64_t n,
-                                                     int64_t n_pad) {
-  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+__device__ __forceinline__ void f16_block(const __bf16* src, const RowMap& m, FastDiv hd8, FastDiv d8,
+                                          _Float16* dst, int64_t n, int64_t n_pad, int block) {
+  const int64_t i = ((int64_t)block * 256 + threadIdx.x) * 8;
   if (i >= n && i < n_pad) {
     const u32x4 z = {0, 0, 0, 0};
     *reinterpret_cast<u32x4*>(dst + i) = z;
@@ -86,6 +86,35 @@ __global__ __launch_bounds__(256) void to_f16_kernel(const __bf16* src, RowMap m
     for (int w = 0; w < 4; ++w) h[w] = pack_f16x2(clamp_f16(bf16_lo(x[w])), clamp_f16(bf16_hi(x[w])));
     *reinterpret_cast<u32x4*>(dst + i) = h;
   }
+}
+
+// The backward's preparation in one launch: blocks [0, nb_pre) compute delta,
+// LSE*log2(e) and the fp16 dO (pre_block); the next ones make the fp16
+// copies of q, then k, then v (f16_block).
+struct PrepArgs {
+  int nb_pre, nb_q, nb_kv;
+  FastDiv d8, q8, k8;
+  int64_t nq, pq, nkv, pkv;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_prep_kernel(AttnArgs a, PrepArgs p) {
+  int b = blockIdx.x;
+  if (b < p.nb_pre) {
+    pre_block<D>(a, b);
+    return;
+  }
+  b -= p.nb_pre;
+  if (b < p.nb_q) {
+    f16_block(a.q, a.mq, p.q8, p.d8, a.q16, p.nq, p.pq, b);
+    return;
+  }
+  b -= p.nb_q;
+  if (b < p.nb_kv) {
+    f16_block(a.k, a.mk, p.k8, p.d8, a.k16, p.nkv, p.pkv, b);
+    return;
+  }
+  f16_block(a.v, a.mk, p.k8, p.d8, a.v16, p.nkv, p.pkv, b - p.nb_kv);
 }
 
 // Per head, n_part partial sums of -exp(sink - LSE_i) delta_i over the rows.
@@ -322,21 +351,21 @@ template <int D, int NW>
 static hipError_t launch_bwd_t(const AttnArgs& args, hipStream_t st) {
   AttnArgs a = args;
   {
+    ProfScope prof("attn_bwd_prep", st);
+    PrepArgs p;
     const int rows = (a.T + kPad) * a.hq, rpb = 256 / (D / 8);
-    ProfScope prof("attn_bwd_pre", st);
-    hipLaunchKernelGGL(attn_bwd_pre_kernel<D>, dim3((rows + rpb - 1) / rpb), dim3(256), 0, st, a);
-  }
-  {
-    ProfScope prof("attn_bwd_f16", st);
-    const int64_t nq = (int64_t)a.T * a.hq * D, nkv = (int64_t)a.T * a.hkv * D;
-    const FastDiv d8 = make_fastdiv(D / 8), q8 = make_fastdiv(a.hq * D / 8), k8 = make_fastdiv(a.hkv * D / 8);
-    const int64_t pq = nq + (int64_t)kPad * a.hq * D, pkv = nkv + (int64_t)kPad * a.hkv * D;
-    hipLaunchKernelGGL(to_f16_kernel, dim3((pq / 8 + 255) / 256), dim3(256), 0, st, a.q, a.mq, q8, d8,
-                       a.q16, nq, pq);
-    hipLaunchKernelGGL(to_f16_kernel, dim3((pkv / 8 + 255) / 256), dim3(256), 0, st, a.k, a.mk, k8, d8,
-                       a.k16, nkv, pkv);
-    hipLaunchKernelGGL(to_f16_kernel, dim3((pkv / 8 + 255) / 256), dim3(256), 0, st, a.v, a.mk, k8, d8,
-                       a.v16, nkv, pkv);
+    p.nq = (int64_t)a.T * a.hq * D;
+    p.nkv = (int64_t)a.T * a.hkv * D;
+    p.pq = p.nq + (int64_t)kPad * a.hq * D;
+    p.pkv = p.nkv + (int64_t)kPad * a.hkv * D;
+    p.d8 = make_fastdiv(D / 8);
+    p.q8 = make_fastdiv(a.hq * D / 8);
+    p.k8 = make_fastdiv(a.hkv * D / 8);
+    p.nb_pre = (rows + rpb - 1) / rpb;
+    p.nb_q = (int)((p.pq / 8 + 255) / 256);
+    p.nb_kv = (int)((p.pkv / 8 + 255) / 256);
+    hipLaunchKernelGGL(attn_bwd_prep_kernel<D>, dim3(p.nb_pre + p.nb_q + 2 * p.nb_kv), dim3(256), 0, st,
+                       a, p);
   }
   dkdv_launch(a, D, st);
   {
