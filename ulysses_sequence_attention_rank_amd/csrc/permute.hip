@@ -40,7 +40,7 @@ template <> struct VecT<2> { typedef unsigned short T; };
 template <> struct VecT<1> { typedef unsigned char T; };
 
 constexpr int kPermThreads = 256;
-constexpr int kPermUnroll = 4;
+constexpr int kPermUnroll = 1;  // one 16-byte chunk a thread: more waves in flight measured best
 
 // Source run of destination run `run` (pack direction):
 //   dst run (c, b, t) -> src run (r = t / Sl, b, s = t % Sl, c / rep)
