@@ -525,14 +525,22 @@ def rocprof_summary(d, workload):
     with open(os.path.join(d, "commands.txt")) as f:
         commands = [ln.rstrip() for ln in f if ln.strip()]
 
-    # scale factors: every thread of the pack kernel (16-byte vectors, 4 per
-    # thread, grids a whole number of blocks for these shapes) reads 64 bytes
-    # and writes 64, so a dispatch moves Grid_Size * 64 bytes each way
+    # scale factors: every thread of the pack kernel reads and writes
+    # kPermUnroll 16-byte vectors (grids are a whole number of blocks for
+    # these shapes), so a dispatch moves Grid_Size * 16 * kPermUnroll bytes
+    # each way; the constant is read from the kernel's source
+    import re
+    with open(os.path.join(ROOT, "ulysses_sequence_attention_rank_amd", "csrc", "permute.hip")) as f:
+        m = re.search(r"constexpr int kPermUnroll = (\d+);", f.read())
+    if m is None:
+        raise SystemExit("kPermUnroll not found in permute.hip")
+    pack_thread_bytes = 16 * int(m.group(1))
+
     def pack_scale(sub, counter):
         known = got = 0.0
         for r in rows(sub, "counter_collection.csv"):
             if _rocprof_name(r["Kernel_Name"]) == "a2a_pack" and r["Counter_Name"] == counter:
-                known += float(r["Grid_Size"]) * 64
+                known += float(r["Grid_Size"]) * pack_thread_bytes
                 got += float(r["Counter_Value"]) * 1024
         return known / got
     f_scale, w_scale = pack_scale("fetch", "FETCH_SIZE"), pack_scale("write", "WRITE_SIZE")
@@ -584,7 +592,7 @@ def rocprof_summary(d, workload):
             tail = (f"{t['fetch_kib']} | {t['write_kib']} | {t['bytes_per_launch'] / 1e6:.2f}"
                     if t else " | | ")
             f.write(f"| {k} | {vals} | {tail} |\n")
-        f.write(f"\nCounter scale (pack kernel, Grid_Size x 64 bytes read and written per "
+        f.write(f"\nCounter scale (pack kernel, Grid_Size x {pack_thread_bytes} bytes read and written per "
                 f"dispatch): FETCH_SIZE x {f_scale:.4f}, WRITE_SIZE x {w_scale:.4f}.\n")
     print(open(out).read())
 
