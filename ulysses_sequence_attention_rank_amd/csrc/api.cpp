@@ -156,7 +156,7 @@ size_t align256(size_t x);
 // the split sums of P dP.
 size_t split_part_bytes(int B, int S, int hq, int hkv, int D) {
   const size_t T = (size_t)B * S;
-  const int nq = uly::qtile_splits(B, S, hq, D), nk = uly::dkdv_splits(B, S, hkv, D);
+  const int nq = uly::qtile_splits(B, S, hq, D, true), nk = uly::dkdv_splits(B, S, hkv, D, true);
   size_t part = 0;
   if (nq > 1) part = (size_t)nq * T * hq * D * 4;
   if (nk > 1 && (size_t)nk * 2 * T * hkv * D * 4 > part) part = (size_t)nk * 2 * T * hkv * D * 4;
@@ -442,7 +442,7 @@ int ulysses_cu_seqlens_from_positions(const void* pos_shards, int pos_bytes, int
 // running max and sum of each split, fp32 [2][nsplit][B][hq][S].
 size_t ulysses_attn_fwd_workspace_bytes(int B, int S, int hq, int hkv, int D) {
   if (B <= 0 || S <= 0 || hq <= 0 || hkv <= 0 || (D != 64 && D != 128)) return 0;
-  const int ns = uly::fwd_splits(B, S, hq, uly::fwd_block_rows(B, S, hq, D), D);
+  const int ns = uly::fwd_splits(B, S, hq, uly::fwd_block_rows(B, S, hq, D), D, true);
   if (ns == 1) return 0;
   const size_t rows = (size_t)B * S * hq;
   return align256((size_t)ns * rows * D * 4) + align256(2 * (size_t)ns * rows * 4);
@@ -473,7 +473,8 @@ int ulysses_attn_fwd_layout(const void* q, const void* k, const void* v, void* o
   a.out = (__bf16*)out;
   a.lse = lse;
   if (need > 0) {
-    a.nsplit = uly::fwd_splits(B, S, hq, uly::fwd_block_rows(B, S, hq, D), D);
+    a.nsplit = uly::fwd_splits(B, S, hq, uly::fwd_block_rows(B, S, hq, D), D,
+                                uly::uneven_layer(a.causal, a.wl, a.wr));
     a.part = (float*)workspace;
     a.part_pdp = (float*)((char*)workspace + align256((size_t)a.nsplit * B * S * hq * D * 4));
   }
@@ -529,7 +530,8 @@ int ulysses_attn_fwd_chunk(const void* q, const void* k_chunk, const void* v_chu
   a.lse = lse;
   a.o_f32 = 1;
   if (need > 0) {
-    a.nsplit = uly::fwd_splits(B, S, hq, uly::fwd_block_rows(B, S, hq, D), D);
+    a.nsplit = uly::fwd_splits(B, S, hq, uly::fwd_block_rows(B, S, hq, D), D,
+                                uly::uneven_layer(a.causal, a.wl, a.wr));
     a.part = (float*)workspace;
     a.part_pdp = (float*)((char*)workspace + align256((size_t)a.nsplit * B * S * hq * D * 4));
   }
@@ -632,7 +634,7 @@ static int attn_bwd_impl(const void* q, const void* k, const void* v, const void
   a.v16 = (_Float16*)(h16 + 2 * qsz + kvsz);
   {
     const size_t T = (size_t)B * S;
-    const int nq = uly::qtile_splits(B, S, hq, D), nk = uly::dkdv_splits(B, S, hkv, D);
+    const int nq = uly::qtile_splits(B, S, hq, D, true), nk = uly::dkdv_splits(B, S, hkv, D, true);
     size_t part = 0;
     if (nq > 1) part = (size_t)nq * T * hq * D * 4;
     if (nk > 1 && (size_t)nk * 2 * T * hkv * D * 4 > part) part = (size_t)nk * 2 * T * hkv * D * 4;

@@ -373,7 +373,7 @@ static hipError_t launch_bwd_t(const AttnArgs& args, hipStream_t st) {
     b.n_tiles = (a.T + 32 * NW - 1) / (32 * NW);
     const int groups = b.n_tiles * a.hkv;
     const int blocks = ((groups + kXcds - 1) / kXcds) * kXcds * a.G;
-    b.nsplit = qtile_splits(a.B, a.S, a.hq, D);
+    b.nsplit = qtile_splits(a.B, a.S, a.hq, D, uneven_layer(a.causal, a.wl, a.wr));
     {
       ProfScope prof("attn_bwd_dq", st);
       hipLaunchKernelGGL((attn_bwd_dq_kernel<D, NW>), dim3(blocks, b.nsplit), dim3(NW * 64), 0, st, b);

@@ -257,7 +257,7 @@ template <int D, int NW>
 static void launch_dkdv_t(const AttnArgs& args, hipStream_t st) {
   AttnArgs b = args;
   b.n_tiles = (b.T + 32 * NW - 1) / (32 * NW);
-  b.nsplit = dkdv_splits(b.B, b.S, b.hkv, D);
+  b.nsplit = dkdv_splits(b.B, b.S, b.hkv, D, uneven_layer(b.causal, b.wl, b.wr));
   {
     ProfScope prof("attn_bwd_dkdv", st);
     const int items = b.n_tiles * b.hkv;

@@ -41,19 +41,22 @@ hipError_t mlp_bwd_launch(const MlpArgs& p, hipStream_t st);
 // has `wgs` work-groups of which `per_round` are resident at once on MI355X
 // (256 CUs times the work-groups a CU holds): the split count (at most 4, at
 // most one per 64-row tile) that minimises the rounds of resident work-groups
-// per unit of work, ceil(wgs * ns / per_round) / ns.  When the unsplit grid
-// fills at most two rounds, a split that only ties with it is still taken:
-// halving the work-groups evens out causal and variable-length work, which
-// the count of rounds does not see (measured, dK/dV with 2 splits instead of
-// 1: S=32768 packed 1.20 -> 1.01 ms, S=65536 window 8.8 -> 5.8 ms; on
-// S=131072, four rounds, it lost 4 %).  Among splits, ties go to
-// fewer.  Each split writes fp32 partials of `split_bytes` that a reduce reads
+// per unit of work, ceil(wgs * ns / per_round) / ns.  On an `uneven` layer
+// (causal or windowed), when the unsplit grid fills at most two rounds, a
+// split that only ties with it is still taken: halving the work-groups evens
+// out causal and variable-length work, which the count of rounds does not
+// see (measured, dK/dV with 2 splits instead of 1: S=32768 packed 1.20 ->
+// 1.01 ms, S=65536 window 8.8 -> 5.8 ms; on S=131072, four rounds, it lost
+// 4 %).  On a full layer the work-groups are even (packed documents aside,
+// which the host does not see) and a tie only adds the partials and their
+// reduce (dK/dV on the full S=4096 layer: 182 us with 2 splits, 160 with
+// none).  Among splits, ties go to fewer.  Each split writes fp32 partials of `split_bytes` that a reduce reads
 // back: two splits may write up to 256 MiB of them, more splits up to 64 MiB
 // (S=4096: dK/dV with 4 splits, 100 MB of partials, took 147 us with its
 // reduce, with 2 splits 142 us).  A function of the sizes only, so the
 // workspace query and the launch agree.
 constexpr double kSplitBytesCap2 = 256.0 * 1024 * 1024, kSplitBytesCapN = 64.0 * 1024 * 1024;
-inline int choose_splits(long wgs, long tiles, long per_round, double split_bytes) {
+inline int choose_splits(long wgs, long tiles, long per_round, double split_bytes, bool uneven) {
   if (wgs <= 0) return 1;
   int best = 1;
   const double t1 = (double)((wgs + per_round - 1) / per_round);
@@ -61,7 +64,7 @@ inline int choose_splits(long wgs, long tiles, long per_round, double split_byte
   for (long ns = 2; ns <= 4 && ns <= tiles; ++ns) {
     if (ns * split_bytes > (ns == 2 ? kSplitBytesCap2 : kSplitBytesCapN)) break;
     const double t = (double)((wgs * ns + per_round - 1) / per_round) / (double)ns;
-    if (t < best_t - 1e-9 || (best == 1 && t1 <= 2.0 && t <= best_t + 1e-9)) {
+    if (t < best_t - 1e-9 || (uneven && best == 1 && t1 <= 2.0 && t <= best_t + 1e-9)) {
       best_t = t;
       best = (int)ns;
     }
@@ -69,22 +72,26 @@ inline int choose_splits(long wgs, long tiles, long per_round, double split_byte
   return best;
 }
 // dK/dV: 128-key work-groups, one per CU (its LDS footprint); partials dK, dV
-inline int dkdv_splits(int B, int S, int hkv, int D) {
+inline int dkdv_splits(int B, int S, int hkv, int D, bool uneven) {
   const long T = (long)B * S;
-  return choose_splits(((T + 127) / 128) * hkv, (T + 63) / 64, 256, 8.0 * T * hkv * D);
+  return choose_splits(((T + 127) / 128) * hkv, (T + 63) / 64, 256, 8.0 * T * hkv * D, uneven);
 }
 // dQ: 128-query work-groups, two per CU; partials dQ and sum P dP
-inline int qtile_splits(int B, int S, int hq, int D) {
+inline int qtile_splits(int B, int S, int hq, int D, bool uneven) {
   const long T = (long)B * S;
-  return choose_splits(((T + 127) / 128) * hq, (T + 63) / 64, 512, 4.0 * T * hq * (D + 1));
+  return choose_splits(((T + 127) / 128) * hq, (T + 63) / 64, 512, 4.0 * T * hq * (D + 1), uneven);
 }
 
 // Forward: query tiles of `bm` rows, two work-groups per CU; partials O and
 // the running max and sum
-inline int fwd_splits(int B, int S, int hq, int bm, int D) {
+inline int fwd_splits(int B, int S, int hq, int bm, int D, bool uneven) {
   const long T = (long)B * S;
-  return choose_splits(((T + bm - 1) / bm) * hq, (T + 63) / 64, 512, 4.0 * T * hq * (D + 2));
+  return choose_splits(((T + bm - 1) / bm) * hq, (T + 63) / 64, 512, 4.0 * T * hq * (D + 2), uneven);
 }
+// A layer's work-groups are uneven when it is causal or windowed.  Split
+// counts never fall when `uneven` is set, so workspaces sized with it serve
+// every layer.
+inline bool uneven_layer(int causal, int wl, int wr) { return causal || wl >= 0 || wr >= 0; }
 // Rows of a forward query tile for head dim D (the launcher's variant choice).
 inline int fwd_block_rows(int B, int S, int hq, int D) {
   if (D == 128) return 128;
