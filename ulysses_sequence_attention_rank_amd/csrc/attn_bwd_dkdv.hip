@@ -33,9 +33,10 @@ struct DkdvSmem {
 
 template <int D, int NW>
 __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, const char* buf, const char* kvs,
+                                          SwzOffsets<D>& so, int (&kvo)[D / 16],
                                           f32x16 (&dkacc)[D / 32], f32x16 (&dvacc)[D / 32],
                                           int qa, int full_lo, int full_hi, int qlo, int qhi,
-                                          int wave, int lane) {
+                                          int lane) {
   typedef DkdvSmem<D, NW> SM;
   constexpr int NB = D / 32, KS = D / 16;
   const int hf = lane >> 5;
@@ -46,19 +47,29 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, const char* buf, co
   const char* vs = kvs + SM::kKV;
   const f32x16 zero = {};
 
-  // visible queries of this lane's key; a fully visible tile opens the interval
+  // visible queries of this lane's key, as offsets from the first row this
+  // lane holds (row 8 i + 4 hf + j of a 32-query block holds value 4 i + j),
+  // so each test compares with a constant; a fully visible tile opens them
   const bool full = qa >= full_lo && qa + kBK <= full_hi;
-  const int mlo = full ? INT_MIN : qlo - qa, mhi = full ? INT_MAX : qhi - qa;
+  const int mlo = full ? -(1 << 30) : qlo - qa - 4 * hf, mhi = full ? (1 << 30) : qhi - qa - 4 * hf;
+
+  // per-lane read offsets, opaque here so that each read forms its address
+  // from them (plus an immediate) instead of the compiler keeping one
+  // register per distinct address across the loop
+  so.refresh();
+#pragma unroll
+  for (int s = 0; s < KS; ++s) asm volatile("" : "+v"(kvo[s]));
+  auto kv_at = [&](const char* base, int s) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + kvo[s]));
+  };
 
   f32x16 sacc[2], dpacc[2];
   bf16x8 pf[2][2], df[2][2];
   auto sdp = [&](int qb) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      sacc[qb] = mfma32h(swz_nat<D>(qs, 32 * qb, s, lane), swz_nat<D>(ks, 32 * wave, s, lane),
-                         s == 0 ? zero : sacc[qb]);
-      dpacc[qb] = mfma32h(swz_nat<D>(dos, 32 * qb, s, lane), swz_nat<D>(vs, 32 * wave, s, lane),
-                          s == 0 ? zero : dpacc[qb]);
+      sacc[qb] = mfma32h(so.nat_at(qs, 32 * qb, s), kv_at(ks, s), s == 0 ? zero : sacc[qb]);
+      dpacc[qb] = mfma32h(so.nat_at(dos, 32 * qb, s), kv_at(vs, s), s == 0 ? zero : dpacc[qb]);
     }
   };
   auto softmax = [&](int qb) {
@@ -70,7 +81,8 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, const char* buf, co
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][4 * i + j], a.scale_log2, -l4[j]));
-        p = (r0 + j >= mlo && r0 + j < mhi) ? p : 0.f;
+        const int rc = 32 * qb + 8 * i + j;
+        p = (rc >= mlo && rc < mhi) ? p : 0.f;
         sacc[qb][4 * i + j] = p;
         dpacc[qb][4 * i + j] = p * (dpacc[qb][4 * i + j] - d4[j]);
       }
@@ -87,8 +99,8 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, const char* buf, co
     for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        dvacc[nb] = mfma32h(pf[qb][ii], swz_tr<D>(dos, 32 * qb + 16 * ii, 32 * nb, lane), dvacc[nb]);
-        dkacc[nb] = mfma32h(df[qb][ii], swz_tr<D>(qs, 32 * qb + 16 * ii, 32 * nb, lane), dkacc[nb]);
+        dvacc[nb] = mfma32h(pf[qb][ii], so.tr_at(dos, 32 * qb + 16 * ii, nb), dvacc[nb]);
+        dkacc[nb] = mfma32h(df[qb][ii], so.tr_at(qs, 32 * qb + 16 * ii, nb), dkacc[nb]);
       }
   };
   // two 32-query blocks in a software pipeline (block 1's products are
@@ -125,7 +137,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(AttnArgs a) {
     kt = L / a.hkv;
     g = L - kt * a.hkv;
   }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hf = lane >> 5;
+  const int lane = threadIdx.x & 63, hf = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int k0 = kt * BN;
   const int krow = k0 + 32 * wave + (lane & 31);
   const bool kvalid = krow < a.T;
@@ -172,8 +185,13 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(AttnArgs a) {
     }
     return qa;
   };
+  // LDS read offsets: swizzled rows of a stage tile, and this wave's K/V rows
+  SwzOffsets<D> so(lane);
+  int kvo[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) kvo[s] = 32 * wave * 2 * D + so.nat[s];
   auto compute = [&](const char* buf, int qa) {
-    dkdv_tile<D, NW>(a, buf, kvs, dkacc, dvacc, qa, full_lo, full_hi, qlo, qhi, wave, lane);
+    dkdv_tile<D, NW>(a, buf, kvs, so, kvo, dkacc, dvacc, qa, full_lo, full_hi, qlo, qhi, lane);
   };
 
   // this split's share of the (head, query tile) iterations
@@ -201,29 +219,36 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(AttnArgs a) {
   const int64_t plane = (int64_t)a.T * a.hkv * D;
   float* pk = a.part + blockIdx.y * plane;
   float* pv = a.part + (a.nsplit + blockIdx.y) * plane;
+  // one row offset per key, shared by the NB column blocks
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
+  for (int e = 0; e < 16; ++e) {
+    const int key = k0 + 32 * wave + 8 * (e >> 2) + 4 * hf + (e & 3);
+    if (key >= a.T) continue;
+    const int col = lane & 31;
+    if (a.nsplit > 1) {
+      const int64_t off = ((int64_t)key * a.hkv + g) * D + col;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int key = k0 + 32 * wave + 8 * (e >> 2) + 4 * hf + (e & 3);
-      if (key < a.T) {
-        const int col = 32 * nb + (lane & 31);
-        if (a.nsplit == 1) {
-          const int64_t off = row_of(a.mk, key) + (int64_t)g * a.mk.head + col;
-          if (a.dkv_f32) {
-            reinterpret_cast<float*>(a.dk)[off] = dkacc[nb][e] * a.scale;
-            reinterpret_cast<float*>(a.dv)[off] = dvacc[nb][e];
-          } else {
-            a.dk[off] = (__bf16)(dkacc[nb][e] * a.scale);
-            a.dv[off] = (__bf16)dvacc[nb][e];
-          }
-        } else {
-          const int64_t off = ((int64_t)key * a.hkv + g) * D + col;
-          pk[off] = dkacc[nb][e];
-          pv[off] = dvacc[nb][e];
-        }
+      for (int nb = 0; nb < NB; ++nb) {
+        pk[off + 32 * nb] = dkacc[nb][e];
+        pv[off + 32 * nb] = dvacc[nb][e];
+      }
+      continue;
+    }
+    const int64_t off = row_of(a.mk, key) + (int64_t)g * a.mk.head + col;
+    if (a.dkv_f32) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        reinterpret_cast<float*>(a.dk)[off + 32 * nb] = dkacc[nb][e] * a.scale;
+        reinterpret_cast<float*>(a.dv)[off + 32 * nb] = dvacc[nb][e];
+      }
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        a.dk[off + 32 * nb] = (__bf16)(dkacc[nb][e] * a.scale);
+        a.dv[off + 32 * nb] = (__bf16)dvacc[nb][e];
       }
     }
+  }
 }
 
 // dK = scale * sum of the split partials, dV = sum (fixed order), to bf16
