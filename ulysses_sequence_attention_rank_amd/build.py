@@ -27,9 +27,8 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
          "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
-# Per-file scheduler choice: the dK/dV kernel runs one wave per SIMD and needs
-# the ILP-oriented strategy to issue LDS operand reads ahead of the products.
-EXTRA = {"attn_bwd_dkdv.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
+# Per-file extra flags (none at present).
+EXTRA: dict = {}
 
 
 def _compile(src: str) -> str:

@@ -1,8 +1,5 @@
 // Attention backward of one Ulysses rank: the key-stationary dK/dV kernel.
-// (The delta pre-pass, the dQ kernel and dsink are in attn_bwd.hip; this file
-// is compiled with an ILP-oriented machine scheduler: at one wave per SIMD the
-// kernel must hide LDS latency inside the wave, by issuing operand reads well
-// ahead of their products.)
+// (The delta pre-pass, the dQ kernel and dsink are in attn_bwd.hip.)
 #include <climits>
 
 #include "attn_common.hpp"
@@ -13,45 +10,56 @@ namespace uly {
 // ------------------------------------------------------------------ dK, dV
 //
 // Products in fp16 on the fp16 copies the pre-pass makes (see attn_bwd.hip).
-// One work-group = NW waves x 32 keys of one KV head.  The work-group's K and
-// V rows are staged once in LDS (swizzled natural tiles) and read as B
-// operands when needed, which leaves registers for the dK/dV accumulators and
-// for operand prefetch.  The work-group walks every query tile (64 rows) of
-// every query head of the group: Q and dO tiles plus their LSE*log2(e) and
-// delta rows arrive by global_load_lds, double-buffered in two distinct LDS
-// arrays (the loop is unrolled by two, so reads of one stage are provably
-// disjoint from the loads into the other), and each tile serves both the
-// natural operand (S = Q K^T, dP = dO V^T) and, through the transposing
-// reads, the operand of dV += P^T dO and dK += dS^T Q.
+// One work-group = KG key groups of 32 keys of one KV head, two waves per
+// group (2 KG waves, two per SIMD).  The work-group's K and V rows are staged
+// once in LDS (swizzled natural tiles) and read as B operands when needed.
+// The work-group walks every query tile (64 rows) of every query head of the
+// group: Q and dO tiles plus their LSE*log2(e) and delta rows arrive by
+// global_load_lds, double-buffered in two distinct LDS arrays (the loop is
+// unrolled by two, so reads of one stage are provably disjoint from the loads
+// into the other).  Of each tile, the two waves of a key group take one
+// 32-query block each (S = Q K^T, dP = dO V^T from the natural operands, then
+// dV += P^T dO and dK += dS^T Q through the transposing reads), so a SIMD
+// runs two independent waves whose products and softmax overlap.  Each wave
+// accumulates its block's share of its keys' dK and dV; the two shares are
+// added once, through LDS, after the last tile.
 
-template <int D, int NW>
+template <int D, int KG>
 struct DkdvSmem {
   static constexpr int kTile = kBK * D * 2;
   static constexpr int kStage = 2 * kTile + 2 * kBK * 4;  // Q, dO, LSE*log2e, delta
-  static constexpr int kKV = 32 * NW * D * 2;              // K or V rows of the work-group
+  static constexpr int kKV = 32 * KG * D * 2;              // K or V rows of the work-group
+  // the second block's dK (in the K/V area) and dV (half the key groups in
+  // each stage) for the final sum
+  static constexpr int kRed = (D / 32) * 16 * 64 * 4;      // one wave's dK or dV, fp32
+  static_assert(KG * kRed <= 2 * kKV && (KG / 2) * kRed <= kStage, "final sum fits the LDS arrays");
 };
 
-template <int D, int NW>
+// One 32-query block of a staged tile for this wave's 32 keys.  `so` holds
+// the per-lane read offsets of the wave's block rows in a stage tile, `kvo`
+// those of its key rows in the K/V area.
+template <int D, int KG>
 __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, const char* buf, const char* kvs,
                                           SwzOffsets<D>& so, int (&kvo)[D / 16],
                                           f32x16 (&dkacc)[D / 32], f32x16 (&dvacc)[D / 32],
-                                          int qa, int full_lo, int full_hi, int qlo, int qhi,
+                                          int qa, int qb, int full_lo, int full_hi, int qlo, int qhi,
                                           int lane) {
-  typedef DkdvSmem<D, NW> SM;
+  typedef DkdvSmem<D, KG> SM;
   constexpr int NB = D / 32, KS = D / 16;
   const int hf = lane >> 5;
   const char* qs = buf;
   const char* dos = buf + SM::kTile;
-  const float* lsd = reinterpret_cast<const float*>(buf + 2 * SM::kTile);
+  const float* lsw = reinterpret_cast<const float*>(buf + 2 * SM::kTile) + 32 * qb + 4 * hf;
   const char* ks = kvs;
   const char* vs = kvs + SM::kKV;
   const f32x16 zero = {};
 
   // visible queries of this lane's key, as offsets from the first row this
-  // lane holds (row 8 i + 4 hf + j of a 32-query block holds value 4 i + j),
-  // so each test compares with a constant; a fully visible tile opens them
+  // lane holds (row 8 i + 4 hf + j of the block holds value 4 i + j), so each
+  // test compares with a constant; a fully visible tile opens them
   const bool full = qa >= full_lo && qa + kBK <= full_hi;
-  const int mlo = full ? -(1 << 30) : qlo - qa - 4 * hf, mhi = full ? (1 << 30) : qhi - qa - 4 * hf;
+  const int rel = qa + 32 * qb + 4 * hf;
+  const int mlo = full ? -(1 << 30) : qlo - rel, mhi = full ? (1 << 30) : qhi - rel;
 
   // per-lane read offsets, opaque here so that each read forms its address
   // from them (plus an immediate) instead of the compiler keeping one
@@ -63,61 +71,46 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, const char* buf, co
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + kvo[s]));
   };
 
-  f32x16 sacc[2], dpacc[2];
-  bf16x8 pf[2][2], df[2][2];
-  auto sdp = [&](int qb) {
+  f32x16 sacc, dpacc;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      sacc[qb] = mfma32h(so.nat_at(qs, 32 * qb, s), kv_at(ks, s), s == 0 ? zero : sacc[qb]);
-      dpacc[qb] = mfma32h(so.nat_at(dos, 32 * qb, s), kv_at(vs, s), s == 0 ? zero : dpacc[qb]);
+  for (int s = 0; s < KS; ++s) {
+    sacc = mfma32h(so.nat_at(qs, 0, s), kv_at(ks, s), s == 0 ? zero : sacc);
+    dpacc = mfma32h(so.nat_at(dos, 0, s), kv_at(vs, s), s == 0 ? zero : dpacc);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x4 l4 = *reinterpret_cast<const f32x4*>(lsw + 8 * i);
+    const f32x4 d4 = *reinterpret_cast<const f32x4*>(lsw + kBK + 8 * i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * i + j], a.scale_log2, -l4[j]));
+      const int rc = 8 * i + j;
+      p = (rc >= mlo && rc < mhi) ? p : 0.f;
+      sacc[4 * i + j] = p;
+      dpacc[4 * i + j] = p * (dpacc[4 * i + j] - d4[j]);
     }
-  };
-  auto softmax = [&](int qb) {
+  }
+  bf16x8 pf[2], df[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r0 = 32 * qb + 8 * i + 4 * hf;
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(lsd + r0);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(lsd + kBK + r0);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][4 * i + j], a.scale_log2, -l4[j]));
-        const int rc = 32 * qb + 8 * i + j;
-        p = (rc >= mlo && rc < mhi) ? p : 0.f;
-        sacc[qb][4 * i + j] = p;
-        dpacc[qb][4 * i + j] = p * (dpacc[qb][4 * i + j] - d4[j]);
-      }
-    }
-#pragma unroll
-    for (int ii = 0; ii < 2; ++ii) {
-      pf[qb][ii] = acc_frag_h(sacc[qb], ii);
-      df[qb][ii] = acc_frag_h(dpacc[qb], ii);
-    }
-  };
+  for (int ii = 0; ii < 2; ++ii) {
+    pf[ii] = acc_frag_h(sacc, ii);
+    df[ii] = acc_frag_h(dpacc, ii);
+  }
   // dV += P^T dO, dK += dS^T Q (contraction over the block's 32 queries)
-  auto dvdk = [&](int qb) {
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii)
+  for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        dvacc[nb] = mfma32h(pf[qb][ii], so.tr_at(dos, 32 * qb + 16 * ii, nb), dvacc[nb]);
-        dkacc[nb] = mfma32h(df[qb][ii], so.tr_at(qs, 32 * qb + 16 * ii, nb), dkacc[nb]);
-      }
-  };
-  // two 32-query blocks in a software pipeline (block 1's products are
-  // independent of block 0's softmax, block 0's dV/dK of block 1's softmax)
-  sdp(0);
-  softmax(0);
-  sdp(1);
-  dvdk(0);
-  softmax(1);
-  dvdk(1);
+    for (int nb = 0; nb < NB; ++nb) {
+      dvacc[nb] = mfma32h(pf[ii], so.tr_at(dos, 16 * ii, nb), dvacc[nb]);
+      dkacc[nb] = mfma32h(df[ii], so.tr_at(qs, 16 * ii, nb), dkacc[nb]);
+    }
 }
 
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(AttnArgs a) {
+template <int D, int KG>
+__global__ __launch_bounds__(KG * 128) void attn_bwd_dkdv_kernel(AttnArgs a) {
+  constexpr int NW = 2 * KG, BN = 32 * KG, NB = D / 32;
   static_assert(NW >= 2, "two waves stage the per-row statistics");
-  typedef DkdvSmem<D, NW> SM;
-  constexpr int BN = 32 * NW, NB = D / 32;
+  typedef DkdvSmem<D, KG> SM;
   __shared__ __attribute__((aligned(1024))) char kvs[2 * SM::kKV];
   __shared__ __attribute__((aligned(1024))) char st0[SM::kStage];
   __shared__ __attribute__((aligned(1024))) char st1[SM::kStage];
@@ -139,8 +132,9 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(AttnArgs a) {
   }
   const int lane = threadIdx.x & 63, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kg = wave % KG, qb = wave / KG;  // key group, query block
   const int k0 = kt * BN;
-  const int krow = k0 + 32 * wave + (lane & 31);
+  const int krow = k0 + 32 * kg + (lane & 31);
   const bool kvalid = krow < a.T;
 
   int qlo = 0, qhi = 0;
@@ -185,13 +179,22 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(AttnArgs a) {
     }
     return qa;
   };
-  // LDS read offsets: swizzled rows of a stage tile, and this wave's K/V rows
+  // LDS read offsets: this wave's key rows in the K/V area, and its block's
+  // swizzled rows of a stage tile (the swizzle repeats every 16 rows)
   SwzOffsets<D> so(lane);
   int kvo[D / 16];
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) kvo[s] = 32 * wave * 2 * D + so.nat[s];
+  for (int s = 0; s < D / 16; ++s) {
+    kvo[s] = 32 * kg * 2 * D + so.nat[s];
+    so.nat[s] += 32 * qb * 2 * D;
+  }
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb) {
+    so.tr[nb][0] += 32 * qb * 2 * D;
+    so.tr[nb][1] += 32 * qb * 2 * D;
+  }
   auto compute = [&](const char* buf, int qa) {
-    dkdv_tile<D, NW>(a, buf, kvs, so, kvo, dkacc, dvacc, qa, full_lo, full_hi, qlo, qhi, lane);
+    dkdv_tile<D, KG>(a, buf, kvs, so, kvo, dkacc, dvacc, qa, qb, full_lo, full_hi, qlo, qhi, lane);
   };
 
   // this split's share of the (head, query tile) iterations
@@ -215,6 +218,31 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(AttnArgs a) {
     }
   }
 
+  // the second block's shares join the first's: one lane-major fp32 slot per
+  // (key group, column block, value); dK in the K/V area, dV in the stages
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();  // every wave is past its last tile's reads
+  float* red_k = reinterpret_cast<float*>(kvs) + kg * (SM::kRed / 4);
+  float* red_v = reinterpret_cast<float*>(kg < KG / 2 ? st0 : st1) + (kg % (KG / 2)) * (SM::kRed / 4);
+  if (qb == 1) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        red_k[(nb * 16 + e) * 64 + lane] = dkacc[nb][e];
+        red_v[(nb * 16 + e) * 64 + lane] = dvacc[nb][e];
+      }
+  }
+  __syncthreads();
+  if (qb == 1) return;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      dkacc[nb][e] += red_k[(nb * 16 + e) * 64 + lane];
+      dvacc[nb][e] += red_v[(nb * 16 + e) * 64 + lane];
+    }
+
   // dK, dV: lane holds column d = 32 nb + l % 32 of key rows 8 i + 4 hf + j
   const int64_t plane = (int64_t)a.T * a.hkv * D;
   float* pk = a.part + blockIdx.y * plane;
@@ -222,7 +250,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(AttnArgs a) {
   // one row offset per key, shared by the NB column blocks
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    const int key = k0 + 32 * wave + 8 * (e >> 2) + 4 * hf + (e & 3);
+    const int key = k0 + 32 * kg + 8 * (e >> 2) + 4 * hf + (e & 3);
     if (key >= a.T) continue;
     const int col = lane & 31;
     if (a.nsplit > 1) {
@@ -278,16 +306,16 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(AttnArgs a, int64_t n)
   *reinterpret_cast<u32x2*>(a.dv + off) = wv;
 }
 
-template <int D, int NW>
+template <int D, int KG>
 static void launch_dkdv_t(const AttnArgs& args, hipStream_t st) {
   AttnArgs b = args;
-  b.n_tiles = (b.T + 32 * NW - 1) / (32 * NW);
+  b.n_tiles = (b.T + 32 * KG - 1) / (32 * KG);
   b.nsplit = dkdv_splits(b.B, b.S, b.hkv, D, uneven_layer(b.causal, b.wl, b.wr));
   {
     ProfScope prof("attn_bwd_dkdv", st);
     const int items = b.n_tiles * b.hkv;
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, NW>), dim3((items + kXcds - 1) / kXcds * kXcds, b.nsplit),
-                       dim3(NW * 64),
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, KG>), dim3((items + kXcds - 1) / kXcds * kXcds, b.nsplit),
+                       dim3(KG * 128),
                        0, st, b);
   }
   if (b.nsplit > 1) {
