@@ -80,3 +80,45 @@ def test_replicated_pack_and_gradient_sum_bit_exact(row):
             uly.a2a_reduce_replicated_into(grads.to(dev), out, P)
             torch.cuda.synchronize()
             assert bits_equal(out, oracle.reduce_replicated(grads, H))
+
+
+# id, P, B, S, kind of positions, dtype
+SEG_CASES = [
+    ("every_token_starts", 2, 1, 96, "zeros", torch.int64),      # n = B*S documents of length 1
+    ("one_doc", 4, 1, 4096, "arange", torch.int32),
+    ("b3_ragged_chunks", 3, 3, 2997, "docs", torch.int64),      # T not a multiple of the threads
+    ("long_chunks_int32", 4, 1, 262144, "docs", torch.int32),   # 256 tokens a thread: many batches
+    ("dense_restarts", 2, 2, 20000, "dense", torch.int64),
+]
+
+
+def _positions(kind, B, S, g):
+    if kind == "zeros":
+        return torch.zeros(B, S, dtype=torch.int64)
+    if kind == "arange":
+        return torch.arange(S, dtype=torch.int64).repeat(B, 1)
+    hi = 40 if kind == "dense" else 5000
+    rows = []
+    for _ in range(B):
+        row, t = [], 0
+        while t < S:
+            n = min(int(torch.randint(1, hi, (1,), generator=g)), S - t)
+            row.append(torch.arange(n, dtype=torch.int64))
+            t += n
+        rows.append(torch.cat(row))
+    return torch.stack(rows)
+
+
+@pytest.mark.parametrize("row", SEG_CASES, ids=[c[0] for c in SEG_CASES])
+def test_cu_seqlens_edge_cases_bit_exact(row):
+    import ulysses_sequence_attention_rank_amd as uly
+    name, P, B, S, kind, dtype = row
+    say(f"cu_seqlens {name}: P={P} B={B} S={S} {kind} {dtype}")
+    g = torch.Generator().manual_seed(zlib.crc32(name.encode()))
+    pos = _positions(kind, B, S, g)
+    shards = pos.reshape(B, P, S // P).permute(1, 0, 2).contiguous().to(dtype)
+    want_cu, want_n, want_mx = oracle.segments(oracle.gather_positions(shards))
+    cu, n, mx = uly.cu_seqlens_from_positions(shards.cuda())
+    torch.cuda.synchronize()
+    assert int(n.item()) == want_n and int(mx.item()) == want_mx
+    assert torch.equal(cu[: want_n + 1].cpu(), want_cu)

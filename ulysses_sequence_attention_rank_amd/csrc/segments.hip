@@ -7,13 +7,17 @@
 // starts, an exclusive scan over the work-group gives each chunk its first
 // output slot, and the chunk writes its starts.  The length of a chunk's last
 // document needs the first start of a later chunk, found with a suffix
-// minimum; max_len is a work-group maximum.
+// minimum; max_len is a work-group maximum.  A thread reads its chunk kBatch
+// tokens at a time (the loads of a batch are in flight together); the scans
+// run within each wave by lane shuffles, then over the waves' totals.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace uly {
 
 constexpr int kSegThreads = 1024;
+constexpr int kSegWaves = kSegThreads / 64;
+constexpr int kBatch = 8;
 
 struct SegArgs {
   const void* pos;
@@ -35,57 +39,76 @@ __device__ __forceinline__ bool is_start(const SegArgs& a, u32 t) {
   return p[((uint64_t)r * a.B + b) * a.Sl.d + s] == 0;
 }
 
+// f(t) for every start t of [lo, hi), in order
+template <typename PosT, typename F>
+__device__ __forceinline__ void for_starts(const SegArgs& a, u32 lo, u32 hi, F f) {
+  for (u32 t0 = lo; t0 < hi; t0 += kBatch) {
+    bool st[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) st[k] = t0 + k < hi && is_start<PosT>(a, t0 + k);
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k)
+      if (st[k]) f(t0 + k);
+  }
+}
+
 template <typename PosT>
 __global__ __launch_bounds__(kSegThreads) void segments_kernel(SegArgs a) {
-  __shared__ int32_t s_cnt[kSegThreads];
-  __shared__ int32_t s_first[kSegThreads];
-  __shared__ int32_t s_max[kSegThreads];
-  const int tid = threadIdx.x;
+  __shared__ int32_t s_sum[kSegWaves], s_min[kSegWaves], s_max[kSegWaves];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const u32 lo = min(a.T, (u32)tid * a.chunk), hi = min(a.T, lo + a.chunk);
+  constexpr int32_t kNone = 0x7fffffff;
 
-  // pass 1: count starts, remember the first and last one
-  int32_t cnt = 0, first = 0x7fffffff, last = -1, best = 0;
-  for (u32 t = lo; t < hi; ++t) {
-    if (is_start<PosT>(a, t)) {
-      if (last >= 0) best = max(best, (int32_t)t - last);
-      if (first == 0x7fffffff) first = (int32_t)t;
-      last = (int32_t)t;
-      ++cnt;
-    }
+  // pass 1: count starts, remember the first and last one and the longest
+  // document that ends inside the chunk
+  int32_t cnt = 0, first = kNone, last = -1, best = 0;
+  for_starts<PosT>(a, lo, hi, [&](u32 t) {
+    if (last >= 0) best = max(best, (int32_t)t - last);
+    if (first == kNone) first = (int32_t)t;
+    last = (int32_t)t;
+    ++cnt;
+  });
+
+  // inclusive prefix sum of the counts and suffix minimum of the first
+  // starts, within the wave
+  int32_t x = cnt, f = first;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t y = __shfl_up(x, off, 64);
+    const int32_t z = __shfl_down(f, off, 64);
+    if (lane >= off) x += y;
+    if (lane + off < 64) f = min(f, z);
   }
-  s_cnt[tid] = cnt;
-  s_first[tid] = first;
+  if (lane == 63) s_sum[w] = x;
+  if (lane == 0) s_min[w] = f;
   __syncthreads();
-  // exclusive scan of the counts and suffix minimum of the first starts
-  // (Hillis-Steele over the work-group, log2(1024) rounds)
-  for (int off = 1; off < kSegThreads; off <<= 1) {
-    const int32_t c = tid >= off ? s_cnt[tid - off] : 0;
-    const int32_t f = tid + off < kSegThreads ? s_first[tid + off] : 0x7fffffff;
-    __syncthreads();
-    s_cnt[tid] += c;
-    s_first[tid] = min(s_first[tid], f);
-    __syncthreads();
+  int32_t before = 0, after = kNone;  // counts of earlier waves, first start of later ones
+  for (int i = 0; i < kSegWaves; ++i) {
+    if (i < w) before += s_sum[i];
+    if (i > w) after = min(after, s_min[i]);
   }
-  const int32_t incl = s_cnt[tid];
-  const int32_t next = tid + 1 < kSegThreads ? s_first[tid + 1] : 0x7fffffff;
-  const int32_t next_start = next == 0x7fffffff ? (int32_t)a.T : next;
-  if (last >= 0) best = max(best, next_start - last);
-  s_max[tid] = best;
+  const int32_t incl = x + before;
+  int32_t next = __shfl_down(f, 1, 64);  // first start after this chunk
+  if (lane == 63) next = kNone;
+  next = min(next, after);
+  if (last >= 0) best = max(best, (next == kNone ? (int32_t)a.T : next) - last);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) best = max(best, __shfl_xor(best, off, 64));
+  if (lane == 0) s_max[w] = best;
 
   // pass 2: write the starts of this chunk
   int32_t slot = incl - cnt;
-  for (u32 t = lo; t < hi; ++t)
-    if (is_start<PosT>(a, t)) a.cu[slot++] = (int32_t)t;
+  for_starts<PosT>(a, lo, hi, [&](u32 t) { a.cu[slot++] = (int32_t)t; });
   __syncthreads();
-  for (int off = kSegThreads / 2; off > 0; off >>= 1) {
-    if (tid < off) s_max[tid] = max(s_max[tid], s_max[tid + off]);
-    __syncthreads();
-  }
   if (tid == kSegThreads - 1) {
     a.cu[incl] = (int32_t)a.T;
     *a.n_out = incl;
   }
-  if (tid == 0) *a.max_len = s_max[0];
+  if (tid == 0) {
+    int32_t m = 0;
+    for (int i = 0; i < kSegWaves; ++i) m = max(m, s_max[i]);
+    *a.max_len = m;
+  }
 }
 
 hipError_t segments_launch(const void* pos, int pos_bytes, int P, int B, int S, int32_t* cu,
