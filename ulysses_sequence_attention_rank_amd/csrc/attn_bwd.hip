@@ -153,7 +153,8 @@ __global__ void dsink_final_kernel(AttnArgs a) {
 // global_load_lds into swizzled natural tiles; K also serves the K^T operand
 // of dQ^T += K^T dS^T through the transposing reads.
 
-template <int D, int NW>
+// SINK: the rows' sum of P dP is accumulated too (it feeds dsink).
+template <int D, int NW, int SINK>
 __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(AttnArgs a) {
   constexpr int BM = 32 * NW, NB = D / 32, KS = D / 16;
   constexpr int TILE = kBK * D * 2;
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(AttnArgs a) {
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) dqacc[nb][e] = 0.f;
-  const bool want_pdp = a.sink != nullptr;
+  constexpr bool want_pdp = SINK != 0;
   float pdp = 0.f;
   const f32x16 zero = {};
 
@@ -231,9 +232,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(AttnArgs a) {
     so.refresh();
 
     const bool full = k0 >= full_lo && k0 + kBK <= full_hi;
-    // this lane's visible keys relative to its first key slot of the tile:
-    // slot e of block mb holds key offset 32 mb + 8 (e / 4) + e % 4
-    const int vis_lo = klo - (k0 + 4 * hf), vis_hi = khi - (k0 + 4 * hf);
+    // this lane's visible keys relative to its first key slot of the tile
+    // (slot e of block mb holds key offset 32 mb + 8 (e / 4) + e % 4); a
+    // fully visible tile opens the interval, so each value takes one select
+    const int vis_lo = full ? -(1 << 30) : klo - (k0 + 4 * hf);
+    const int vis_hi = full ? (1 << 30) : khi - (k0 + 4 * hf);
     // one 32-key block at a time keeps two accumulators live, not four
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -246,10 +249,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], a.scale_log2, -lse2));
-        if (!full) {
-          const int c = 32 * mb + 8 * (e >> 2) + (e & 3);
-          if (c < vis_lo || c >= vis_hi) p = 0.f;
-        }
+        const int c = 32 * mb + 8 * (e >> 2) + (e & 3);
+        p = (c >= vis_lo && c < vis_hi) ? p : 0.f;
         if (want_pdp) pdp = __builtin_fmaf(p, dpacc[e], pdp);
         sacc[e] = p * (dpacc[e] - dlt);  // dS^T
       }
@@ -322,6 +323,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(AttnArgs a) {
   }
 }
 
+// Explicit instantiations: with the two launches of the launcher's if/else,
+// hipcc emitted the host stub of only one of them.
+template __global__ void attn_bwd_dq_kernel<128, 4, 0>(AttnArgs);
+template __global__ void attn_bwd_dq_kernel<128, 4, 1>(AttnArgs);
+template __global__ void attn_bwd_dq_kernel<64, 4, 0>(AttnArgs);
+template __global__ void attn_bwd_dq_kernel<64, 4, 1>(AttnArgs);
+
 // dQ = scale * sum of the split partials (fixed order), to bf16; the same for
 // the rows' sum of P dP.
 template <int D>
@@ -376,7 +384,10 @@ static hipError_t launch_bwd_t(const AttnArgs& args, hipStream_t st) {
     b.nsplit = qtile_splits(a.B, a.S, a.hq, D, uneven_layer(a.causal, a.wl, a.wr));
     {
       ProfScope prof("attn_bwd_dq", st);
-      hipLaunchKernelGGL((attn_bwd_dq_kernel<D, NW>), dim3(blocks, b.nsplit), dim3(NW * 64), 0, st, b);
+      if (a.sink != nullptr)
+        hipLaunchKernelGGL((attn_bwd_dq_kernel<D, NW, 1>), dim3(blocks, b.nsplit), dim3(NW * 64), 0, st, b);
+      else
+        hipLaunchKernelGGL((attn_bwd_dq_kernel<D, NW, 0>), dim3(blocks, b.nsplit), dim3(NW * 64), 0, st, b);
     }
     if (b.nsplit > 1) {
       ProfScope prof("attn_bwd_dq_reduce", st);
