@@ -162,9 +162,15 @@ __global__ __launch_bounds__(KG * 128) void attn_bwd_dkdv_kernel(AttnArgs a) {
   const int n_iter = nq * a.G;
   // Q and dO tiles share row stride and swizzle: one set of per-lane offsets
   const TileOffsets<D, kBK, NW> offs(ld, wave, lane);
-  int nh = 0, nt = 0;  // (head in the group, tile) of the next tile to issue
+  // Tiles are walked last first, the group's heads inner: every work-group of
+  // a KV head starts on the same (last) query tile, so the work-groups that
+  // share an XCD (neighbouring key tiles) stream the same Q/dO tiles at about
+  // the same time and share them through its L2.  (Starting each at its own
+  // first visible tile, the S=131072 causal kernel fetched 115 GB a launch
+  // from beyond L2.)
+  int nh = 0, nt = 0;  // (head in the group, tile counted from the last) of the next tile to issue
   auto issue = [&](char* buf) {
-    const int qa = wg_lo + nt * kBK, h = g * a.G + nh;
+    const int qa = wg_lo + (nq - 1 - nt) * kBK, h = g * a.G + nh;
     const int64_t row0 = (int64_t)qa * a.hq + h;  // rows up to wg_hi + 63 < T + kPad exist
     offs.load(buf, a.q16 + row0 * D, wave);
     offs.load(buf + SM::kTile, a.do16 + row0 * D, wave);
@@ -173,9 +179,9 @@ __global__ __launch_bounds__(KG * 128) void attn_bwd_dkdv_kernel(AttnArgs a) {
       const float* src = wave == 0 ? a.lse2 + idx : a.delta + idx;
       __builtin_amdgcn_global_load_lds(src, (lds_void*)(buf + 2 * SM::kTile + wave * kBK * 4), 4, 0, 0);
     }
-    if (++nt == nq) {
-      nt = 0;
-      ++nh;
+    if (++nh == a.G) {
+      nh = 0;
+      ++nt;
     }
     return qa;
   };
@@ -201,8 +207,8 @@ __global__ __launch_bounds__(KG * 128) void attn_bwd_dkdv_kernel(AttnArgs a) {
   int it_lo, it_hi;
   split_range(n_iter, blockIdx.y, a.nsplit, it_lo, it_hi);
   if (it_lo < it_hi) {
-    nh = it_lo / nq;
-    nt = it_lo - nh * nq;
+    nt = it_lo / a.G;
+    nh = it_lo - nt * a.G;
   }
   int qa0 = it_lo < it_hi ? issue(st0) : 0, qa1 = 0;
   for (int it = it_lo; it < it_hi; it += 2) {
