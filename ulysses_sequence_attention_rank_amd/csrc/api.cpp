@@ -154,14 +154,25 @@ size_t align256(size_t x);
 // fp32 partial sums of the split backward kernels (they run one after the
 // other, so one buffer serves both): max(dQ partials, dK+dV partials) plus
 // the split sums of P dP.
-size_t split_part_bytes(int B, int S, int hq, int hkv, int D) {
+// The dK/dV balanced schedule's part slots (2 W of dK and dV for 128 keys)
+// share that buffer; its key-tile prefix follows it.
+size_t bal_slot_bytes(int B, int S, int hkv, int D) {
+  const int W = uly::dkdv_bal_workgroups(B, S, hkv);
+  return W > 0 ? (size_t)2 * W * 2 * 128 * D * 4 : 0;
+}
+size_t split_main_bytes(int B, int S, int hq, int hkv, int D) {
   const size_t T = (size_t)B * S;
   const int nq = uly::qtile_splits(B, S, hq, D, true), nk = uly::dkdv_splits(B, S, hkv, D, true);
-  size_t part = 0;
-  if (nq > 1) part = (size_t)nq * T * hq * D * 4;
+  size_t part = bal_slot_bytes(B, S, hkv, D);
+  if (nq > 1 && (size_t)nq * T * hq * D * 4 > part) part = (size_t)nq * T * hq * D * 4;
   if (nk > 1 && (size_t)nk * 2 * T * hkv * D * 4 > part) part = (size_t)nk * 2 * T * hkv * D * 4;
+  return align256(part) + align256((size_t)(uly::kBalMaxTilesHost + 1) * 4);
+}
+size_t split_part_bytes(int B, int S, int hq, int hkv, int D) {
+  const size_t T = (size_t)B * S;
+  const int nq = uly::qtile_splits(B, S, hq, D, true);
   const size_t pdp = nq > 1 ? (size_t)nq * T * hq * 4 : 0;
-  return align256(part) + align256(pdp);
+  return split_main_bytes(B, S, hq, hkv, D) + align256(pdp);
 }
 
 // ---- optional per-kernel timing: a HIP event before and after each launch
@@ -633,13 +644,12 @@ static int attn_bwd_impl(const void* q, const void* k, const void* v, const void
   a.k16 = (_Float16*)(h16 + 2 * qsz);
   a.v16 = (_Float16*)(h16 + 2 * qsz + kvsz);
   {
-    const size_t T = (size_t)B * S;
-    const int nq = uly::qtile_splits(B, S, hq, D, true), nk = uly::dkdv_splits(B, S, hkv, D, true);
-    size_t part = 0;
-    if (nq > 1) part = (size_t)nq * T * hq * D * 4;
-    if (nk > 1 && (size_t)nk * 2 * T * hkv * D * 4 > part) part = (size_t)nk * 2 * T * hkv * D * 4;
-    a.part = (float*)(h16 + 2 * qsz + 2 * kvsz);
-    a.part_pdp = (float*)(h16 + 2 * qsz + 2 * kvsz + align256(part));
+    char* base = h16 + 2 * qsz + 2 * kvsz;
+    const size_t main = split_main_bytes(B, S, hq, hkv, D);
+    a.part = (float*)base;
+    a.bal_prefix = (int*)(base + main - align256((size_t)(uly::kBalMaxTilesHost + 1) * 4));
+    a.part_pdp = (float*)(base + main);
+    a.bal_W = uly::dkdv_bal_workgroups(B, S, hkv);
   }
   a.n_part = kDsinkParts;
   return hip_status(uly::attn_bwd_launch(a, D, (hipStream_t)stream), "ulysses_attn_bwd launch");

@@ -106,7 +106,21 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, const char* buf, co
     }
 }
 
-template <int D, int KG>
+// (query tile, head) iterations a key tile of BN keys visits (at least one
+// unit: see the balanced schedule in attn_common.hpp)
+template <int BN>
+__device__ __forceinline__ int dkdv_tile_units(const AttnArgs& a, int kt) {
+  const int k0 = kt * BN, kl = min(k0 + BN, a.T) - 1;
+  int lo, hi, x, y;
+  query_interval(a, k0, lo, x);
+  query_interval(a, kl, y, hi);
+  return max(a.G * ((hi - lo + kBK - 1) / kBK), 1);
+}
+
+// BAL: the balanced schedule of small grids (a 1-D grid of bal_W
+// work-groups, each walking its share of the (key tile, KV head) items);
+// otherwise one item per work-group, its iterations split over blockIdx.y.
+template <int D, int KG, bool BAL>
 __global__ __launch_bounds__(KG * 128) void attn_bwd_dkdv_kernel(AttnArgs a) {
   constexpr int NW = 2 * KG, BN = 32 * KG, NB = D / 32;
   static_assert(NW >= 2, "two waves stage the per-row statistics");
@@ -115,24 +129,30 @@ __global__ __launch_bounds__(KG * 128) void attn_bwd_dkdv_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char st0[SM::kStage];
   __shared__ __attribute__((aligned(1024))) char st1[SM::kStage];
 
-  // Unsplit (large) grids: key tiles of one KV head in bands per XCD, so
-  // neighbouring key tiles, which read mostly the same Q/dO tiles at about
-  // the same time, share an L2 (measured 4 % on a 131072-token causal head;
-  // on small split grids the plain order is faster).
-  int L = (int)blockIdx.x, g, kt;
-  if (a.nsplit == 1) {
-    L = xcd_band_item(L, a.n_tiles * a.hkv, 32);
-    if (L < 0) return;
-    g = L / a.n_tiles;
-    kt = L - g * a.n_tiles;
-  } else {
-    if (L >= a.n_tiles * a.hkv) return;
-    kt = L / a.hkv;
-    g = L - kt * a.hkv;
-  }
   const int lane = threadIdx.x & 63, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kg = wave % KG, qb = wave / KG;  // key group, query block
+  const int ld = a.hq * D;
+  // Q and dO tiles share row stride and swizzle: one set of per-lane offsets
+  const TileOffsets<D, kBK, NW> offs(ld, wave, lane);
+  // LDS read offsets: this wave's key rows in the K/V area, and its block's
+  // swizzled rows of a stage tile (the swizzle repeats every 16 rows)
+  SwzOffsets<D> so(lane);
+  int kvo[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    kvo[s] = 32 * kg * 2 * D + so.nat[s];
+    so.nat[s] += 32 * qb * 2 * D;
+  }
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb) {
+    so.tr[nb][0] += 32 * qb * 2 * D;
+    so.tr[nb][1] += 32 * qb * 2 * D;
+  }
+
+  // Key tile kt of KV head g, iterations [seg_lo, seg_hi) of its walk (BAL),
+  // into part slot `slot` (BAL, slot >= 0) or finished.
+  auto item = [&](int kt, int g, int seg_lo, int seg_hi, int slot) __attribute__((always_inline)) {
   const int k0 = kt * BN;
   const int krow = k0 + 32 * kg + (lane & 31);
   const bool kvalid = krow < a.T;
@@ -157,11 +177,8 @@ __global__ __launch_bounds__(KG * 128) void attn_bwd_dkdv_kernel(AttnArgs a) {
       dvacc[nb][e] = 0.f;
     }
 
-  const int ld = a.hq * D;
   const int nq = (wg_hi - wg_lo + kBK - 1) / kBK;  // query tiles per head
   const int n_iter = nq * a.G;
-  // Q and dO tiles share row stride and swizzle: one set of per-lane offsets
-  const TileOffsets<D, kBK, NW> offs(ld, wave, lane);
   // Tiles are walked last first, the group's heads inner: every work-group of
   // a KV head starts on the same (last) query tile, so the work-groups that
   // share an XCD (neighbouring key tiles) stream the same Q/dO tiles at about
@@ -185,27 +202,18 @@ __global__ __launch_bounds__(KG * 128) void attn_bwd_dkdv_kernel(AttnArgs a) {
     }
     return qa;
   };
-  // LDS read offsets: this wave's key rows in the K/V area, and its block's
-  // swizzled rows of a stage tile (the swizzle repeats every 16 rows)
-  SwzOffsets<D> so(lane);
-  int kvo[D / 16];
-#pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    kvo[s] = 32 * kg * 2 * D + so.nat[s];
-    so.nat[s] += 32 * qb * 2 * D;
-  }
-#pragma unroll
-  for (int nb = 0; nb < D / 32; ++nb) {
-    so.tr[nb][0] += 32 * qb * 2 * D;
-    so.tr[nb][1] += 32 * qb * 2 * D;
-  }
   auto compute = [&](const char* buf, int qa) {
     dkdv_tile<D, KG>(a, buf, kvs, so, kvo, dkacc, dvacc, qa, qb, full_lo, full_hi, qlo, qhi, lane);
   };
 
-  // this split's share of the (head, query tile) iterations
+  // this split's (or segment's) share of the (query tile, head) iterations
   int it_lo, it_hi;
-  split_range(n_iter, blockIdx.y, a.nsplit, it_lo, it_hi);
+  if constexpr (BAL) {
+    it_lo = seg_lo;
+    it_hi = min(seg_hi, n_iter);
+  } else {
+    split_range(n_iter, blockIdx.y, a.nsplit, it_lo, it_hi);
+  }
   if (it_lo < it_hi) {
     nt = it_lo / a.G;
     nh = it_lo - nt * a.G;
@@ -250,6 +258,20 @@ __global__ __launch_bounds__(KG * 128) void attn_bwd_dkdv_kernel(AttnArgs a) {
     }
 
   // dK, dV: lane holds column d = 32 nb + l % 32 of key rows 8 i + 4 hf + j
+  if (BAL && slot >= 0) {  // this part, unscaled: slot [2][BN][D] (dK, then dV)
+    float* sk = a.part + (int64_t)slot * 2 * BN * D;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int kr = 32 * kg + 8 * (e >> 2) + 4 * hf + (e & 3);
+      const int64_t off = (int64_t)kr * D + (lane & 31);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        sk[off + 32 * nb] = dkacc[nb][e];
+        sk[BN * D + off + 32 * nb] = dvacc[nb][e];
+      }
+    }
+    return;
+  }
   const int64_t plane = (int64_t)a.T * a.hkv * D;
   float* pk = a.part + blockIdx.y * plane;
   float* pv = a.part + (a.nsplit + blockIdx.y) * plane;
@@ -259,7 +281,7 @@ __global__ __launch_bounds__(KG * 128) void attn_bwd_dkdv_kernel(AttnArgs a) {
     const int key = k0 + 32 * kg + 8 * (e >> 2) + 4 * hf + (e & 3);
     if (key >= a.T) continue;
     const int col = lane & 31;
-    if (a.nsplit > 1) {
+    if (!BAL && a.nsplit > 1) {
       const int64_t off = ((int64_t)key * a.hkv + g) * D + col;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
@@ -282,6 +304,32 @@ __global__ __launch_bounds__(KG * 128) void attn_bwd_dkdv_kernel(AttnArgs a) {
         a.dv[off + 32 * nb] = (__bf16)dvacc[nb][e];
       }
     }
+  }
+  };
+
+  if constexpr (BAL) {
+    __shared__ int pre[kBalMaxTiles + 1];
+    bal_prefix(pre, a.n_tiles, [&](int t) { return dkdv_tile_units<BN>(a, t); });
+    if (blockIdx.x == 0)
+      for (int t = threadIdx.x; t <= a.n_tiles; t += blockDim.x) a.bal_prefix[t] = pre[t];
+    bal_walk(pre, a.n_tiles, a.hkv, a.bal_W, item);
+  } else {
+    // Unsplit (large) grids: key tiles of one KV head in bands per XCD, so
+    // neighbouring key tiles, which read mostly the same Q/dO tiles at about
+    // the same time, share an L2 (measured 4 % on a 131072-token causal head;
+    // on small split grids the plain order is faster).
+    int L = (int)blockIdx.x, g, kt;
+    if (a.nsplit == 1) {
+      L = xcd_band_item(L, a.n_tiles * a.hkv, 32);
+      if (L < 0) return;
+      g = L / a.n_tiles;
+      kt = L - g * a.n_tiles;
+    } else {
+      if (L >= a.n_tiles * a.hkv) return;
+      kt = L / a.hkv;
+      g = L - kt * a.hkv;
+    }
+    item(kt, g, 0, 0, -1);
   }
 }
 
@@ -312,15 +360,67 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(AttnArgs a, int64_t n)
   *reinterpret_cast<u32x2*>(a.dv + off) = wv;
 }
 
+// dK = scale * the sum of the parts of a balanced schedule's items, dV = the
+// sum, in work-group order (rows of items finished in place are skipped).
+template <int D, int BN>
+__global__ __launch_bounds__(256) void dkdv_reduce_bal_kernel(AttnArgs a, int64_t n) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  const int rr = (int)(i / D), t = rr / a.hkv, g = rr - t * a.hkv;  // row rr = t * hkv + g
+  const int c = (int)(i - (int64_t)rr * D);
+  const int kt = t / BN, lr = t - kt * BN;
+  const BalItem it(a.bal_prefix, a.n_tiles, kt, g, a.hkv, a.bal_W);
+  if (it.la == it.lb) return;
+  f32x4 k = {0.f, 0.f, 0.f, 0.f}, v = {0.f, 0.f, 0.f, 0.f};
+  for (int lam = it.la; lam <= it.lb; ++lam) {
+    if (!it.holds(lam)) continue;
+    const float* p = a.part + (int64_t)it.slot(lam) * 2 * BN * D + (int64_t)lr * D + c;
+    k += *reinterpret_cast<const f32x4*>(p);
+    v += *reinterpret_cast<const f32x4*>(p + BN * D);
+  }
+  const int64_t off = row_of(a.mk, t) + (int64_t)g * a.mk.head + c;
+  if (a.dkv_f32) {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.dk) + off) = k * a.scale;
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.dv) + off) = v;
+    return;
+  }
+  u32x2 wk, wv;
+  wk[0] = pack_bf16x2(k[0] * a.scale, k[1] * a.scale);
+  wk[1] = pack_bf16x2(k[2] * a.scale, k[3] * a.scale);
+  wv[0] = pack_bf16x2(v[0], v[1]);
+  wv[1] = pack_bf16x2(v[2], v[3]);
+  *reinterpret_cast<u32x2*>(a.dk + off) = wk;
+  *reinterpret_cast<u32x2*>(a.dv + off) = wv;
+}
+
+// Explicit instantiations: with two launches of one kernel template in an
+// if/else, hipcc has emitted the host stub of only one of them.
+template __global__ void attn_bwd_dkdv_kernel<128, 4, true>(AttnArgs);
+template __global__ void attn_bwd_dkdv_kernel<128, 4, false>(AttnArgs);
+template __global__ void attn_bwd_dkdv_kernel<64, 4, true>(AttnArgs);
+template __global__ void attn_bwd_dkdv_kernel<64, 4, false>(AttnArgs);
+
+static_assert(kBalMaxTiles == kBalMaxTilesHost, "host and device agree on the balanced tile cap");
+
 template <int D, int KG>
 static void launch_dkdv_t(const AttnArgs& args, hipStream_t st) {
   AttnArgs b = args;
   b.n_tiles = (b.T + 32 * KG - 1) / (32 * KG);
+  if (b.bal_W > 0) {  // balanced schedule: parts in 2 bal_W slots, then their sum
+    {
+      ProfScope prof("attn_bwd_dkdv", st);
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, KG, true>), dim3(b.bal_W), dim3(KG * 128), 0, st, b);
+    }
+    ProfScope prof("attn_bwd_dkdv_reduce", st);
+    const int64_t n = (int64_t)b.T * b.hkv * D;
+    hipLaunchKernelGGL((dkdv_reduce_bal_kernel<D, 32 * KG>), dim3((n / 4 + 255) / 256), dim3(256), 0, st, b, n);
+    return;
+  }
   b.nsplit = dkdv_splits(b.B, b.S, b.hkv, D, uneven_layer(b.causal, b.wl, b.wr));
   {
     ProfScope prof("attn_bwd_dkdv", st);
     const int items = b.n_tiles * b.hkv;
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, KG>), dim3((items + kXcds - 1) / kXcds * kXcds, b.nsplit),
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, KG, false>), dim3((items + kXcds - 1) / kXcds * kXcds, b.nsplit),
                        dim3(KG * 128),
                        0, st, b);
   }

@@ -91,6 +91,11 @@ struct AttnArgs {
   int nsplit;
   float* part;       // dq: [nsplit][T][hq][D]; dkdv: dK then dV, [nsplit][T][hkv][D]
   float* part_pdp;   // dq: [nsplit][B][hq][S]; fwd: running max then sum, [2][nsplit][B][hq][S]
+  // dK/dV balanced schedule (bal_W > 0 work-groups, see the balanced
+  // schedule below): `part` then holds 2 bal_W slots of [2][BN][D] fp32
+  // parts, and bal_prefix receives the unit prefix over the key tiles.
+  int bal_W;
+  int* bal_prefix;
 };
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -389,6 +394,106 @@ struct SwzOffsets {
     const i16x8 x = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(bf16x8, x);
   }
+};
+
+// ------------------------------------------------ balanced schedule
+//
+// For grids too small to fill the GPU with one work-group per item.  An item
+// is (tile t, head h), numbered i = h * n_tiles + t; it is a run of c[t] >= 1
+// units (the tiles it visits; an item with none still takes one, to write its
+// empty result).  With the runs concatenated, U units in all, work-group lam
+// takes units [start(lam), start(lam + 1)), start(lam) = floor(lam U / W):
+// equal shares whatever the mask makes of the runs.  An item whose run lies
+// inside one share is finished by that work-group.  Otherwise each
+// work-group writes its part of the item to a slot: 2 lam for an item begun
+// by an earlier work-group, 2 lam + 1 for one continued by a later one; a
+// reduce kernel adds an item's parts in work-group order (deterministic).
+constexpr int kBalMaxTiles = 2048;
+
+__device__ __forceinline__ int64_t bal_start(int64_t lam, int64_t U, int W) { return lam * U / W; }
+// the work-group whose share holds unit u (the largest lam with start <= u)
+__device__ __forceinline__ int bal_owner(int64_t u, int64_t U, int W) { return (int)(((u + 1) * W - 1) / U); }
+
+// Exclusive prefix P[0..n] of count(t), t < n (n <= kBalMaxTiles), in LDS;
+// every thread of the work-group calls it.
+template <typename F>
+__device__ __forceinline__ void bal_prefix(int* P, int n, F count) {
+  for (int t = threadIdx.x; t < n; t += blockDim.x) P[t + 1] = count(t);
+  __syncthreads();
+  if (threadIdx.x < 64) {  // one wave scans: lane l owns tiles [l C, (l + 1) C)
+    const int lane = threadIdx.x, C = (n + 63) / 64;
+    const int lo = min(lane * C, n), hi = min(lo + C, n);
+    int s = 0;
+    for (int t = lo; t < hi; ++t) s += P[t + 1];
+    int x = s;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off, 64);
+      if (lane >= off) x += y;
+    }
+    int run = x - s;
+    for (int t = lo; t < hi; ++t) {
+      run += P[t + 1];
+      P[t + 1] = run;
+    }
+    if (lane == 0) P[0] = 0;
+  }
+  __syncthreads();
+}
+
+// The tile t holding unit r of a head's run (P[t] <= r < P[t + 1]).
+__device__ __forceinline__ int bal_tile(const int* P, int n, int r) {
+  int lo = 0, hi = n;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (P[mid] <= r) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// This work-group's share, item by item: f(t, h, seg_lo, seg_hi, slot) runs
+// units [seg_lo, seg_hi) of item (t, h) (offsets in its run) and writes the
+// finished result (slot < 0) or part slot `slot`.  Work-groups are dealt to
+// the XCDs round-robin; consecutive shares go to one XCD (W % kXcds == 0).
+template <typename F>
+__device__ __forceinline__ void bal_walk(const int* P, int n, int nh, int W, F f) {
+  const int tot = P[n];
+  const int64_t U = (int64_t)nh * tot;
+  const int lam = (int)(blockIdx.x % kXcds) * (W / kXcds) + (int)(blockIdx.x / kXcds);
+  const int64_t s0 = bal_start(lam, U, W), s1 = bal_start(lam + 1, U, W);
+  int64_t u = s0;
+  bool first = true;
+  while (u < s1) {
+    const int h = (int)(u / tot), r = (int)(u - (int64_t)h * tot);
+    const int t = bal_tile(P, n, r);
+    const int64_t p0 = (int64_t)h * tot + P[t], p1 = p0 + (P[t + 1] - P[t]);
+    const int64_t e = min(s1, p1);
+    const int slot = (u == p0 && e == p1) ? -1 : (p0 < s0 ? 2 * lam : 2 * lam + 1);
+    if (!first) __syncthreads();  // the previous item's LDS is no longer read
+    first = false;
+    f(t, h, (int)(u - p0), (int)(e - p0), slot);
+    u = e;
+  }
+}
+
+// For the reduce of item (t, h) of n tiles and nh heads: the work-groups
+// la .. lb that hold its parts (la == lb: finished in place), whether
+// work-group lam of them holds one (shares can be empty when U < W), and
+// its slot (2 lam + 1 for la, which begins the item; 2 lam after).
+struct BalItem {
+  int la, lb, W;
+  int64_t U;
+  __device__ __forceinline__ BalItem(const int* P, int n, int t, int h, int nh, int W_) : W(W_) {
+    const int tot = P[n];
+    U = (int64_t)nh * tot;
+    const int64_t p0 = (int64_t)h * tot + P[t], p1 = p0 + (P[t + 1] - P[t]);
+    la = bal_owner(p0, U, W);
+    lb = bal_owner(p1 - 1, U, W);
+  }
+  __device__ __forceinline__ bool holds(int lam) const {
+    return lam == la || bal_start(lam + 1, U, W) > bal_start(lam, U, W);
+  }
+  __device__ __forceinline__ int slot(int lam) const { return lam == la ? 2 * lam + 1 : 2 * lam; }
 };
 
 // Contiguous share [lo, hi) of n iterations for split s of ns.

@@ -88,6 +88,25 @@ inline int fwd_splits(int B, int S, int hq, int bm, int D, bool uneven) {
   const long T = (long)B * S;
   return choose_splits(((T + bm - 1) / bm) * hq, (T + 63) / 64, 512, 4.0 * T * hq * (D + 2), uneven);
 }
+// dK/dV balanced schedule (attn_common.hpp): one round of 256 work-groups
+// takes equal shares of the (query tile, head) iterations of all (key tile,
+// KV head) items of 128 keys.  Used when the items fill at most two rounds of
+// one-per-CU work-groups and there are at least 256 key tiles: long causal
+// or packed sequences, whose key tiles carry very uneven work (measured,
+// dK/dV per launch: packed S=32768, GQA 4, 825 -> 643 us; the same over 16
+// ranks with replicated KV, 295 -> 193 us; S=65536 window + causal,
+// unchanged).  On short sequences (S=4096, 32 key tiles) it lost: every
+// item is split, the parts must be summed, and work-groups that continue an
+// item walk other query tiles than their XCD neighbours, which loses the
+// shared L2 streaming (full layer 132 -> 132 + 14 us, causal 84 -> 107 us).
+// Returns the work-group count, 0 for none.
+constexpr int kBalMaxTilesHost = 2048;
+constexpr int kDkdvBalWorkgroups = 256;
+inline int dkdv_bal_workgroups(int B, int S, int hkv) {
+  const long tiles = ((long)B * S + 127) / 128;
+  if (tiles < 256 || tiles > kBalMaxTilesHost || tiles * hkv > 2 * 256) return 0;
+  return kDkdvBalWorkgroups;
+}
 // A layer's work-groups are uneven when it is causal or windowed.  Split
 // counts never fall when `uneven` is set, so workspaces sized with it serve
 // every layer.
