@@ -77,17 +77,32 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, const char* buf, co
     sacc = mfma32h(so.nat_at(qs, 0, s), kv_at(ks, s), s == 0 ? zero : sacc);
     dpacc = mfma32h(so.nat_at(dos, 0, s), kv_at(vs, s), s == 0 ? zero : dpacc);
   }
+  // a fully visible tile (wave-uniform) skips the per-element mask
+  if (__builtin_amdgcn_readfirstlane((int)full)) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const f32x4 l4 = *reinterpret_cast<const f32x4*>(lsw + 8 * i);
-    const f32x4 d4 = *reinterpret_cast<const f32x4*>(lsw + kBK + 8 * i);
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(lsw + 8 * i);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(lsw + kBK + 8 * i);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * i + j], a.scale_log2, -l4[j]));
-      const int rc = 8 * i + j;
-      p = (rc >= mlo && rc < mhi) ? p : 0.f;
-      sacc[4 * i + j] = p;
-      dpacc[4 * i + j] = p * (dpacc[4 * i + j] - d4[j]);
+      for (int j = 0; j < 4; ++j) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * i + j], a.scale_log2, -l4[j]));
+        sacc[4 * i + j] = p;
+        dpacc[4 * i + j] = p * (dpacc[4 * i + j] - d4[j]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(lsw + 8 * i);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(lsw + kBK + 8 * i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * i + j], a.scale_log2, -l4[j]));
+        const int rc = 8 * i + j;
+        p = (rc >= mlo && rc < mhi) ? p : 0.f;
+        sacc[4 * i + j] = p;
+        dpacc[4 * i + j] = p * (dpacc[4 * i + j] - d4[j]);
+      }
     }
   }
   bf16x8 pf[2], df[2];
