@@ -154,6 +154,12 @@ __global__ void dsink_final_kernel(AttnArgs a) {
 // of dQ^T += K^T dS^T through the transposing reads.
 
 // SINK: the rows' sum of P dP is accumulated too (it feeds dsink).
+// a compile-time flag carried by a generic lambda's argument type
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+
 template <int D, int NW, int SINK>
 __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(AttnArgs a) {
   constexpr int BM = 32 * NW, NB = D / 32, KS = D / 16;
@@ -215,28 +221,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(AttnArgs a) {
     offs.load(stage0 + TILE, vbase + r0, kBK, wave);
   }
 
-  // one key tile: `cur` holds tile `it`, tile it+1 goes to `nxt`
-  auto step = [&](int it, const char* cur, char* nxt) __attribute__((always_inline)) {
-    const int k0 = wg_lo + it * kBK;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (it + 1 < it_hi) {
-      const int64_t r0 = (int64_t)(k0 + kBK) * ld;
-      offs.load(nxt, kbase + r0, kBK, wave);
-      offs.load(nxt + TILE, vbase + r0, kBK, wave);
-    }
-    const char* kt = cur;
-    const char* vt = cur + TILE;
-    // one set of read offsets for both stages (two hoisted sets would not
-    // fit the register budget next to the accumulators)
-    so.refresh();
-
-    const bool full = k0 >= full_lo && k0 + kBK <= full_hi;
+  // the products and softmax of one staged key tile (FULL: every key of
+  // the tile is visible to every row of the work-group, no mask)
+  auto body = [&](auto full_c, int k0, const char* kt, const char* vt) __attribute__((always_inline)) {
+    constexpr bool FULL = decltype(full_c)::value;
     // this lane's visible keys relative to its first key slot of the tile
-    // (slot e of block mb holds key offset 32 mb + 8 (e / 4) + e % 4); a
-    // fully visible tile opens the interval, so each value takes one select
-    const int vis_lo = full ? -(1 << 30) : klo - (k0 + 4 * hf);
-    const int vis_hi = full ? (1 << 30) : khi - (k0 + 4 * hf);
+    // (slot e of block mb holds key offset 32 mb + 8 (e / 4) + e % 4)
+    const int vis_lo = klo - (k0 + 4 * hf), vis_hi = khi - (k0 + 4 * hf);
     // one 32-key block at a time keeps two accumulators live, not four
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -249,8 +240,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], a.scale_log2, -lse2));
-        const int c = 32 * mb + 8 * (e >> 2) + (e & 3);
-        p = (c >= vis_lo && c < vis_hi) ? p : 0.f;
+        if constexpr (!FULL) {
+          const int c = 32 * mb + 8 * (e >> 2) + (e & 3);
+          p = (c >= vis_lo && c < vis_hi) ? p : 0.f;
+        }
         if (want_pdp) pdp = __builtin_fmaf(p, dpacc[e], pdp);
         sacc[e] = p * (dpacc[e] - dlt);  // dS^T
       }
@@ -285,6 +278,28 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(AttnArgs a) {
       }
       __builtin_amdgcn_sched_group_barrier(0x008, PF / 2, 0);
     }
+  };
+  // one key tile: `cur` holds tile `it`, tile it+1 goes to `nxt`
+  auto step = [&](int it, const char* cur, char* nxt) __attribute__((always_inline)) {
+    const int k0 = wg_lo + it * kBK;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (it + 1 < it_hi) {
+      const int64_t r0 = (int64_t)(k0 + kBK) * ld;
+      offs.load(nxt, kbase + r0, kBK, wave);
+      offs.load(nxt + TILE, vbase + r0, kBK, wave);
+    }
+    const char* kt = cur;
+    const char* vt = cur + TILE;
+    // one set of read offsets for both stages (two hoisted sets would not
+    // fit the register budget next to the accumulators)
+    so.refresh();
+    // a fully visible tile (wave-uniform) takes a copy of the body without
+    // the per-element mask; each copy is one scheduling region
+    if (__builtin_amdgcn_readfirstlane((int)(k0 >= full_lo && k0 + kBK <= full_hi)))
+      body(BoolC<true>{}, k0, kt, vt);
+    else
+      body(BoolC<false>{}, k0, kt, vt);
   };
   for (int it = it_lo; it < it_hi; it += 2) {
     step(it, stage0, stage1);
