@@ -632,7 +632,7 @@ static int attn_bwd_impl(const void* q, const void* k, const void* v, const void
   a.dsink = dsink;
   char* ws = (char*)workspace;
   const size_t rows = align256((size_t)B * S * hq * sizeof(float));
-  a.delta = (float*)ws;
+  a.ndelta = (float*)ws;
   a.pdp = (float*)(ws + rows);
   a.lse2 = (float*)(ws + 2 * rows);
   a.dsink_part = (float*)(ws + 3 * rows);

@@ -1,6 +1,6 @@
 // Attention backward of one Ulysses rank.
 //
-//   delta_i = sum_d dO_i,d O_i,d                         (attn_bwd_prep)
+//   delta_i = sum_d dO_i,d O_i,d                         (attn_bwd_prep, stored negated)
 //   P_ij = exp(s_ij - LSE_i), dP_ij = dO_i . v_j, dS_ij = P_ij (dP_ij - delta_i)
 //   dK_j = scale sum_i dS_ij q_i, dV_j = sum_i P_ij dO_i  (attn_bwd_dkdv: one
 //          work-group owns 32*NW keys of one KV head and walks every query of
@@ -58,7 +58,7 @@ __device__ __forceinline__ void pre_block(const AttnArgs& a, int block) {
   if (valid && c == 0) {
     const int t = row / a.hq, h = row - t * a.hq;
     const int idx = lse_index(a, t, h);
-    a.delta[idx] = acc;
+    a.ndelta[idx] = -acc;
     const float l = a.lse[idx];
     a.lse2[idx] = l == -INFINITY ? INFINITY : l * kLog2e;  // rows with no key: P = 0
   }
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(AttnArgs a) {
   float lse2 = INFINITY, dlt = 0.f;  // invalid rows: P = 0
   if (qvalid) {
     lse2 = a.lse2[lse_index(a, qrow, h)];
-    dlt = a.delta[lse_index(a, qrow, h)];
+    dlt = -a.ndelta[lse_index(a, qrow, h)];
   }
 
   f32x16 dqacc[NB];

@@ -14,7 +14,7 @@ namespace uly {
 // group (2 KG waves, two per SIMD).  The work-group's K and V rows are staged
 // once in LDS (swizzled natural tiles) and read as B operands when needed.
 // The work-group walks every query tile (64 rows) of every query head of the
-// group: Q and dO tiles plus their LSE*log2(e) and delta rows arrive by
+// group: Q and dO tiles plus their LSE*log2(e) and -delta rows arrive by
 // global_load_lds, double-buffered in two distinct LDS arrays (the loop is
 // unrolled by two, so reads of one stage are provably disjoint from the loads
 // into the other).  Of each tile, the two waves of a key group take one
@@ -71,37 +71,44 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, const char* buf, co
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + kvo[s]));
   };
 
+  // dP - delta: the sums start from the rows' -delta (value 4 i + j of a lane
+  // belongs to row 8 i + j of its first row)
+  f32x16 dinit;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x4 d4 = *reinterpret_cast<const f32x4*>(lsw + kBK + 8 * i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dinit[4 * i + j] = d4[j];
+  }
   f32x16 sacc, dpacc;
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
     sacc = mfma32h(so.nat_at(qs, 0, s), kv_at(ks, s), s == 0 ? zero : sacc);
-    dpacc = mfma32h(so.nat_at(dos, 0, s), kv_at(vs, s), s == 0 ? zero : dpacc);
+    dpacc = mfma32h(so.nat_at(dos, 0, s), kv_at(vs, s), s == 0 ? dinit : dpacc);
   }
   // a fully visible tile (wave-uniform) skips the per-element mask
   if (__builtin_amdgcn_readfirstlane((int)full)) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(lsw + 8 * i);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(lsw + kBK + 8 * i);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * i + j], a.scale_log2, -l4[j]));
         sacc[4 * i + j] = p;
-        dpacc[4 * i + j] = p * (dpacc[4 * i + j] - d4[j]);
+        dpacc[4 * i + j] *= p;
       }
     }
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(lsw + 8 * i);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(lsw + kBK + 8 * i);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * i + j], a.scale_log2, -l4[j]));
         const int rc = 8 * i + j;
         p = (rc >= mlo && rc < mhi) ? p : 0.f;
         sacc[4 * i + j] = p;
-        dpacc[4 * i + j] = p * (dpacc[4 * i + j] - d4[j]);
+        dpacc[4 * i + j] *= p;
       }
     }
   }
@@ -208,7 +215,7 @@ __global__ __launch_bounds__(KG * 128) void attn_bwd_dkdv_kernel(AttnArgs a) {
     offs.load(buf + SM::kTile, a.do16 + row0 * D, wave);
     if (wave < 2) {
       const int idx = lse_index(a, min(qa + lane, a.T - 1), h);
-      const float* src = wave == 0 ? a.lse2 + idx : a.delta + idx;
+      const float* src = wave == 0 ? a.lse2 + idx : a.ndelta + idx;
       __builtin_amdgcn_global_load_lds(src, (lds_void*)(buf + 2 * SM::kTile + wave * kBK * 4), 4, 0, 0);
     }
     if (++nh == a.G) {

@@ -57,7 +57,7 @@ struct AttnArgs {
   __bf16* dv;
   int dkv_f32;   // dK, dV written unrounded in fp32
   float* lse;    // fwd output / bwd input, [B][hq][S]
-  float* delta;  // bwd: rowsum(dO * O) with the bf16 O, [B][hq][S]
+  float* ndelta;  // bwd: -rowsum(dO * O) with the bf16 O, [B][hq][S] (negated: dK/dV starts its dP sums from it)
   float* pdp;    // bwd: sum_j P_ij dP_ij = dO_i . O_i with the exact O, [B][hq][S]
   float* lse2;   // bwd: LSE * log2(e) (+inf for rows without keys), [B][hq][S]
   // bwd: exact fp16 copies of q, k, v, dout (the backward's products run in
