@@ -51,10 +51,11 @@ typedef enum {
 } uly_status;
 
 /* ------------------------------------------------------------------------
- * Layout permutation of the all-to-all ("scatter heads, gather sequence",
- * [accelerate#4209] PR body; the layouts are stated in its reply on the four
- * all-to-all call sites; the differentiable all-to-all's backward "swaps
- * scatter and gather", so the same two calls serve dO and dQ/dK/dV).
+ * Layout permutation of the sequence-to-head all-to-all ([accelerate#4209]
+ * PR body; the layouts are stated in its reply on the four all-to-all call
+ * sites, where the backward of the differentiable all-to-all runs the same
+ * exchange with the two directions exchanged, so the same two calls serve dO
+ * and dQ/dK/dV).
  *
  * ulysses_a2a_pack: seq_shards [P][B][S/P][H][D] -> head_shards [P][B][S][H/P][D]
  *   head[c][b][r*S/P + s][h'][d] = seq[r][b][s][c*H/P + h'][d]
@@ -148,7 +149,7 @@ int ulysses_cu_seqlens_from_positions(const void* pos_shards, int pos_bytes, int
  *   lse                   fp32 [B][hq][S], natural-log log-sum-exp per row
  * GQA: query head h uses KV head h / (hq/hkv) (contiguous groups; the rank
  * holds hq = Hq/P query heads and hkv = Hkv/P KV heads, [arctic#45] feature
- * list "modern MHA-variations").
+ * list, on attention variants beyond plain multi-head).
  * Documents: cu_seqlens (int32, n+1 entries over the B*S flattened tokens,
  * as produced by ulysses_cu_seqlens_from_positions) with *n_seqs on the
  * device; both NULL means one document per batch row.  Documents must not

@@ -9,7 +9,11 @@ The sequence-tiled gated MLP (fp64 torch CPU matmuls) is in ``oracle/mlp.py``.
 
 parity unpinned: none.  Every function is pinned by the CPU tests in
 ``tests/test_oracle_*.py`` (library special cases, finite differences, closed
-forms, brute force, a hand-worked example and invariants of the method).
+forms, brute force, a hand-worked example and invariants of the method).  The
+row/key subset mode of ``attn_fwd``/``attn_bwd`` (``rows``, ``qrows``,
+``krows``), which computes the softmax statistics of only the rows the
+requested outputs need, is pinned bit for bit to the full mode
+(``tests/test_oracle_subset.py``); statistics of skipped rows are NaN.
 """
 from __future__ import annotations
 

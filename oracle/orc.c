@@ -15,7 +15,7 @@
  *    sharded, the output leaves as [batch, seq, heads / sp_size, head_dim]);
  *    shards are numbered by where they sit in the sequence (same PR, the
  *    _prepare_sp_model comment); rank c receives the c-th contiguous chunk of
- *    heads ("scatter heads, gather sequence", PR body).
+ *    heads (the sequence-to-head all-to-all of the PR body).
  *  - orc_pack_replicated / orc_reduce_replicated: KV heads fewer than ranks,
  *    each sent to the ranks whose query heads use it, and the sum of the
  *    replicas' gradients (see the functions).
@@ -389,7 +389,8 @@ int orc_bwd(const orc_prob* p, const double* dout, const int64_t* qrows, int64_t
   if (dsink)
     for (int64_t i = 0; i < T; ++i) need[i] = 1;
 
-  /* 2. LSE_i and D_i = dO_i . O_i for those rows */
+  /* 2. LSE_i and D_i = dO_i . O_i for those rows (NaN for the others: a
+        result that read them would come out NaN, not silently wrong) */
   double* lse = (double*)malloc(sizeof(double) * (size_t)(T * hq > 0 ? T * hq : 1));
   double* Di = (double*)malloc(sizeof(double) * (size_t)(T * hq > 0 ? T * hq : 1));
 #pragma omp parallel
@@ -399,7 +400,11 @@ int orc_bwd(const orc_prob* p, const double* dout, const int64_t* qrows, int64_t
 #pragma omp for schedule(dynamic, 1)
     for (int64_t x = 0; x < T * hq; ++x) {
       const int64_t i = x / hq, h = x % hq;
-      if (!need[i]) continue;
+      if (!need[i]) {
+        lse[x] = NAN;
+        Di[x] = NAN;
+        continue;
+      }
       row_forward(p, doc, i, h, s, o, &lse[x]);
       Di[x] = dot(dout + x * D, o, D);
     }

@@ -3,10 +3,11 @@
 The step follows the accelerate PR "Add an FSDP2-native Ulysses sequence
 parallelism backend": the position_ids are gathered once and cu_seqlens /
 max_len rebuilt from them; Q, K, V go from sequence shards to head shards
-("scatter heads, gather sequence"); every rank runs attention over the whole
+(the sequence-to-head all-to-all); every rank runs attention over the whole
 sequence for its heads with its slice of the sink logits; the output goes
 back to sequence shards.  Backward mirrors it: dO is packed, each rank runs
-the attention backward, dQ/dK/dV are unpacked ("swap scatter and gather").
+the attention backward, dQ/dK/dV are unpacked (the all-to-all's backward is
+the same exchange with its directions exchanged).
 The exchange itself is a permutation here (one GPU); every step is a call
 into the HIP library.
 """
