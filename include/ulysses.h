@@ -311,6 +311,19 @@ size_t ulysses_attn_fwd_workspace_bytes(int B, int S, int hq, int hkv, int D);
 /* Bytes of device workspace ulysses_attn_bwd needs for these sizes. */
 size_t ulysses_attn_bwd_workspace_bytes(int B, int S, int hq, int hkv, int D);
 
+/* Byte offset, inside the workspace of a ulysses_attn_bwd* call with these
+ * sizes, of six int32 values the call leaves there (valid once the call's
+ * work on its stream has completed, until the workspace is reused):
+ *   [0..3] the exponents e, c, a, b of the power-of-two scales of the fp16
+ *       copies dout * 2^e, v * 2^c, q * 2^a, k * 2^b (see "Precision" below);
+ *   [4] the number of copied elements that saturated at +-65504 (scaled
+ *       magnitude above 65504, or NaN): the gradients may then be wrong;
+ *   [5] the number of other copied elements that are inexact (scaled
+ *       magnitude below 2^-17 with bits below 2^-24; error <= 2^-25 each,
+ *       before the scale is removed).
+ * A function of the sizes only (0 for sizes the backward rejects). */
+size_t ulysses_attn_bwd_status_offset(int B, int S, int hq, int hkv, int D);
+
 /* Backward of ulysses_attn_fwd for the loss sum(out * dout) ([accelerate#4209]:
  * gradients compared against an unsharded run; [lca#135]: backward of the
  * sharded attention).  Inputs as in the forward, plus out and lse from it.
@@ -323,8 +336,22 @@ size_t ulysses_attn_bwd_workspace_bytes(int B, int S, int hq, int hkv, int D);
  *   not matter and on return are unspecified (it holds per-row statistics,
  *   fp16 copies of q, k, v, dout and, on small problems, fp32 partial sums).
  * Precision: the products run in fp16 (fp32 accumulation) on fp16 copies of
- *   q, k, v and dout, which are exact for every bf16 value of magnitude up to
- *   65504; larger magnitudes saturate to +-65504.
+ *   q, k, v and dout that the call makes in the workspace, each an exact
+ *   power-of-two scaling of its bf16 tensor: q * 2^a, k * 2^b, v * 2^c,
+ *   dout * 2^e, with integer exponents (|x| <= 100) chosen on the device so
+ *   that every copied value, and every scaled dS_ij = P_ij (dP_ij - delta_i)
+ *   2^(e+c), stays below 2^15 in magnitude (bound for dS: max_i |dout_i|
+ *   max_j |v_j| + max_i |delta_i|, norms over the head dimension; a and b
+ *   are the largest such exponents, e and c share what the dS bound leaves).
+ *   The softmax scale absorbs 2^-(a+b) exactly and the gradients are
+ *   multiplied back by exact powers of two before they are stored, so inputs
+ *   and gradients of any magnitude keep fp16's 11 significant bits in P and
+ *   dS (a loss averaged over many tokens gives dout far below 1, which
+ *   unscaled fp16 would flush to zero).  A copied value is exact when its
+ *   scaled magnitude is at least 2^-17 (for q and k: magnitudes down to about
+ *   2^-32 of the tensor's largest); smaller ones round to a multiple of 2^-24
+ *   of the scaled value.  The call does not fail on inputs it cannot copy
+ *   exactly; it counts them on the device (ulysses_attn_bwd_status_offset).
  * Errors: as ulysses_attn_fwd, plus ULY_ERR_CAPACITY (workspace too small)
  *   and ULY_ERR_NULL (sink and dsink not both NULL or both set).
  */

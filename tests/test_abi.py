@@ -40,6 +40,7 @@ def test_header_declares_the_boundary():
                           "ulysses_attn_merge", "ulysses_attn_merge_finish",
                           "ulysses_attn_fwd_workspace_bytes",
                           "ulysses_attn_bwd_workspace_bytes", "ulysses_attn_bwd",
+                          "ulysses_attn_bwd_status_offset",
                           "ulysses_tiled_mlp_workspace_bytes", "ulysses_tiled_mlp_fwd",
                           "ulysses_tiled_mlp_bwd",
                           "ulysses_profile_start", "ulysses_profile_stop",
@@ -237,3 +238,16 @@ def test_tiled_mlp_argument_errors(lib):
                                                  _p(A), _p(A), 200, 128, 256, 128, _p(A), ws, None)
     assert bwd(dw=0) == NULL
     assert bwd(dw=A + 4) == ALIGN
+
+
+def test_bwd_status_words_sit_inside_the_workspace(lib):
+    """The status words' offset is a function of the sizes, 256-byte aligned,
+    inside the workspace the same sizes ask for; 0 for rejected sizes."""
+    lib.ulysses_attn_bwd_status_offset.restype = ctypes.c_size_t
+    lib.ulysses_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    for B, S, hq, hkv, D in ((1, 512, 4, 4, 64), (1, 4096, 6, 6, 128), (2, 1000, 7, 1, 128),
+                             (1, 131072, 7, 1, 128)):
+        off = lib.ulysses_attn_bwd_status_offset(B, S, hq, hkv, D)
+        need = lib.ulysses_attn_bwd_workspace_bytes(B, S, hq, hkv, D)
+        assert off > 0 and off % 256 == 0 and off + 24 <= need
+    assert lib.ulysses_attn_bwd_status_offset(0, 512, 4, 4, 64) == 0

@@ -70,11 +70,15 @@ def _sample_rows(cfg, cu, n, count=96):
 
 def _sample_keys(cfg, cu, n, variant):
     """Keys whose gradients the oracle can afford: every key whose visible rows are few
-    (window), the tail of the sequence, and the first keys of a document when the
-    document is short enough."""
+    (window), the tail of the sequence, 64 keys spread over its last 2048 (the
+    oracle then needs rows >= S - 2048 only), and the first keys of a document
+    when the document is short enough.  (Keys with the longest walks are
+    compared at 16k-32k tokens in test_gpu_long.py.)"""
     c = CONFIGS[cfg]
     S = c.S
     keys = set(range(S - 48, S))
+    if S >= 65536:
+        keys |= set(range(S - 2048, S, 32))
     if variant.window_left >= 0:
         g = torch.Generator().manual_seed(2000 + cfg)
         keys |= set(range(0, 48)) | set(torch.randint(0, S, (64,), generator=g).tolist())
@@ -165,6 +169,52 @@ def test_workload_parity(cfg, variant):
                 # rounding noise of L bf16 outputs and of delta grows like sqrt(L)
                 thr = 0.05 + 3e-3 * L ** 0.5
                 assert float(sdk.abs().max()) < thr, (d, float(sdk.abs().max()), thr)
+
+
+def test_fused_step_full_size():
+    """The fused step (attention reading Q/K/V and writing O/dQ/dK/dV in the
+    sequence shards in place, no pack/unpack) on the S=131072 workload, as the
+    benchmark times it: bit-identical to the packed step, whose outputs the
+    workload test compares with the oracle, and compared with the oracle on
+    sampled rows and keys of ranks 0 and P-1 directly."""
+    from ulysses_sequence_attention_rank_amd import sim
+    cfg = 5
+    inp = _inputs(cfg)
+    c = inp.case
+    P, S, D, hq, hkv = c.P, c.S, c.D, c.hq, c.hkv
+    variant = c.variants[0]
+    kw_step = dict(causal=variant.causal, window_left=variant.window_left,
+                   window_right=variant.window_right)
+    packed = _device_step(cfg, variant)
+    ref = [t.clone() for t in (packed.o_seq, packed.dq_seq, packed.dk_seq, packed.dv_seq, packed.lse)]
+    del packed
+    torch.cuda.empty_cache()
+    dev = torch.device("cuda", 0)
+    b = sim.allocate(seq_shards(inp.q, P).to(dev), seq_shards(inp.k, P).to(dev),
+                     seq_shards(inp.v, P).to(dev), seq_shards(inp.dout, P).to(dev),
+                     seq_shards(inp.positions, P).to(dev), None)
+    say(f"workload {cfg}: fused step, all {P} ranks")
+    sim.step(b, fused=True, **kw_step)
+    torch.cuda.synchronize()
+    for name, x, y in zip(("O", "dQ", "dK", "dV", "LSE"),
+                          (b.o_seq, b.dq_seq, b.dk_seq, b.dv_seq, b.lse), ref):
+        assert bits_equal(x, y), f"fused {name} differs from the packed step"
+    cu, n, _ = oracle.segments(oracle.gather_positions(seq_shards(inp.positions, P)))
+    rows, keys = _sample_rows(cfg, cu, n, count=32), list(range(S - 48, S))
+    qh, kh, vh, dh = _oracle_heads(cfg)
+    kw = dict(cu=cu, **kw_step)
+    ridx, kidx = torch.tensor(rows), torch.tensor(keys)
+    for r in (0, P - 1):
+        say(f"fused, rank {r}: oracle on {len(rows)} rows / {len(keys)} keys")
+        o, _ = oracle.attn_fwd(qh[r], kh[r], vh[r], rows=rows, **kw)
+        dq, dk, dv, _ = oracle.attn_bwd(qh[r], kh[r], vh[r], dh[r], qrows=rows, krows=keys,
+                                        want_dsink=False, **kw)
+        # rank r's heads, in the sequence shards: token t of shard t // (S/P)
+        seq_rows = lambda x, H, h0, idx: x.permute(1, 0, 2, 3, 4).reshape(S, -1, D)[idx, h0:h0 + H]
+        assert_close_tol(seq_rows(b.o_seq, hq, r * hq, ridx), o, f"fused rank{r} O")
+        assert_close_tol(seq_rows(b.dq_seq, hq, r * hq, ridx), dq, f"fused rank{r} dQ")
+        assert_close_tol(seq_rows(b.dk_seq, hkv, r * hkv, kidx), dk, f"fused rank{r} dK")
+        assert_close_tol(seq_rows(b.dv_seq, hkv, r * hkv, kidx), dv, f"fused rank{r} dV")
 
 
 def test_workload_parity_replicated_kv():

@@ -104,3 +104,16 @@ def test_wrapper_layout_equals_packed(row):
         assert bits_equal(want, got.contiguous())
     if dsink is not None:
         assert bits_equal(b.dsink, dsink)
+    # and directly against the oracle, read from the wrapper-layout storage
+    cu, n, mx = oracle.segments(oracle.gather_positions(seq_shards(inp.positions, P)))
+    okw = dict(sink=inp.sink, cu=cu if docs is not None else None, causal=causal, window_left=wl,
+               window_right=wr)
+    wo, _ = oracle.attn_fwd(inp.q, inp.k, inp.v, **okw)
+    wdq, wdk, wdv, wds = oracle.attn_bwd(inp.q, inp.k, inp.v, inp.dout, **okw)
+    shard = lambda x, H: seq_shards(x.reshape(B, S, H, D), P)
+    assert_close_tol(o, shard(wo, Hq), "wrapper O")
+    assert_close_tol(dq, shard(wdq, Hq), "wrapper dQ")
+    assert_close_tol(dk, shard(wdk, Hkv), "wrapper dK")
+    assert_close_tol(dv, shard(wdv, Hkv), "wrapper dV")
+    if dsink is not None:
+        assert_close_tol(dsink, wds, "wrapper dsink")

@@ -83,6 +83,8 @@ def load():
     lib.ulysses_attn_bwd_workspace_bytes.argtypes = [i32] * 5
     lib.ulysses_attn_bwd_workspace_bytes.restype = sz
     lib.ulysses_attn_bwd.argtypes = [vp] * 14 + [sz] + [i32] * 5 + [f32] + [i32] * 3 + [vp]
+    lib.ulysses_attn_bwd_status_offset.argtypes = [i32] * 5
+    lib.ulysses_attn_bwd_status_offset.restype = sz
     lib.ulysses_tiled_mlp_workspace_bytes.argtypes = [i32] * 4
     lib.ulysses_tiled_mlp_workspace_bytes.restype = sz
     lib.ulysses_tiled_mlp_fwd.argtypes = [vp] * 5 + [i32] * 4 + [vp, sz, vp]
@@ -342,11 +344,18 @@ def attn_fwd(q, k, v, *, sink=None, cu_seqlens=None, n_seqs=None, causal=True, w
     if workspace is None:
         need = attn_fwd_workspace_bytes(B, S, hq, hkv, D)
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    common = (float(softmax_scale), int(bool(causal)), int(window_left), int(window_right),
+              _stream(q.device))
+    if all(_is_head_layout(t) for t in (q, k, v, out)):  # the plain [B, S, h, D] entry point
+        _check(load().ulysses_attn_fwd(
+            _p(q), _p(k), _p(v), _p(out), _p(lse), _p(sink), _p(cu_seqlens), _p(n_seqs),
+            _p(workspace), ws_bytes, B, S, hq, hkv, D, *common), "ulysses_attn_fwd")
+        return out, lse
     _check(load().ulysses_attn_fwd_layout(
         _p(q), _p(k), _p(v), _p(out), _p(lse), _p(sink), _p(cu_seqlens), _p(n_seqs), _p(workspace),
-        0 if workspace is None else workspace.numel(), ctypes.byref(lq), ctypes.byref(lk), B, S, hq,
-        hkv, D, float(softmax_scale), int(bool(causal)), int(window_left), int(window_right),
-        _stream(q.device)), "ulysses_attn_fwd_layout")
+        ws_bytes, ctypes.byref(lq), ctypes.byref(lk), B, S, hq, hkv, D, *common),
+        "ulysses_attn_fwd_layout")
     return out, lse
 
 
@@ -414,6 +423,15 @@ def attn_bwd_workspace_bytes(B, S, hq, hkv, D) -> int:
     return int(load().ulysses_attn_bwd_workspace_bytes(B, S, hq, hkv, D))
 
 
+def attn_bwd_status(workspace: torch.Tensor, B, S, hq, hkv, D) -> torch.Tensor:
+    """The six int32 status words a backward call with these sizes left in
+    ``workspace`` (a device view; read it after the call on its stream): the
+    exponents of the power-of-two scales of the fp16 copies of dout, v, q and k,
+    the count of copied elements that saturated, and the count of inexact ones."""
+    off = int(load().ulysses_attn_bwd_status_offset(B, S, hq, hkv, D))
+    return workspace[off:off + 24].view(torch.int32)
+
+
 def attn_bwd(q, k, v, out, dout, lse, *, sink=None, cu_seqlens=None, n_seqs=None, causal=True,
              window_left=-1, window_right=-1, softmax_scale=None, dq=None, dk=None, dv=None,
              dsink=None, workspace=None, kv_grad_fp32=False):
@@ -444,12 +462,16 @@ def attn_bwd(q, k, v, out, dout, lse, *, sink=None, cu_seqlens=None, n_seqs=None
     need = attn_bwd_workspace_bytes(B, S, hq, hkv, D)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    fn = "ulysses_attn_bwd_layout_f32kv" if kv_grad_fp32 else "ulysses_attn_bwd_layout"
-    _check(getattr(load(), fn)(
-        _p(q), _p(k), _p(v), _p(out), _p(dout), _p(lse), _p(sink), _p(cu_seqlens), _p(n_seqs),
-        _p(dq), _p(dk), _p(dv), _p(dsink), _p(workspace), workspace.numel(), ctypes.byref(lq),
-        ctypes.byref(lk), B, S, hq, hkv, D, float(softmax_scale), int(bool(causal)),
-        int(window_left), int(window_right), _stream(q.device)), fn)
+    ptrs = (_p(q), _p(k), _p(v), _p(out), _p(dout), _p(lse), _p(sink), _p(cu_seqlens), _p(n_seqs),
+            _p(dq), _p(dk), _p(dv), _p(dsink), _p(workspace), workspace.numel())
+    common = (float(softmax_scale), int(bool(causal)), int(window_left), int(window_right),
+              _stream(q.device))
+    if not kv_grad_fp32 and all(_is_head_layout(t) for t in (q, k, v, out, dout, dq, dk, dv)):
+        _check(load().ulysses_attn_bwd(*ptrs, B, S, hq, hkv, D, *common), "ulysses_attn_bwd")
+    else:
+        fn = "ulysses_attn_bwd_layout_f32kv" if kv_grad_fp32 else "ulysses_attn_bwd_layout"
+        _check(getattr(load(), fn)(*ptrs, ctypes.byref(lq), ctypes.byref(lk), B, S, hq, hkv, D,
+                                   *common), fn)
     return dq, dk, dv, (dsink if sink is not None else None)
 
 

@@ -585,15 +585,29 @@ int ulysses_attn_merge_finish(const float* acc_out, const float* acc_lse, const 
                     "ulysses_attn_merge_finish launch");
 }
 
+// Backward workspace: delta, sum_j P dP, LSE*log2(e) (each [B][hq][S] fp32),
+// dsink partials [hq][parts], the status words (scale exponent, counts) and
+// the stats blocks' maxima, fp16 copies of q, dout ([B*S + kPad][hq][D]) and
+// k, v ([B*S + kPad][hkv][D]), then the split partials.
+constexpr size_t kStatusBytes = 256;
+static size_t bwd_status_offset(int B, int S, int hq) {
+  return 3 * align256((size_t)B * S * hq * sizeof(float)) +
+         align256((size_t)hq * kDsinkParts * sizeof(float));
+}
+static size_t bwd_copies_offset(int B, int S, int hq) {
+  return bwd_status_offset(B, S, hq) + kStatusBytes + align256((size_t)uly::kStatBlocks * uly::kStatFloats * sizeof(float));
+}
+
 size_t ulysses_attn_bwd_workspace_bytes(int B, int S, int hq, int hkv, int D) {
   if (B <= 0 || S <= 0 || hq <= 0 || hkv <= 0 || D <= 0) return 0;
-  // delta, sum_j P dP, LSE*log2(e) (each [B][hq][S] fp32), dsink partials [hq][parts],
-  // fp16 copies of q, dout ([B*S + kPad][hq][D]) and k, v ([B*S + kPad][hkv][D])
-  const size_t rows = align256((size_t)B * S * hq * sizeof(float));
   const size_t qsz = align256(((size_t)B * S + uly::kPad) * hq * D * 2),
                kvsz = align256(((size_t)B * S + uly::kPad) * hkv * D * 2);
-  return 3 * rows + align256((size_t)hq * kDsinkParts * sizeof(float)) + 2 * qsz + 2 * kvsz +
-         split_part_bytes(B, S, hq, hkv, D);
+  return bwd_copies_offset(B, S, hq) + 2 * qsz + 2 * kvsz + split_part_bytes(B, S, hq, hkv, D);
+}
+
+size_t ulysses_attn_bwd_status_offset(int B, int S, int hq, int hkv, int D) {
+  if (B <= 0 || S <= 0 || hq <= 0 || hkv <= 0 || D <= 0) return 0;
+  return bwd_status_offset(B, S, hq);
 }
 
 static int attn_bwd_impl(const void* q, const void* k, const void* v, const void* out,
@@ -636,7 +650,9 @@ static int attn_bwd_impl(const void* q, const void* k, const void* v, const void
   a.pdp = (float*)(ws + rows);
   a.lse2 = (float*)(ws + 2 * rows);
   a.dsink_part = (float*)(ws + 3 * rows);
-  char* h16 = ws + 3 * rows + align256((size_t)hq * kDsinkParts * sizeof(float));
+  a.bwd_status = (int*)(ws + bwd_status_offset(B, S, hq));
+  a.stat_part = (float*)(ws + bwd_status_offset(B, S, hq) + kStatusBytes);
+  char* h16 = ws + bwd_copies_offset(B, S, hq);
   const size_t qsz = align256(((size_t)B * S + uly::kPad) * hq * D * 2),
                kvsz = align256(((size_t)B * S + uly::kPad) * hkv * D * 2);
   a.q16 = (_Float16*)h16;

@@ -1,6 +1,6 @@
 // Attention backward of one Ulysses rank.
 //
-//   delta_i = sum_d dO_i,d O_i,d                         (attn_bwd_prep, stored negated)
+//   delta_i = sum_d dO_i,d O_i,d                         (attn_bwd_stats, stored negated)
 //   P_ij = exp(s_ij - LSE_i), dP_ij = dO_i . v_j, dS_ij = P_ij (dP_ij - delta_i)
 //   dK_j = scale sum_i dS_ij q_i, dV_j = sum_i P_ij dO_i  (attn_bwd_dkdv: one
 //          work-group owns 32*NW keys of one KV head and walks every query of
@@ -11,11 +11,12 @@
 //          with D_i = sum_j P_ij dP_ij accumulated by attn_bwd_dq: equal to
 //          dO_i . O_i for the exact O, not the bf16-rounded O delta_i uses
 // Both main kernels recompute P from LSE; neither uses atomics, so the
-// gradients are deterministic.  Their products run in fp16 on exact fp16
-// copies of q, k, v, dout (made here, in the workspace): P and dS are rounded
-// to fp16's 11 significant bits instead of bf16's 8 before the dV, dK and dQ
-// products, which keeps the gradients within the bf16-output tolerance even
-// where attention is concentrated on few keys.
+// gradients are deterministic.  Their products run in fp16 on fp16 copies of
+// q, k, v and dout * 2^e (made here, in the workspace; the power-of-two scale
+// below keeps dout and dS inside fp16's range whatever the gradients'
+// magnitude): P and dS are rounded to fp16's 11 significant bits instead of
+// bf16's 8 before the dV, dK and dQ products, which keeps the gradients within
+// the bf16-output tolerance even where attention is concentrated on few keys.
 #include <climits>
 
 #include "attn_common.hpp"
@@ -25,17 +26,202 @@ namespace uly {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// ------------------------------------------------------------- delta, dsink
+// ------------------------------------------- statistics, the copies' scales
+//
+// The products run in fp16, whose finite range is 2^-24 .. 65504: bf16
+// gradients far below 1 (a loss averaged over many tokens) would fall into
+// fp16's subnormals or flush to zero, and values beyond 65504 would
+// saturate.  So each copy is an exact power-of-two scaling of its tensor:
+// dout * 2^e, v * 2^c, q * 2^a, k * 2^b, with the integer exponents chosen on
+// the device such that every scaled value that becomes an fp16 operand stays
+// below 2^15 in magnitude:
+//   |q| 2^a, |k| 2^b, |dout| 2^e, |v| 2^c     (the copies themselves), and
+//   |dS_ij| 2^(e+c) = P_ij |dP_ij - delta_i| 2^(e+c)
+//              <= (max_i |dout_i| max_j |v_j| + max_i |delta_i|) 2^(e+c)
+// (Euclidean norms over the head dimension, Cauchy-Schwarz; 0 <= P <= 1).
+// a and b take the largest such value; e and c share the headroom the dS
+// bound leaves, each giving up half of what is missing.  All are clamped to
+// |x| <= kScaleExpMax.  Then S_ij comes out 2^(a+b) times larger (the softmax
+// scale absorbs it, so P is the very same), dP and dS 2^(e+c), dV 2^e, dK
+// 2^(e+c+a), dQ 2^(e+c+b), until the epilogues remove the factors with
+// v_ldexp_f32 (exact).  Each copy is checked element by element; elements
+// that saturated or are inexact are counted.
 
-// One 16-byte chunk of dO and O per thread, D/8 threads per (row, head);
-// `block` plays the role of the block index.
+constexpr float kF16Max = 65504.f;
+
+// The fp16 copy of two values (saturating at +-65504), counting those that
+// saturated (or are NaN) and those whose copy is not the value itself.
+__device__ __forceinline__ u32 f16_copy2(float x0, float x1, int& sat, int& inexact) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  const u32 h = pack_f16x2(clamp_f16(x0), clamp_f16(x1));
+  const f16x2 hv = __builtin_bit_cast(f16x2, h);
+  const bool s0 = !(fabsf(x0) <= kF16Max), s1 = !(fabsf(x1) <= kF16Max);
+  sat += (int)s0 + (int)s1;
+  inexact += (int)(!s0 && (float)hv[0] != x0) + (int)(!s1 && (float)hv[1] != x1);
+  return h;
+}
+
+// Adds the wave's counts to the status words (only when one is nonzero).
+__device__ __forceinline__ void add_counts(const AttnArgs& a, int sat, int inexact) {
+  if (!__any(sat | inexact)) return;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    sat += __shfl_xor(sat, off, 64);
+    inexact += __shfl_xor(inexact, off, 64);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    if (sat) atomicAdd(a.bwd_status + kCntSat, sat);
+    if (inexact) atomicAdd(a.bwd_status + kCntInexact, inexact);
+  }
+}
+
+constexpr int kStats = kStatFloats;  // per-block maxima (7 used)
+enum { kMaxDoutNorm2, kMaxDout, kMaxDelta, kMaxVNorm2, kMaxV, kMaxQ, kMaxK };
+
+// Per (row, head): delta = dO . O (bf16 O, fp32 sums; stored negated) and
+// LSE * log2(e).  Per block, over its share of the rows, the maxima listed
+// above: stat_part[block][kStats].  D/8 threads per row, one 16-byte chunk
+// each; blocks stride over the rows.
 template <int D>
-__device__ __forceinline__ void pre_block(const AttnArgs& a, int block) {
+__global__ __launch_bounds__(256) void attn_bwd_stats_kernel(AttnArgs a) {
+  constexpr int TPR = D / 8, RPB = 256 / TPR;
+  __shared__ float red[4][kStats];
+  const int c = threadIdx.x % TPR;
+  float m[kStats] = {};
+  const int rows = a.T * a.hq;
+  for (int r0 = blockIdx.x * RPB; r0 < rows; r0 += gridDim.x * RPB) {
+    const int row = r0 + threadIdx.x / TPR;  // row = t * hq + h
+    const bool valid = row < rows;
+    const int t = row / a.hq, hh = row - t * a.hq;
+    float acc = 0.f, n2 = 0.f;
+    if (valid) {
+      const int64_t src = row_of(a.mq, t) + (int64_t)hh * a.mq.head + 8 * c;
+      const u32x4 x = *reinterpret_cast<const u32x4*>(a.dout + src);
+      const u32x4 y = *reinterpret_cast<const u32x4*>(a.o + src);
+      const u32x4 z = *reinterpret_cast<const u32x4*>(a.q + src);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float x0 = bf16_lo(x[w]), x1 = bf16_hi(x[w]);
+        acc += x0 * bf16_lo(y[w]) + x1 * bf16_hi(y[w]);
+        n2 = __builtin_fmaf(x0, x0, __builtin_fmaf(x1, x1, n2));
+        m[kMaxDout] = fmaxf(m[kMaxDout], fmaxf(fabsf(x0), fabsf(x1)));
+        m[kMaxQ] = fmaxf(m[kMaxQ], fmaxf(fabsf(bf16_lo(z[w])), fabsf(bf16_hi(z[w]))));
+      }
+    }
+#pragma unroll
+    for (int off = TPR / 2; off > 0; off >>= 1) {
+      acc += __shfl_xor(acc, off, TPR);
+      n2 += __shfl_xor(n2, off, TPR);
+    }
+    if (valid && c == 0) {
+      const int idx = lse_index(a, t, hh);
+      a.ndelta[idx] = -acc;
+      const float l = a.lse[idx];
+      a.lse2[idx] = l == -INFINITY ? INFINITY : l * kLog2e;  // rows with no key: P = 0
+      m[kMaxDelta] = fmaxf(m[kMaxDelta], fabsf(acc));
+      m[kMaxDoutNorm2] = fmaxf(m[kMaxDoutNorm2], n2);
+    }
+  }
+  const int vrows = a.T * a.hkv;
+  for (int r0 = blockIdx.x * RPB; r0 < vrows; r0 += gridDim.x * RPB) {
+    const int row = r0 + threadIdx.x / TPR;  // row = t * hkv + g
+    const bool valid = row < vrows;
+    float n2 = 0.f;
+    if (valid) {
+      const int t = row / a.hkv, g = row - t * a.hkv;
+      const int64_t src = row_of(a.mk, t) + (int64_t)g * a.mk.head + 8 * c;
+      const u32x4 x = *reinterpret_cast<const u32x4*>(a.v + src);
+      const u32x4 z = *reinterpret_cast<const u32x4*>(a.k + src);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float x0 = bf16_lo(x[w]), x1 = bf16_hi(x[w]);
+        n2 = __builtin_fmaf(x0, x0, __builtin_fmaf(x1, x1, n2));
+        m[kMaxV] = fmaxf(m[kMaxV], fmaxf(fabsf(x0), fabsf(x1)));
+        m[kMaxK] = fmaxf(m[kMaxK], fmaxf(fabsf(bf16_lo(z[w])), fabsf(bf16_hi(z[w]))));
+      }
+    }
+#pragma unroll
+    for (int off = TPR / 2; off > 0; off >>= 1) n2 += __shfl_xor(n2, off, TPR);
+    if (valid && c == 0) m[kMaxVNorm2] = fmaxf(m[kMaxVNorm2], n2);
+  }
+#pragma unroll
+  for (int k = 0; k < kStats; ++k)
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m[k] = fmaxf(m[k], __shfl_xor(m[k], off, 64));
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0)
+#pragma unroll
+    for (int k = 0; k < kStats; ++k) red[wave][k] = m[k];
+  __syncthreads();
+  if (threadIdx.x < kStats) {
+    const int k = threadIdx.x;
+    a.stat_part[kStats * blockIdx.x + k] = fmaxf(fmaxf(red[0][k], red[1][k]), fmaxf(red[2][k], red[3][k]));
+  }
+}
+
+// The largest e with 2^e x < 2^15 for x = m 2^p (frexp, 0.5 <= m < 1):
+// e = 15 - p.  x = 0 leaves the scale free (0 here); inf or NaN: the lowest.
+__device__ __forceinline__ int exp_below_2p15(float x) {
+  if (!(x <= 3.0e38f)) return -kScaleExpMax;
+  if (x == 0.f) return 0;
+  int p;
+  frexpf(x, &p);
+  return 15 - p;
+}
+
+__device__ __forceinline__ int clamp_exp(int e) { return min(max(e, -kScaleExpMax), kScaleExpMax); }
+
+// One block: the maxima over the stats blocks, the four exponents, and zero
+// counts.
+__global__ __launch_bounds__(256) void attn_bwd_scale_kernel(AttnArgs a, int nparts) {
+  __shared__ float red[4][kStats];
+  float m[kStats] = {};
+  for (int i = threadIdx.x; i < nparts; i += 256)
+#pragma unroll
+    for (int k = 0; k < kStats; ++k) m[k] = fmaxf(m[k], a.stat_part[kStats * i + k]);
+#pragma unroll
+  for (int k = 0; k < kStats; ++k)
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m[k] = fmaxf(m[k], __shfl_xor(m[k], off, 64));
+  if ((threadIdx.x & 63) == 0)
+#pragma unroll
+    for (int k = 0; k < kStats; ++k) red[threadIdx.x >> 6][k] = m[k];
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int k = 0; k < kStats; ++k) m[k] = fmaxf(fmaxf(red[0][k], red[1][k]), fmaxf(red[2][k], red[3][k]));
+    // >= |dP - delta| for every pair
+    const float bound = sqrtf(m[kMaxDoutNorm2]) * sqrtf(m[kMaxVNorm2]) + m[kMaxDelta];
+    int e = exp_below_2p15(m[kMaxDout]), c = exp_below_2p15(m[kMaxV]);
+    if (bound != 0.f) {
+      const int room = exp_below_2p15(bound);  // e + c may not exceed it
+      const int over = e + c - room;
+      if (over > 0) {
+        e -= (over + 1) / 2;
+        c -= over / 2;
+      }
+    }
+    e = clamp_exp(e);
+    c = clamp_exp(c);
+    a.bwd_status[kExpDout] = e;
+    a.bwd_status[kExpV] = c;
+    a.bwd_status[kExpQ] = clamp_exp(exp_below_2p15(m[kMaxQ]));
+    a.bwd_status[kExpK] = clamp_exp(exp_below_2p15(m[kMaxK]));
+    a.bwd_status[kCntSat] = 0;
+    a.bwd_status[kCntInexact] = 0;
+  }
+}
+
+// The fp16 copy of dout * 2^e for one 16-byte chunk per thread (D/8 threads
+// per (row, head)), and delta scaled by 2^(e+c); `block` plays the role of
+// the block index.  Rows T .. T + kPad - 1 of the copy are zero.
+template <int D>
+__device__ __forceinline__ void dout_block(const AttnArgs& a, int block, int e) {
   constexpr int TPR = D / 8;  // threads per row
   const int row = block * (256 / TPR) + threadIdx.x / TPR;  // row = t * hq + h
   const int c = threadIdx.x % TPR;
-  float acc = 0.f;
   const bool valid = row < a.T * a.hq;
+  int sat = 0, inexact = 0;
   if (!valid && row < (a.T + kPad) * a.hq) {  // the zero rows after the last token
     const u32x4 z = {0, 0, 0, 0};
     *reinterpret_cast<u32x4*>(a.do16 + (int64_t)row * D + 8 * c) = z;
@@ -44,34 +230,30 @@ __device__ __forceinline__ void pre_block(const AttnArgs& a, int block) {
     const int t = row / a.hq, hh = row - t * a.hq;
     const int64_t src = row_of(a.mq, t) + (int64_t)hh * a.mq.head + 8 * c;
     const u32x4 x = *reinterpret_cast<const u32x4*>(a.dout + src);
-    const u32x4 y = *reinterpret_cast<const u32x4*>(a.o + src);
     u32x4 h;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      acc += bf16_lo(x[w]) * bf16_lo(y[w]) + bf16_hi(x[w]) * bf16_hi(y[w]);
-      h[w] = pack_f16x2(clamp_f16(bf16_lo(x[w])), clamp_f16(bf16_hi(x[w])));
-    }
+    for (int w = 0; w < 4; ++w)
+      h[w] = f16_copy2(ldexpf(bf16_lo(x[w]), e), ldexpf(bf16_hi(x[w]), e), sat, inexact);
     *reinterpret_cast<u32x4*>(a.do16 + (int64_t)row * D + 8 * c) = h;
+    if (c == 0) {  // delta joins dP = dO V, which carries 2^(e+c)
+      const int idx = lse_index(a, t, hh);
+      a.ndelta[idx] = ldexpf(a.ndelta[idx], e + a.bwd_status[kExpV]);
+    }
   }
-#pragma unroll
-  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, TPR);
-  if (valid && c == 0) {
-    const int t = row / a.hq, h = row - t * a.hq;
-    const int idx = lse_index(a, t, h);
-    a.ndelta[idx] = -acc;
-    const float l = a.lse[idx];
-    a.lse2[idx] = l == -INFINITY ? INFINITY : l * kLog2e;  // rows with no key: P = 0
-  }
+  add_counts(a, sat, inexact);
 }
 
-// Exact fp16 copy, in the head layout [T][H][D], of a bf16 tensor laid out
-// as `m` says: every bf16 value of magnitude <= 65504 is an fp16 value (fp16
-// keeps 11 significant bits, bf16 8); larger magnitudes saturate, values below
-// 2^-14 round to fp16's subnormals.  One 16-byte chunk per thread; hd8 = H*D/8.
-// Elements n .. n_pad - 1 (the kPad rows after the last token) are zero.
-__device__ __forceinline__ void f16_block(const __bf16* src, const RowMap& m, FastDiv hd8, FastDiv d8,
-                                          _Float16* dst, int64_t n, int64_t n_pad, int block) {
+// The fp16 copy times 2^ex, in the head layout [T][H][D], of a bf16 tensor
+// laid out as `m` says: exact for every scaled value with 2^-17 <= |x| <=
+// 65504 (fp16 keeps 11 significant bits, bf16 8); larger magnitudes saturate,
+// smaller ones round to a multiple of 2^-24 (both counted).  One 16-byte
+// chunk per thread; hd8 = H*D/8.  Elements n .. n_pad - 1 (the kPad rows
+// after the last token) are zero.
+__device__ __forceinline__ void f16_block(const AttnArgs& a, const __bf16* src, const RowMap& m,
+                                          FastDiv hd8, FastDiv d8, _Float16* dst, int64_t n,
+                                          int64_t n_pad, int block, int ex) {
   const int64_t i = ((int64_t)block * 256 + threadIdx.x) * 8;
+  int sat = 0, inexact = 0;
   if (i >= n && i < n_pad) {
     const u32x4 z = {0, 0, 0, 0};
     *reinterpret_cast<u32x4*>(dst + i) = z;
@@ -83,14 +265,16 @@ __device__ __forceinline__ void f16_block(const __bf16* src, const RowMap& m, Fa
     const u32x4 x = *reinterpret_cast<const u32x4*>(src + row_of(m, (int)t) + (int64_t)hh * m.head + 8 * c);
     u32x4 h;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) h[w] = pack_f16x2(clamp_f16(bf16_lo(x[w])), clamp_f16(bf16_hi(x[w])));
+    for (int w = 0; w < 4; ++w)
+      h[w] = f16_copy2(ldexpf(bf16_lo(x[w]), ex), ldexpf(bf16_hi(x[w]), ex), sat, inexact);
     *reinterpret_cast<u32x4*>(dst + i) = h;
   }
+  add_counts(a, sat, inexact);
 }
 
-// The backward's preparation in one launch: blocks [0, nb_pre) compute delta,
-// LSE*log2(e) and the fp16 dO (pre_block); the next ones make the fp16
-// copies of q, then k, then v (f16_block).
+// The backward's copies in one launch: blocks [0, nb_pre) make the fp16
+// dout * 2^e and scale delta (dout_block); the next ones make the fp16
+// copies of q * 2^a, then k * 2^b, then v * 2^c (f16_block).
 struct PrepArgs {
   int nb_pre, nb_q, nb_kv;
   FastDiv d8, q8, k8;
@@ -101,20 +285,20 @@ template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(AttnArgs a, PrepArgs p) {
   int b = blockIdx.x;
   if (b < p.nb_pre) {
-    pre_block<D>(a, b);
+    dout_block<D>(a, b, a.bwd_status[kExpDout]);
     return;
   }
   b -= p.nb_pre;
   if (b < p.nb_q) {
-    f16_block(a.q, a.mq, p.q8, p.d8, a.q16, p.nq, p.pq, b);
+    f16_block(a, a.q, a.mq, p.q8, p.d8, a.q16, p.nq, p.pq, b, a.bwd_status[kExpQ]);
     return;
   }
   b -= p.nb_q;
   if (b < p.nb_kv) {
-    f16_block(a.k, a.mk, p.k8, p.d8, a.k16, p.nkv, p.pkv, b);
+    f16_block(a, a.k, a.mk, p.k8, p.d8, a.k16, p.nkv, p.pkv, b, a.bwd_status[kExpK]);
     return;
   }
-  f16_block(a.v, a.mk, p.k8, p.d8, a.v16, p.nkv, p.pkv, b - p.nb_kv);
+  f16_block(a, a.v, a.mk, p.k8, p.d8, a.v16, p.nkv, p.pkv, b - p.nb_kv, a.bwd_status[kExpV]);
 }
 
 // Per head, n_part partial sums of -exp(sink - LSE_i) delta_i over the rows.
@@ -162,6 +346,8 @@ struct BoolC {
 
 template <int D, int NW, int SINK>
 __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(AttnArgs a) {
+  // S from the copies q 2^a and k 2^b: the scale absorbs 2^-(a+b), exactly
+  a.scale_log2 = ldexpf(a.scale_log2, -(a.bwd_status[kExpQ] + a.bwd_status[kExpK]));
   constexpr int BM = 32 * NW, NB = D / 32, KS = D / 16;
   constexpr int TILE = kBK * D * 2;
   constexpr int STAGE = 2 * TILE;  // K, then V
@@ -306,8 +492,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(AttnArgs a) {
     if (it + 1 < it_hi) step(it + 1, stage1, stage0);
   }
 
-  pdp = halves_sum(pdp);
-  if (a.nsplit > 1) {  // fp32 partials, summed by dq_reduce_kernel
+  // P dP carries 2^(e+c), dQ 2^(e+c+b) (removed here, exactly)
+  const int edp = a.bwd_status[kExpDout] + a.bwd_status[kExpV], es = edp + a.bwd_status[kExpK];
+  pdp = ldexpf(halves_sum(pdp), -edp);
+  if (a.nsplit > 1) {  // fp32 partials (still scaled by 2^e), summed by dq_reduce_kernel
     if (qvalid && want_pdp && hf == 0)
       a.part_pdp[(int64_t)blockIdx.y * a.T * a.hq + lse_index(a, qrow, h)] = pdp;
     if (qvalid) {
@@ -331,8 +519,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         u32x2 w;
-        w[0] = pack_bf16x2(dqacc[nb][4 * i + 0] * a.scale, dqacc[nb][4 * i + 1] * a.scale);
-        w[1] = pack_bf16x2(dqacc[nb][4 * i + 2] * a.scale, dqacc[nb][4 * i + 3] * a.scale);
+        w[0] = pack_bf16x2(ldexpf(dqacc[nb][4 * i + 0] * a.scale, -es),
+                           ldexpf(dqacc[nb][4 * i + 1] * a.scale, -es));
+        w[1] = pack_bf16x2(ldexpf(dqacc[nb][4 * i + 2] * a.scale, -es),
+                           ldexpf(dqacc[nb][4 * i + 3] * a.scale, -es));
         *reinterpret_cast<u32x2*>(row + 32 * nb + 8 * i + 4 * hf) = w;
       }
   }
@@ -345,17 +535,18 @@ template __global__ void attn_bwd_dq_kernel<128, 4, 1>(AttnArgs);
 template __global__ void attn_bwd_dq_kernel<64, 4, 0>(AttnArgs);
 template __global__ void attn_bwd_dq_kernel<64, 4, 1>(AttnArgs);
 
-// dQ = scale * sum of the split partials (fixed order), to bf16; the same for
-// the rows' sum of P dP.
+// dQ = scale * 2^-(e+c+b) * the sum of the split partials (fixed order), to
+// bf16; the same sum for the rows' P dP (its parts already unscaled).
 template <int D>
 __global__ __launch_bounds__(256) void dq_reduce_kernel(AttnArgs a, int64_t n) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i < n) {
+    const int es = a.bwd_status[kExpDout] + a.bwd_status[kExpV] + a.bwd_status[kExpK];
     f32x4 q = {0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < a.nsplit; ++s) q += *reinterpret_cast<const f32x4*>(a.part + s * n + i);
     u32x2 w;
-    w[0] = pack_bf16x2(q[0] * a.scale, q[1] * a.scale);
-    w[1] = pack_bf16x2(q[2] * a.scale, q[3] * a.scale);
+    w[0] = pack_bf16x2(ldexpf(q[0] * a.scale, -es), ldexpf(q[1] * a.scale, -es));
+    w[1] = pack_bf16x2(ldexpf(q[2] * a.scale, -es), ldexpf(q[3] * a.scale, -es));
     const int rr = (int)(i / D), t = rr / a.hq, h = rr - t * a.hq;  // row rr = t * hq + h
     *reinterpret_cast<u32x2*>(a.out + row_of(a.mq, t) + (int64_t)h * a.mq.head + (i - (int64_t)rr * D)) = w;
   }
@@ -373,6 +564,14 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(AttnArgs a, int64_t n) {
 template <int D, int NW>
 static hipError_t launch_bwd_t(const AttnArgs& args, hipStream_t st) {
   AttnArgs a = args;
+  {
+    ProfScope prof("attn_bwd_stats", st);
+    constexpr int rpb = 256 / (D / 8);
+    const long need = ((long)a.T * (a.hq > a.hkv ? a.hq : a.hkv) + rpb - 1) / rpb;
+    const int nb = (int)(need < kStatBlocks ? (need > 0 ? need : 1) : kStatBlocks);
+    hipLaunchKernelGGL(attn_bwd_stats_kernel<D>, dim3(nb), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(attn_bwd_scale_kernel, dim3(1), dim3(256), 0, st, a, nb);
+  }
   {
     ProfScope prof("attn_bwd_prep", st);
     PrepArgs p;

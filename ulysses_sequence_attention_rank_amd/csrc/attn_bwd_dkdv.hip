@@ -145,6 +145,8 @@ __device__ __forceinline__ int dkdv_tile_units(const AttnArgs& a, int kt) {
 template <int D, int KG, bool BAL>
 __global__ __launch_bounds__(KG * 128) void attn_bwd_dkdv_kernel(AttnArgs a) {
   constexpr int NW = 2 * KG, BN = 32 * KG, NB = D / 32;
+  // S from the copies q 2^a and k 2^b: the scale absorbs 2^-(a+b), exactly
+  a.scale_log2 = ldexpf(a.scale_log2, -(a.bwd_status[kExpQ] + a.bwd_status[kExpK]));
   static_assert(NW >= 2, "two waves stage the per-row statistics");
   typedef DkdvSmem<D, KG> SM;
   __shared__ __attribute__((aligned(1024))) char kvs[2 * SM::kKV];
@@ -280,7 +282,7 @@ __global__ __launch_bounds__(KG * 128) void attn_bwd_dkdv_kernel(AttnArgs a) {
     }
 
   // dK, dV: lane holds column d = 32 nb + l % 32 of key rows 8 i + 4 hf + j
-  if (BAL && slot >= 0) {  // this part, unscaled: slot [2][BN][D] (dK, then dV)
+  if (BAL && slot >= 0) {  // this part, as accumulated: slot [2][BN][D] (dK, then dV)
     float* sk = a.part + (int64_t)slot * 2 * BN * D;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -294,6 +296,8 @@ __global__ __launch_bounds__(KG * 128) void attn_bwd_dkdv_kernel(AttnArgs a) {
     }
     return;
   }
+  // dV carries 2^e, dK 2^(e+c+a) (removed here, exactly)
+  const int ev = a.bwd_status[kExpDout], es = ev + a.bwd_status[kExpV] + a.bwd_status[kExpQ];
   const int64_t plane = (int64_t)a.T * a.hkv * D;
   float* pk = a.part + blockIdx.y * plane;
   float* pv = a.part + (a.nsplit + blockIdx.y) * plane;
@@ -316,14 +320,14 @@ __global__ __launch_bounds__(KG * 128) void attn_bwd_dkdv_kernel(AttnArgs a) {
     if (a.dkv_f32) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        reinterpret_cast<float*>(a.dk)[off + 32 * nb] = dkacc[nb][e] * a.scale;
-        reinterpret_cast<float*>(a.dv)[off + 32 * nb] = dvacc[nb][e];
+        reinterpret_cast<float*>(a.dk)[off + 32 * nb] = ldexpf(dkacc[nb][e] * a.scale, -es);
+        reinterpret_cast<float*>(a.dv)[off + 32 * nb] = ldexpf(dvacc[nb][e], -ev);
       }
     } else {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        a.dk[off + 32 * nb] = (__bf16)(dkacc[nb][e] * a.scale);
-        a.dv[off + 32 * nb] = (__bf16)dvacc[nb][e];
+        a.dk[off + 32 * nb] = (__bf16)ldexpf(dkacc[nb][e] * a.scale, -es);
+        a.dv[off + 32 * nb] = (__bf16)ldexpf(dvacc[nb][e], -ev);
       }
     }
   }
@@ -355,6 +359,30 @@ __global__ __launch_bounds__(KG * 128) void attn_bwd_dkdv_kernel(AttnArgs a) {
   }
 }
 
+// dK = scale * 2^-(e+c+a) * k and dV = 2^-e * v (the sums of an item's
+// parts, which carry those factors from the copies' scales), four
+// consecutive columns at element offset `off`, to bf16 (or fp32).
+__device__ __forceinline__ void store_dkdv4(const AttnArgs& a, int64_t off, f32x4 k, f32x4 v) {
+  const int ev = a.bwd_status[kExpDout], es = ev + a.bwd_status[kExpV] + a.bwd_status[kExpQ];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    k[c] = ldexpf(k[c] * a.scale, -es);
+    v[c] = ldexpf(v[c], -ev);
+  }
+  if (a.dkv_f32) {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.dk) + off) = k;
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.dv) + off) = v;
+    return;
+  }
+  u32x2 wk, wv;
+  wk[0] = pack_bf16x2(k[0], k[1]);
+  wk[1] = pack_bf16x2(k[2], k[3]);
+  wv[0] = pack_bf16x2(v[0], v[1]);
+  wv[1] = pack_bf16x2(v[2], v[3]);
+  *reinterpret_cast<u32x2*>(a.dk + off) = wk;
+  *reinterpret_cast<u32x2*>(a.dv + off) = wv;
+}
+
 // dK = scale * sum of the split partials, dV = sum (fixed order), to bf16
 // (or fp32).
 template <int D>
@@ -368,18 +396,7 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(AttnArgs a, int64_t n)
   }
   const int rr = (int)(i / D), t = rr / a.hkv, g = rr - t * a.hkv;  // row rr = t * hkv + g
   const int64_t off = row_of(a.mk, t) + (int64_t)g * a.mk.head + (i - (int64_t)rr * D);
-  if (a.dkv_f32) {
-    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.dk) + off) = k * a.scale;
-    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.dv) + off) = v;
-    return;
-  }
-  u32x2 wk, wv;
-  wk[0] = pack_bf16x2(k[0] * a.scale, k[1] * a.scale);
-  wk[1] = pack_bf16x2(k[2] * a.scale, k[3] * a.scale);
-  wv[0] = pack_bf16x2(v[0], v[1]);
-  wv[1] = pack_bf16x2(v[2], v[3]);
-  *reinterpret_cast<u32x2*>(a.dk + off) = wk;
-  *reinterpret_cast<u32x2*>(a.dv + off) = wv;
+  store_dkdv4(a, off, k, v);
 }
 
 // dK = scale * the sum of the parts of a balanced schedule's items, dV = the
@@ -401,18 +418,7 @@ __global__ __launch_bounds__(256) void dkdv_reduce_bal_kernel(AttnArgs a, int64_
     v += *reinterpret_cast<const f32x4*>(p + BN * D);
   }
   const int64_t off = row_of(a.mk, t) + (int64_t)g * a.mk.head + c;
-  if (a.dkv_f32) {
-    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.dk) + off) = k * a.scale;
-    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.dv) + off) = v;
-    return;
-  }
-  u32x2 wk, wv;
-  wk[0] = pack_bf16x2(k[0] * a.scale, k[1] * a.scale);
-  wk[1] = pack_bf16x2(k[2] * a.scale, k[3] * a.scale);
-  wv[0] = pack_bf16x2(v[0], v[1]);
-  wv[1] = pack_bf16x2(v[2], v[3]);
-  *reinterpret_cast<u32x2*>(a.dk + off) = wk;
-  *reinterpret_cast<u32x2*>(a.dv + off) = wv;
+  store_dkdv4(a, off, k, v);
 }
 
 // Explicit instantiations: with two launches of one kernel template in an

@@ -68,6 +68,13 @@ struct AttnArgs {
   _Float16* k16;
   _Float16* v16;
   _Float16* do16;
+  // bwd: [0] the exponent e of the power-of-two scale 2^e of the fp16 dout
+  // copy (every gradient is 2^e times the true one until its epilogue),
+  // [1] and [2] the counts of q, k, v, dout*2^e elements whose fp16 copy
+  // saturated or is inexact; stat_part: per-block maxima behind the choice of
+  // e ([kStatBlocks][4])
+  int* bwd_status;
+  float* stat_part;
   const float* sink;
   float* dsink_part;  // [hq][n_part]
   float* dsink;

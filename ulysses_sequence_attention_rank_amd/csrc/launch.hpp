@@ -117,6 +117,15 @@ inline int fwd_block_rows(int B, int S, int hq, int D) {
   return (long)(((long)B * S + 255) / 256) * hq >= 512 ? 256 : 128;
 }
 
+// The backward's power-of-two scales of its fp16 copies (attn_bwd.hip):
+// kStatFloats per-block maxima from kStatBlocks blocks at most; exponents
+// clamped to [-kScaleExpMax, kScaleExpMax].  The status words: the exponents
+// of dout, v, q, k, then the counts of saturated and of inexact copies.
+constexpr int kStatBlocks = 1024;
+constexpr int kStatFloats = 8;
+constexpr int kScaleExpMax = 100;
+enum { kExpDout = 0, kExpV = 1, kExpQ = 2, kExpK = 3, kCntSat = 4, kCntInexact = 5 };
+
 // When profiling is on, prof_mark(name, st) records a HIP event on `st`
 // before a kernel launch and prof_mark(nullptr, st) after it.
 void prof_mark(const char* name, hipStream_t st);
