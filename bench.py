@@ -28,7 +28,7 @@ if ROOT not in sys.path:
 METRIC = "attn fwd+bwd TFLOP/s per rank share (% bf16 MFMA peak); a2a pack GB/s"
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E
-DEFAULT_WORKLOAD = 2         # S=4096, 12 heads, D=128, full + causal layers, P=2
+DEFAULT_WORKLOAD = 5         # S=131072 causal, GQA 28/4, D=128, P=4 (the largest)
 
 
 PROFILES = os.path.join(ROOT, "profiles")
@@ -114,15 +114,24 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD, choices=[1, 2, 3, 4, 5, 6],
-                    help="which of the five simulated workloads (default: the S=4096 one)")
+                    help="which of the five simulated workloads (default: the S=131072 one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mlp", action="store_true", help="skip the sequence-tiled MLP measurement")
     ap.add_argument("--cpu-heads", type=int, default=None,
                     help="query heads of rank 0 the CPU oracle baseline runs (default: all of "
                          "rank 0's heads, every layer, for the S<=4096 workloads; one KV group of "
                          "rank 0 for the S=32768 ones; none for the larger ones)")
+    ap.add_argument("--cpu-rows", type=int, default=1024,
+                    help="S > 32768: query rows (stratified) of the CPU oracle's subset baseline")
+    ap.add_argument("--cpu-keys", type=int, default=1024,
+                    help="S > 32768: last keys whose dK/dV the CPU oracle's subset baseline computes")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches instead of a captured HIP graph of the step")
+    ap.add_argument("--layer", default=None,
+                    help="run only this layer type of the workload (e.g. swa128)")
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="for counter collection: warm-up and --steps eager steps only, no other "
+                         "measurement; prints a short JSON line")
     ap.add_argument("--rocprof-summary", metavar="DIR",
                     help="no GPU run: summarise rocprofv3 CSV output under DIR (trace/, sq/, "
                          "fetch/, write/ and commands.txt) of a run of this script on --workload "
@@ -150,6 +159,12 @@ def main():
     uly.load()
 
     case = CONFIGS[args.workload]
+    if args.layer is not None:
+        import dataclasses
+        keep = tuple(v for v in case.variants if v.name == args.layer)
+        if not keep:
+            raise SystemExit(f"workload {case.name} has no layer {args.layer!r}")
+        case = dataclasses.replace(case, variants=keep)
     log(f"workload {args.workload} {case.name}: generating inputs")
     inp = make_inputs(case)
     dev = torch.device("cuda", 0)
@@ -168,6 +183,14 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.profile_pass:
+        log(f"profile pass: {args.steps} eager steps")
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_pass": case.name, "layers": [v.name for v in case.variants],
+                          "steps": args.steps}), flush=True)
+        return
 
     # The whole step is captured once into a HIP graph and replayed: about 50
     # kernel launches per step, many of them a few microseconds long, so
@@ -218,18 +241,26 @@ def main():
     fused_ms = 1e3 * (time.perf_counter() - t0) / args.steps
     del fgraph
 
-    # per-kernel durations: the same steps launched eagerly, each kernel
-    # bracketed by HIP events on the stream it runs on
-    log(f"per-kernel timing over {args.steps} eager steps")
-    uly.profile_start(max_launches=64 * args.steps * len(case.variants) * P + 64)
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    uly.profile_stop()
-    kern = uly.profile_report()
+    # per-kernel durations: the same steps launched eagerly, one layer type at
+    # a time, each kernel bracketed by HIP events on the stream it runs on
+    kern_layer = {}
+    for v in case.variants:
+        log(f"per-kernel timing over {args.steps} eager steps of the {v.name} layer")
+        uly.profile_start(max_launches=64 * args.steps * P + 64)
+        for _ in range(args.steps):
+            sim.step(b, causal=v.causal, window_left=v.window_left, window_right=v.window_right)
+        torch.cuda.synchronize()
+        uly.profile_stop()
+        kern_layer[v.name] = uly.profile_report()
+    kern = {}
+    for rep in kern_layer.values():
+        for name, (cnt, tot, mn, mx) in rep.items():
+            c0 = kern.get(name, (0, 0.0, float("inf"), 0.0))
+            kern[name] = (c0[0] + cnt, c0[1] + tot, min(c0[2], mn), max(c0[3], mx))
 
     docs = docs_of(inp)
     credit = kernel_credit(case, docs)
+    layers = layer_figures(case, credit, kern_layer, args.steps)
     step_flops = sum(12 * case.D * credit[v.name]["pairs"] for v in case.variants) * P
     value = step_flops / (ms_per_step * 1e-3) / 1e12
 
@@ -293,6 +324,8 @@ def main():
             cpu = cpu_baseline(inp, ranks=[0], n_heads=case.Hq // P)
         elif case.S <= 32768:
             cpu = cpu_baseline(inp, ranks=[0], n_heads=case.Hq // case.Hkv)
+        else:
+            cpu = cpu_baseline_subset(inp, n_rows=args.cpu_rows, n_keys=args.cpu_keys)
 
     line = {
         "metric": METRIC,
@@ -306,6 +339,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
+        "precision": ("bf16 inputs and outputs; forward products bf16 MFMA, backward products fp16 "
+                      "MFMA on exact power-of-two-scaled fp16 copies; fp32 accumulation"),
         "data": "synthetic",
         "config": {"workload": case.name, "P": P, "B": case.B, "S": case.S, "Hq": case.Hq,
                    "Hkv": case.Hkv, "D": case.D, "layers": [v.name for v in case.variants],
@@ -321,6 +356,7 @@ def main():
         "pack_frac_of_hbm": round(perm["pack_gbps"] / PEAK_HBM_GBPS, 4),
         "unpack_gbps": perm["unpack_gbps"],
         "permutation": perm,
+        "layers": layers,
         "kernels": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in r.items()}
                     for k, r in rows.items()},
         "ring_inner_step": ring,
@@ -329,6 +365,41 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+ATTN_KERNELS = ("attn_fwd", "attn_fwd_merge", "attn_bwd_stats", "attn_bwd_prep", "attn_bwd_dkdv",
+                "attn_bwd_dkdv_reduce", "attn_bwd_dq", "attn_bwd_dq_reduce", "attn_bwd_dsink")
+
+
+def layer_figures(case, credit, kern_layer, steps):
+    """Per layer type: the attention kernels' time per rank call (forward and
+    backward, every launch of the attention calls), the credited TFLOP/s, and
+    for a sliding-window layer, whose arithmetic intensity is below the ridge,
+    the compulsory HBM bytes against the 8 TB/s peak: each rank call must read
+    q, k, v and write O and LSE (forward), read q, k, v, O, dO, LSE and write
+    dQ, dK, dV (backward)."""
+    P, B, S, D, hq, hkv = case.P, case.B, case.S, case.D, case.hq, case.hkv
+    qb, kvb, lseb = B * S * hq * D * 2, B * S * hkv * D * 2, B * S * hq * 4
+    out = {}
+    for v in case.variants:
+        rep = kern_layer[v.name]
+        calls = P * steps
+        attn_ms = sum(t for k, (c, t, _, _) in rep.items() if k in ATTN_KERNELS) / calls
+        fl = 12 * D * credit[v.name]["pairs"]
+        rec = {"ms_per_rank": round(attn_ms, 5),
+               "tflops": round(fl / (attn_ms * 1e-3) / 1e12, 2),
+               "frac_of_mfma_peak": round(fl / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+               "kernels_ms_per_rank": {k: round(t / calls, 5) for k, (c, t, _, _) in rep.items()
+                                       if k in ATTN_KERNELS}}
+        if v.window_left >= 0 or v.window_right >= 0:
+            hbm = (qb + 2 * kvb + qb + lseb) + (qb + 2 * kvb + 2 * qb + lseb + qb + 2 * kvb)
+            gbps = hbm / (attn_ms * 1e-3) / 1e9
+            rec["hbm"] = {"bound": "hbm", "bytes_per_rank": hbm, "floor_ms": round(hbm / 8e12 * 1e3, 5),
+                          "achieved_gbps": round(gbps, 1), "peak_gbps": PEAK_HBM_GBPS,
+                          "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                          "flop_per_byte": round(fl / hbm, 1)}
+        out[v.name] = rec
+    return out
 
 
 def measure_permutation(case, b, dev, launches=40):
@@ -498,12 +569,52 @@ def _rocprof_name(full):
     return name
 
 
+def alg_bytes_per_launch(case, kernel):
+    """Compulsory HBM bytes of one launch of `kernel` on `case` (per rank call
+    for the attention kernels; per launch averaged over the step's launches for
+    the permutation): every operand read once and every result written once.
+    None for kernels without a stated figure."""
+    B, S, D, hq, hkv, P = case.B, case.S, case.D, case.hq, case.hkv, case.P
+    qb, kvb, lseb = B * S * hq * D * 2, B * S * hkv * D * 2, B * S * hq * 4
+    eq, ekv = B * S * case.Hq * D * 2, B * S * case.Hkv * D * 2
+    return {
+        # forward: q, k, v in; O, LSE out
+        "attn_fwd": qb + 2 * kvb + qb + lseb,
+        # fp16 copies of q, dO, k, v and LSE*log2e, -delta in; dK, dV out
+        "attn_bwd_dkdv": 2 * qb + 2 * kvb + 2 * lseb + 2 * kvb,
+        # the same in; dQ out
+        "attn_bwd_dq": 2 * qb + 2 * kvb + 2 * lseb + qb,
+        # dout, O, q, k, v, LSE in; -delta, LSE*log2e out
+        "attn_bwd_stats": 3 * qb + 2 * kvb + 3 * lseb,
+        # q, k, v, dout in, their fp16 copies out; -delta rescaled in place
+        "attn_bwd_prep": 2 * (2 * qb + 2 * kvb) + 2 * lseb,
+        # Q, K, V in one launch, then dO: each element read and written once
+        "a2a_pack": (2 * (eq + 2 * ekv) + 2 * eq) // 2 if case.Hkv >= P else None,
+        # O, then dQ, dK, dV in one launch
+        "a2a_unpack": (2 * eq + 2 * (eq + 2 * ekv)) // 2 if case.Hkv >= P else None,
+    }.get(kernel)
+
+
+PEAK_CLOCK_GHZ = 2.4
+SIMDS = 1024  # 256 CUs x 4 SIMDs
+
+
 def rocprof_summary(d, workload):
-    """Write profiles/<workload>_kernels.md from rocprofv3 CSV files and record
-    per-launch HBM traffic in profiles/traffic.json."""
+    """Write profiles/<workload>_kernels.md from rocprofv3 CSV files under d and
+    record per-launch HBM traffic in profiles/traffic.json.
+
+    d/trace: --kernel-trace --stats of the benchmark command; d/<layer>/sq,
+    d/<layer>/fetch, d/<layer>/write: counter passes of `--profile-pass
+    --layer <layer>` runs (one layer type each); d/commands.txt: the commands.
+    Per kernel: executed MFMA utilisation = SQ_VALU_MFMA_BUSY_CYCLES / (1024
+    SIMDs x cycles), at the nominal 2.4 GHz over the traced duration and at the
+    clock the kernel ran at (GRBM_GUI_ACTIVE cycles over the dispatch);
+    VALU and MFMA instructions; HBM bytes (FETCH_SIZE, WRITE_SIZE scaled by the
+    pack kernel's known bytes), GB/s, and their ratio to the compulsory bytes."""
     import collections
     import csv
     import glob
+    import re
     from ulysses_inputs import CONFIGS
     case = CONFIGS[workload]
 
@@ -520,16 +631,10 @@ def rocprof_summary(d, workload):
             agg[_rocprof_name(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
         return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in agg.items()}
 
-    stats = rows("trace", "kernel_stats.csv")
-    sq, fe, wr = counters("sq"), counters("fetch"), counters("write")
-    with open(os.path.join(d, "commands.txt")) as f:
-        commands = [ln.rstrip() for ln in f if ln.strip()]
-
     # scale factors: every thread of the pack kernel reads and writes
     # kPermUnroll 16-byte vectors (grids are a whole number of blocks for
     # these shapes), so a dispatch moves Grid_Size * 16 * kPermUnroll bytes
     # each way; the constant is read from the kernel's source
-    import re
     with open(os.path.join(ROOT, "ulysses_sequence_attention_rank_amd", "csrc", "permute.hip")) as f:
         m = re.search(r"constexpr int kPermUnroll = (\d+);", f.read())
     if m is None:
@@ -543,16 +648,35 @@ def rocprof_summary(d, workload):
                 known += float(r["Grid_Size"]) * pack_thread_bytes
                 got += float(r["Counter_Value"]) * 1024
         return known / got
-    f_scale, w_scale = pack_scale("fetch", "FETCH_SIZE"), pack_scale("write", "WRITE_SIZE")
-    pack_bytes = None
 
-    traffic = {}
-    for k in sorted(k for k in fe if not k.startswith("torch")):
-        if k in wr:
-            traffic[k] = {"fetch_kib": round(fe[k]["FETCH_SIZE"], 1),
-                          "write_kib": round(wr[k]["WRITE_SIZE"], 1),
-                          "bytes_per_launch": round(1024 * (fe[k]["FETCH_SIZE"] * f_scale +
-                                                            wr[k]["WRITE_SIZE"] * w_scale))}
+    stats = rows("trace", "kernel_stats.csv")
+    avg_us = {}
+    for r in stats:
+        avg_us.setdefault(_rocprof_name(r["Name"]), float(r["AverageNs"]) / 1e3)
+    with open(os.path.join(d, "commands.txt")) as f:
+        commands = [ln.rstrip() for ln in f if ln.strip()]
+
+    per_layer = {}
+    for v in case.variants:
+        sub = v.name
+        sq, fe, wr = counters(f"{sub}/sq"), counters(f"{sub}/fetch"), counters(f"{sub}/write")
+        f_scale, w_scale = pack_scale(f"{sub}/fetch", "FETCH_SIZE"), pack_scale(f"{sub}/write", "WRITE_SIZE")
+        # per-dispatch durations of this layer's counter pass are not the traced
+        # ones (counters serialise dispatches); the traced average is used
+        lay = {"fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4), "kernels": {}}
+        for k in sorted(sq):
+            if k.startswith("torch"):
+                continue
+            rec = {"sq": sq[k]}
+            if k in fe and k in wr:
+                rec["fetch_kib"] = round(fe[k]["FETCH_SIZE"], 1)
+                rec["write_kib"] = round(wr[k]["WRITE_SIZE"], 1)
+                rec["bytes_per_launch"] = round(1024 * (fe[k]["FETCH_SIZE"] * f_scale +
+                                                        wr[k]["WRITE_SIZE"] * w_scale))
+            lay["kernels"][k] = rec
+        per_layer[sub] = lay
+
+    # traffic.json: per workload, per kernel, bytes per launch averaged over the layer types
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
@@ -561,9 +685,16 @@ def rocprof_summary(d, workload):
     if rec.get("source_sha256") != kernel_source_digest():
         rec = {"source_sha256": kernel_source_digest(), "workloads": {}}
     rec["note"] = ("HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per "
-                   "dispatch), each scaled by bytes/counter of the pack kernel in the same run")
-    rec["workloads"][case.name] = {"fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
-                                   **traffic}
+                   "dispatch), each scaled by bytes/counter of the pack kernel in the same run; "
+                   "averaged over the workload's layer types")
+    wl_rec = {}
+    for k in sorted({k for lay in per_layer.values() for k in lay["kernels"]}):
+        vals = [lay["kernels"][k] for lay in per_layer.values() if "bytes_per_launch" in lay["kernels"].get(k, {})]
+        if vals:
+            wl_rec[k] = {"bytes_per_launch": round(sum(x["bytes_per_launch"] for x in vals) / len(vals)),
+                         "fetch_kib": round(sum(x["fetch_kib"] for x in vals) / len(vals), 1),
+                         "write_kib": round(sum(x["write_kib"] for x in vals) / len(vals), 1)}
+    rec["workloads"][case.name] = wl_rec
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(rec, f, indent=1, sort_keys=True)
         f.write("\n")
@@ -576,25 +707,127 @@ def rocprof_summary(d, workload):
         f.write("Commands (run from /tmp with TMPDIR=/tmp; R = repository root):\n\n")
         for c in commands:
             f.write(f"    {c}\n")
-        f.write("\n## kernel trace (--kernel-trace --stats)\n\n")
+        f.write("\n## kernel trace of the benchmark command (--kernel-trace --stats)\n\n")
         f.write("| kernel | short name | calls | avg us | total us | % |\n|---|---|---|---|---|---|\n")
         for r in stats:
             f.write(f"| `{r['Name']}` | {_rocprof_name(r['Name'])} | {r['Calls']} | "
                     f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['TotalDurationNs']) / 1e3:.1f} | "
                     f"{float(r['Percentage']):.1f} |\n")
-        cols = sorted({c for v in sq.values() for c in v})
-        f.write("\n## counters, average per dispatch (FETCH_SIZE / WRITE_SIZE in KiB)\n\n")
-        f.write("| kernel | " + " | ".join(cols) + " | FETCH_SIZE | WRITE_SIZE | HBM MB/launch |\n")
-        f.write("|" + "---|" * (len(cols) + 4) + "\n")
-        for k in sorted(sq):
-            vals = " | ".join(f"{sq[k].get(c, float('nan')):.0f}" for c in cols)
-            t = traffic.get(k)
-            tail = (f"{t['fetch_kib']} | {t['write_kib']} | {t['bytes_per_launch'] / 1e6:.2f}"
-                    if t else " | | ")
-            f.write(f"| {k} | {vals} | {tail} |\n")
-        f.write(f"\nCounter scale (pack kernel, Grid_Size x {pack_thread_bytes} bytes read and written per "
-                f"dispatch): FETCH_SIZE x {f_scale:.4f}, WRITE_SIZE x {w_scale:.4f}.\n")
+        for lname, lay in per_layer.items():
+            f.write(f"\n## layer `{lname}`: utilisation per kernel (counter passes of this layer type)\n\n")
+            f.write("MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles): over the traced "
+                    "average duration at the nominal 2.4 GHz, and over GRBM_GUI_ACTIVE cycles (the "
+                    "clock the dispatch ran at).  HBM bytes: FETCH_SIZE x "
+                    f"{lay['fetch_scale']} + WRITE_SIZE x {lay['write_scale']} (KiB, scaled by the "
+                    "pack kernel's known bytes).  Compulsory bytes: every operand read and every "
+                    "result written once.\n\n")
+            f.write("| kernel | avg us | MFMA busy @2.4 GHz | MFMA busy @run clock | run clock GHz | "
+                    "VALU / MFMA instr | LDS instr / MFMA | LDS bank conflicts | HBM MB/launch | "
+                    "HBM GB/s | HBM / compulsory bytes |\n|" + "---|" * 11 + "\n")
+            for k, r in lay["kernels"].items():
+                sqk = r["sq"]
+                us = avg_us.get(k)
+                busy = sqk.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+                gui = sqk.get("GRBM_GUI_ACTIVE")
+                mfma = sqk.get("SQ_INSTS_MFMA", 0.0)
+                u_nom = busy / (SIMDS * us * 1e-6 * PEAK_CLOCK_GHZ * 1e9) if us else None
+                u_run = busy / (SIMDS * gui) if gui else None
+                clk = gui / (us * 1e-6) / 1e9 if (gui and us) else None
+                hbm = r.get("bytes_per_launch")
+                alg = alg_bytes_per_launch(case, k)
+                fmt = lambda x, p="{:.3f}": "" if x is None else p.format(x)
+                f.write(f"| {k} | {fmt(us, '{:.1f}')} | {fmt(u_nom)} | {fmt(u_run)} | {fmt(clk, '{:.2f}')} | "
+                        f"{fmt(sqk.get('SQ_INSTS_VALU', 0) / mfma if mfma else None, '{:.2f}')} | "
+                        f"{fmt(sqk.get('SQ_INSTS_LDS', 0) / mfma if mfma else None, '{:.2f}')} | "
+                        f"{sqk.get('SQ_LDS_BANK_CONFLICT', 0):.0f} | {fmt(hbm / 1e6 if hbm else None, '{:.1f}')} | "
+                        f"{fmt(hbm / (us * 1e-6) / 1e9 if (hbm and us) else None, '{:.0f}')} | "
+                        f"{fmt(hbm / alg if (hbm and alg) else None, '{:.2f}')} |\n")
+            cols = sorted({c for r in lay["kernels"].values() for c in r["sq"]})
+            f.write("\nRaw counters, average per dispatch:\n\n| kernel | " + " | ".join(cols) +
+                    " | FETCH_SIZE KiB | WRITE_SIZE KiB |\n|" + "---|" * (len(cols) + 3) + "\n")
+            for k, r in lay["kernels"].items():
+                f.write(f"| {k} | " + " | ".join(f"{r['sq'].get(c, float('nan')):.0f}" for c in cols) +
+                        f" | {r.get('fetch_kib', '')} | {r.get('write_kib', '')} |\n")
     print(open(out).read())
+
+
+def _visible_counts(docs, S_total, causal, wl, wr, idx, keys_side):
+    """Per flattened token in `idx`: visible keys of that query (keys_side False)
+    or queries that see that key (keys_side True), under the mask rules."""
+    import numpy as np
+    starts = np.cumsum([0] + list(docs))
+    out = []
+    for t in idx:
+        d = int(np.searchsorted(starts, t, side="right") - 1)
+        lo, hi = int(starts[d]), int(starts[d + 1])
+        if not keys_side:   # keys j visible to query t
+            a, b = lo, hi
+            if causal:
+                b = min(b, t + 1)
+            if wl >= 0:
+                a = max(a, t - wl)
+            if wr >= 0:
+                b = min(b, t + wr + 1)
+        else:               # queries i that see key t
+            a, b = lo, hi
+            if causal:
+                a = max(a, t)
+            if wl >= 0:
+                b = min(b, t + wl + 1)
+            if wr >= 0:
+                a = max(a, t - wr)
+        out.append(max(0, b - a))
+    return out
+
+
+def cpu_baseline_subset(inp, n_rows, n_keys):
+    """The fp64 CPU oracle, as it stands, on a bounded sample of rank 0's share
+    of a long workload: O, LSE and dQ of `n_rows` query rows stratified over the
+    sequence (one seeded row in each of n_rows equal strata), and dK, dV of the
+    last `n_keys` keys, for every query head of rank 0 and every layer type.
+    Credited FLOPs: 6*D per visible pair on each side (forward 4*D + dQ 2*D
+    for the rows; dP, dV, dK for the keys), as the GPU figure credits them;
+    the oracle's recompute of the statistics of the rows a key needs is timed
+    but not credited."""
+    import oracle
+    import torch
+    from ulysses_inputs import seq_shards
+    c = inp.case
+    P, D, S, hq = c.P, c.D, c.S, c.hq
+    kv_pack = oracle.pack_replicated if c.Hkv < P else oracle.pack
+    qh = oracle.pack(seq_shards(inp.q, P))[0]
+    kh, vh = kv_pack(seq_shards(inp.k, P))[0], kv_pack(seq_shards(inp.v, P))[0]
+    dh = oracle.pack(seq_shards(inp.dout, P))[0]
+    sk = None if inp.sink is None else inp.sink[:hq].contiguous()
+    cu = None
+    if inp.doc_lengths is not None:
+        cu, _, _ = oracle.segments(oracle.gather_positions(seq_shards(inp.positions, P)))
+    docs = docs_of(inp)
+    T = c.B * S
+    g = torch.Generator().manual_seed(4242)
+    rows = [int(k * T // n_rows + torch.randint(0, max(1, T // n_rows), (1,), generator=g))
+            for k in range(n_rows)]
+    keys = list(range(T - n_keys, T))
+    log(f"cpu baseline: oracle on rank 0 ({hq} query heads), {n_rows} stratified rows and the "
+        f"last {n_keys} keys, {oracle.num_threads()} threads")
+    flops = 0
+    t0 = time.perf_counter()
+    for v in c.variants:
+        kw = dict(sink=sk, cu=cu, causal=v.causal, window_left=v.window_left,
+                  window_right=v.window_right)
+        oracle.attn_fwd(qh, kh, vh, rows=rows, **kw)
+        oracle.attn_bwd(qh, kh, vh, dh, qrows=rows, want_dkdv=False, want_dsink=False, **kw)
+        oracle.attn_bwd(qh, kh, vh, dh, krows=keys, want_dq=False, want_dsink=False, **kw)
+        pr = sum(_visible_counts(docs, T, v.causal, v.window_left, v.window_right, rows, False))
+        pk = sum(_visible_counts(docs, T, v.causal, v.window_left, v.window_right, keys, True))
+        flops += 6 * D * (pr + pk) * hq
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": round(dt, 2), "subset": True,
+            "sample": (f"subset of rank 0's share (all {hq} query heads, layers "
+                       f"{[v.name for v in c.variants]}): O, LSE and dQ of {n_rows} query rows "
+                       f"stratified over S={S}, dK and dV of the last {n_keys} keys; fp64; "
+                       f"{flops / 1e9:.1f} GFLOP credited at 6*D per visible pair and side")}
 
 
 def cpu_baseline(inp, ranks, n_heads):

@@ -127,7 +127,8 @@ int ulysses_a2a_unpack_multi(int n, const void* const* head_shards, void* const*
  *     *max_len          the longest document
  *   cu_capacity is the number of int32 slots in cu_seqlens; it must be at
  *   least B*S + 1 (the worst case, one token per document), so the host never
- *   needs n.  Slots past n are left untouched.
+ *   needs n.  Slots n+1 .. B*S are left untouched; with cu_capacity >=
+ *   ulysses_cu_seqlens_capacity(B, S) the slots after B*S serve as scratch.
  *   Errors: ULY_ERR_NULL, ULY_ERR_SHAPE, ULY_ERR_UNSUPPORTED (pos_bytes),
  *   ULY_ERR_CAPACITY (cu_capacity < B*S + 1), ULY_ERR_ALIGN (pos_shards not
  *   pos_bytes-aligned, outputs not 4-byte aligned).
@@ -135,6 +136,14 @@ int ulysses_a2a_unpack_multi(int n, const void* const* head_shards, void* const*
 int ulysses_cu_seqlens_from_positions(const void* pos_shards, int pos_bytes, int P, int B, int S,
                                       int32_t* cu_seqlens, int cu_capacity, int32_t* n_seqs,
                                       int32_t* max_len, void* stream);
+
+/* The cu_capacity at which ulysses_cu_seqlens_from_positions runs its scan on
+ * many work-groups, in two passes: B*S + 1 plus 4 int32 per chunk of at least
+ * 2048 tokens (at most 1024 chunks).  Those slots past B*S are its scratch:
+ * their contents on return are unspecified.  With a smaller (still valid)
+ * capacity the scan runs in one work-group.  Both give the same result.
+ * 0 for sizes the scan rejects. */
+int ulysses_cu_seqlens_capacity(int B, int S);
 
 /* ------------------------------------------------------------------------
  * One rank's attention over the whole gathered sequence ([accelerate#4209]

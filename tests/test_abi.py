@@ -34,7 +34,8 @@ def test_header_declares_the_boundary():
     assert declared() == {"ulysses_a2a_pack", "ulysses_a2a_unpack", "ulysses_a2a_pack_multi",
                           "ulysses_a2a_unpack_multi", "ulysses_a2a_pack_replicated",
                           "ulysses_a2a_reduce_replicated",
-                          "ulysses_cu_seqlens_from_positions", "ulysses_attn_fwd",
+                          "ulysses_cu_seqlens_from_positions", "ulysses_cu_seqlens_capacity",
+                          "ulysses_attn_fwd",
                           "ulysses_attn_fwd_layout", "ulysses_attn_bwd_layout",
                           "ulysses_attn_bwd_layout_f32kv", "ulysses_attn_fwd_chunk",
                           "ulysses_attn_merge", "ulysses_attn_merge_finish",
@@ -251,3 +252,13 @@ def test_bwd_status_words_sit_inside_the_workspace(lib):
         need = lib.ulysses_attn_bwd_workspace_bytes(B, S, hq, hkv, D)
         assert off > 0 and off % 256 == 0 and off + 24 <= need
     assert lib.ulysses_attn_bwd_status_offset(0, 512, 4, 4, 64) == 0
+
+
+def test_cu_seqlens_capacity(lib):
+    """B*S + 1 plus 4 slots per chunk of at least 2048 tokens, at most 1024 chunks."""
+    f = lib.ulysses_cu_seqlens_capacity
+    assert f(1, 512) == 512 + 1 + 4
+    assert f(1, 131072) == 131072 + 1 + 4 * 64
+    assert f(2, 4194304) == 8388608 + 1 + 4 * 1024
+    assert f(0, 512) == 0 and f(1, 0) == 0
+

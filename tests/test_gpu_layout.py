@@ -89,6 +89,10 @@ SEG_CASES = [
     ("b3_ragged_chunks", 3, 3, 2997, "docs", torch.int64),      # T not a multiple of the threads
     ("long_chunks_int32", 4, 1, 262144, "docs", torch.int32),   # 256 tokens a thread: many batches
     ("dense_restarts", 2, 2, 20000, "dense", torch.int64),
+    # many-work-group scan: 1024 chunks of two rounds each, documents spanning chunks
+    ("multi_round_chunks", 2, 1, 4194304, "docs", torch.int64),
+    # 977 chunks of three rounds, short documents, two batch rows, int32
+    ("multi_round_dense_b2", 1, 2, 3000000, "dense", torch.int32),
 ]
 
 
@@ -109,16 +113,25 @@ def _positions(kind, B, S, g):
     return torch.stack(rows)
 
 
+@pytest.mark.parametrize("path", ["wide", "one_group"])
 @pytest.mark.parametrize("row", SEG_CASES, ids=[c[0] for c in SEG_CASES])
-def test_cu_seqlens_edge_cases_bit_exact(row):
+def test_cu_seqlens_edge_cases_bit_exact(row, path):
+    """Both scans: the many-work-group one (cu_seqlens with room for its
+    scratch, ulysses_cu_seqlens_capacity) and the one-work-group one (exactly
+    B*S + 1 slots)."""
     import ulysses_sequence_attention_rank_amd as uly
     name, P, B, S, kind, dtype = row
-    say(f"cu_seqlens {name}: P={P} B={B} S={S} {kind} {dtype}")
+    if path == "one_group" and B * S > 300000:
+        pytest.skip("the one-work-group scan is exercised on the smaller cases")
+    say(f"cu_seqlens {name} ({path}): P={P} B={B} S={S} {kind} {dtype}")
     g = torch.Generator().manual_seed(zlib.crc32(name.encode()))
     pos = _positions(kind, B, S, g)
     shards = pos.reshape(B, P, S // P).permute(1, 0, 2).contiguous().to(dtype)
     want_cu, want_n, want_mx = oracle.segments(oracle.gather_positions(shards))
-    cu, n, mx = uly.cu_seqlens_from_positions(shards.cuda())
+    cap = uly.cu_seqlens_capacity(B, S) if path == "wide" else B * S + 1
+    assert cap >= B * S + 1
+    cu = torch.full((cap,), -7, dtype=torch.int32, device="cuda")
+    cu, n, mx = uly.cu_seqlens_from_positions(shards.cuda(), cu=cu)
     torch.cuda.synchronize()
     assert int(n.item()) == want_n and int(mx.item()) == want_mx
     assert torch.equal(cu[: want_n + 1].cpu(), want_cu)

@@ -19,7 +19,8 @@ import torch
 __all__ = [
     "UlyssesError", "lib_path", "load", "a2a_pack", "a2a_unpack", "a2a_pack_into",
     "a2a_unpack_into", "a2a_pack_multi_into", "a2a_unpack_multi_into", "a2a_pack_replicated_into",
-    "a2a_reduce_replicated_into", "cu_seqlens_from_positions", "attn_fwd", "attn_bwd",
+    "a2a_reduce_replicated_into", "cu_seqlens_from_positions", "cu_seqlens_capacity", "attn_fwd",
+    "attn_bwd",
     "attn_fwd_workspace_bytes", "attn_bwd_workspace_bytes", "Layout", "view_layout",
     "attn_fwd_chunk", "attn_merge", "attn_merge_finish", "profile_start", "profile_stop", "profile_report",
 ]
@@ -71,6 +72,7 @@ def load():
     lib.ulysses_a2a_reduce_replicated.argtypes = [vp, i32, vp] + [i32] * 5 + [vp]
     lib.ulysses_a2a_unpack_multi.argtypes = [i32, vp, vp, vp] + [i32] * 5 + [vp]
     lib.ulysses_cu_seqlens_from_positions.argtypes = [vp, i32, i32, i32, i32, vp, i32, vp, vp, vp]
+    lib.ulysses_cu_seqlens_capacity.argtypes = [i32, i32]
     lib.ulysses_attn_fwd.argtypes = [vp] * 9 + [sz] + [i32] * 5 + [f32] + [i32] * 3 + [vp]
     lib.ulysses_attn_fwd_workspace_bytes.argtypes = [i32] * 5
     lib.ulysses_attn_fwd_layout.argtypes = [vp] * 9 + [sz, vp, vp] + [i32] * 5 + [f32] + [i32] * 3 + [vp]
@@ -248,18 +250,24 @@ def a2a_reduce_replicated_into(head: torch.Tensor, seq: torch.Tensor, P: int):
 
 # ---------------------------------------------------------------- segments
 
+def cu_seqlens_capacity(B: int, S: int) -> int:
+    """Slots of a cu_seqlens buffer that lets the scan run on many work-groups."""
+    return int(load().ulysses_cu_seqlens_capacity(B, S))
+
+
 def cu_seqlens_from_positions(pos_shards: torch.Tensor, cu: Optional[torch.Tensor] = None,
                               n_seqs: Optional[torch.Tensor] = None,
                               max_len: Optional[torch.Tensor] = None):
-    """``[P, B, S/P]`` int32/int64 position shards -> (cu int32 [B*S+1], n_seqs int32 [1],
-    max_len int32 [1]), all on the device (entries of cu past n_seqs are unspecified)."""
+    """``[P, B, S/P]`` int32/int64 position shards -> (cu int32 [cu_seqlens_capacity(B, S)],
+    n_seqs int32 [1], max_len int32 [1]), all on the device (entries of cu past
+    n_seqs are unspecified)."""
     _dev(pos_shards, "pos_shards")
     if pos_shards.dtype not in (torch.int32, torch.int64):
         raise ValueError("positions must be int32 or int64")
     P, B, Sl = pos_shards.shape
     dev = pos_shards.device
     if cu is None:
-        cu = torch.empty(B * Sl * P + 1, dtype=torch.int32, device=dev)
+        cu = torch.empty(cu_seqlens_capacity(B, Sl * P), dtype=torch.int32, device=dev)
     if n_seqs is None:
         n_seqs = torch.empty(1, dtype=torch.int32, device=dev)
     if max_len is None:

@@ -428,6 +428,12 @@ int ulysses_a2a_unpack_multi(int n, const void* const* head_shards, void* const*
                        "ulysses_a2a_unpack_multi launch");
 }
 
+int ulysses_cu_seqlens_capacity(int B, int S) {
+  if (B <= 0 || S <= 0 || (int64_t)B * S >= kMaxI32) return 0;
+  const int64_t c = (int64_t)B * S + 1 + uly::segments_scratch_slots(B, S);
+  return c <= kMaxI32 ? (int)c : 0;
+}
+
 int ulysses_cu_seqlens_from_positions(const void* pos_shards, int pos_bytes, int P, int B, int S,
                                       int32_t* cu_seqlens, int cu_capacity, int32_t* n_seqs,
                                       int32_t* max_len, void* stream) {
@@ -444,8 +450,8 @@ int ulysses_cu_seqlens_from_positions(const void* pos_shards, int pos_bytes, int
   if (!aligned(pos_shards, pos_bytes) || !aligned(cu_seqlens, 4) || !aligned(n_seqs, 4) ||
       !aligned(max_len, 4))
     return fail(ULY_ERR_ALIGN, "misaligned pointer");
-  return hip_status(uly::segments_launch(pos_shards, pos_bytes, P, B, S, cu_seqlens, n_seqs,
-                                         max_len, (hipStream_t)stream),
+  return hip_status(uly::segments_launch(pos_shards, pos_bytes, P, B, S, cu_seqlens, cu_capacity,
+                                         n_seqs, max_len, (hipStream_t)stream),
                     "ulysses_cu_seqlens_from_positions launch");
 }
 

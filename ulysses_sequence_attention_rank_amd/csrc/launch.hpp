@@ -14,7 +14,9 @@ hipError_t permute_launch(bool pack, int n, const void* const* src, void* const*
 hipError_t reduce_replicated_launch(const void* head, bool head_f32, void* seq, int P, int B, int S,
                                     int H, int D, hipStream_t st);
 hipError_t segments_launch(const void* pos, int pos_bytes, int P, int B, int S, int32_t* cu,
-                           int32_t* n_seqs, int32_t* max_len, hipStream_t st);
+                           int64_t cu_capacity, int32_t* n_seqs, int32_t* max_len, hipStream_t st);
+// int32 slots the many-work-group scan needs after cu_seqlens[B*S]
+int64_t segments_scratch_slots(int B, int S);
 hipError_t attn_fwd_launch(const AttnArgs& a, int D, hipStream_t st);
 hipError_t attn_merge_launch(float* acc_o, float* acc_lse, const float* o, const float* lse, int B,
                              int S, int hq, int D, hipStream_t st);

@@ -20,7 +20,8 @@ import torch
 
 from . import (a2a_pack_into, a2a_pack_multi_into, a2a_pack_replicated_into,
                a2a_reduce_replicated_into, a2a_unpack_into, a2a_unpack_multi_into, attn_bwd,
-               attn_bwd_workspace_bytes, attn_fwd, attn_fwd_workspace_bytes, cu_seqlens_from_positions)
+               attn_bwd_workspace_bytes, attn_fwd, attn_fwd_workspace_bytes, cu_seqlens_capacity,
+               cu_seqlens_from_positions)
 
 
 @dataclasses.dataclass
@@ -99,7 +100,7 @@ def allocate(q_seq, k_seq, v_seq, dout_seq, pos_seq, sink) -> StepBuffers:
     b.dq_seq = torch.empty_like(q_seq)
     b.dk_seq = torch.empty_like(k_seq)
     b.dv_seq = torch.empty_like(v_seq)
-    b.cu = torch.empty(B * S + 1, dtype=torch.int32, device=dev)
+    b.cu = torch.empty(cu_seqlens_capacity(B, S), dtype=torch.int32, device=dev)
     b.n_seqs = torch.empty(1, dtype=torch.int32, device=dev)
     b.max_len = torch.empty(1, dtype=torch.int32, device=dev)
     # the forward and backward run one after the other on one stream: one workspace
