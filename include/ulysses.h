@@ -187,6 +187,27 @@ int ulysses_attn_fwd(const void* q, const void* k, const void* v, void* out, flo
                      void* stream);
 
 /* ------------------------------------------------------------------------
+ * ulysses_attn_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  It computes exactly what ulysses_attn_fwd
+ * computes, with the same kernels.  Its split partials (small problems only,
+ * as ulysses_attn_fwd_workspace_bytes gives them) live in a file-scope device
+ * array of ulysses_attn_fwd_noalloc_max_workspace() bytes (32 MiB), one per
+ * GPU, held until the process ends; the call allocates nothing.  Every call on
+ * one GPU shares that GPU's array: calls that overlap on one GPU (other
+ * streams, other host threads) race.  Nothing in the array needs to be zero
+ * on entry.
+ * Errors: as ulysses_attn_fwd, plus ULY_ERR_CAPACITY when the problem needs
+ *   more split-partial bytes than the array holds, ULY_ERR_HIP if the array's
+ *   device address cannot be obtained.
+ * ---------------------------------------------------------------------- */
+int ulysses_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out, float* lse,
+                             const float* sink, const int32_t* cu_seqlens, const int32_t* n_seqs,
+                             int B, int S, int hq, int hkv, int D, float softmax_scale, int causal,
+                             int window_left, int window_right, void* stream);
+size_t ulysses_attn_fwd_noalloc_max_workspace(void);
+
+/* ------------------------------------------------------------------------
  * The same two calls on tensors in other layouts, read and written in place:
  * attention takes the rank's heads straight from the sequence shards and
  * writes its outputs back into them, with no pack or unpack (the all-to-all's

@@ -37,6 +37,7 @@ def test_header_declares_the_boundary():
                           "ulysses_cu_seqlens_from_positions", "ulysses_cu_seqlens_capacity",
                           "ulysses_attn_fwd",
                           "ulysses_attn_fwd_layout", "ulysses_attn_bwd_layout",
+                          "ulysses_attn_fwd_noalloc", "ulysses_attn_fwd_noalloc_max_workspace",
                           "ulysses_attn_bwd_layout_f32kv", "ulysses_attn_fwd_chunk",
                           "ulysses_attn_merge", "ulysses_attn_merge_finish",
                           "ulysses_attn_fwd_workspace_bytes",
@@ -262,3 +263,15 @@ def test_cu_seqlens_capacity(lib):
     assert f(2, 4194304) == 8388608 + 1 + 4 * 1024
     assert f(0, 512) == 0 and f(1, 0) == 0
 
+
+def test_noalloc_forward_rejects_sizes_beyond_its_scratch(lib):
+    """A problem whose split partials exceed the static scratch is refused on the
+    host with ULY_ERR_CAPACITY (S=8192, 12 heads, D=128 splits in two: 100 MB)."""
+    lib.ulysses_attn_fwd_noalloc_max_workspace.restype = ctypes.c_size_t
+    lib.ulysses_attn_fwd_workspace_bytes.restype = ctypes.c_size_t
+    cap = lib.ulysses_attn_fwd_noalloc_max_workspace()
+    assert cap == 32 << 20
+    assert lib.ulysses_attn_fwd_workspace_bytes(1, 8192, 12, 12, 128) > cap
+    rc = lib.ulysses_attn_fwd_noalloc(_p(A), _p(A), _p(A), _p(A), _p(A), None, None, None, 1, 8192,
+                                      12, 12, 128, ctypes.c_float(0.088), 1, -1, -1, None)
+    assert rc == CAP and b"static scratch" in lib.ulysses_last_error()

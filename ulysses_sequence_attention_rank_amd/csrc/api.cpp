@@ -9,6 +9,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -507,6 +508,56 @@ int ulysses_attn_fwd(const void* q, const void* k, const void* v, void* out, flo
   return ulysses_attn_fwd_layout(q, k, v, out, lse, sink, cu_seqlens, n_seqs, workspace,
                                  workspace_bytes, &lq, &lk, B, S, hq, hkv, D, softmax_scale, causal,
                                  window_left, window_right, stream);
+}
+
+// ---- allocation-free forward: the split partials in a file-scope array
+//
+// One array per GPU, held until the process ends.  In host code `scratch` is
+// a stand-in for the device symbol, not an address: every use goes through
+// the pointer hipGetSymbolAddress returns for the current device, looked up
+// on the first call on that device and kept.
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices] = {};
+
+static int scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(ULY_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ok();
+}
+
+size_t ulysses_attn_fwd_noalloc_max_workspace(void) { return kNoAllocScratchBytes; }
+
+int ulysses_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out, float* lse,
+                             const float* sink, const int32_t* cu_seqlens, const int32_t* n_seqs,
+                             int B, int S, int hq, int hkv, int D, float softmax_scale, int causal,
+                             int window_left, int window_right, void* stream) {
+  const size_t need = ulysses_attn_fwd_workspace_bytes(B, S, hq, hkv, D);
+  if (need > kNoAllocScratchBytes)
+    return fail(ULY_ERR_CAPACITY,
+                "this problem's forward needs %zu bytes of split partials, above the %zu-byte "
+                "static scratch of the allocation-free entry point (use ulysses_attn_fwd)",
+                need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    int rc = scratch_for_current_device(&ws);
+    if (rc) return rc;
+  }
+  return ulysses_attn_fwd(q, k, v, out, lse, sink, cu_seqlens, n_seqs, ws, need > 0 ? kNoAllocScratchBytes : 0,
+                          B, S, hq, hkv, D, softmax_scale, causal, window_left, window_right, stream);
 }
 
 int ulysses_attn_fwd_chunk(const void* q, const void* k_chunk, const void* v_chunk, float* out,
