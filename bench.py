@@ -597,6 +597,7 @@ def alg_bytes_per_launch(case, kernel):
 
 PEAK_CLOCK_GHZ = 2.4
 SIMDS = 1024  # 256 CUs x 4 SIMDs
+XCDS = 8
 
 
 def rocprof_summary(d, workload):
@@ -608,7 +609,8 @@ def rocprof_summary(d, workload):
     --layer <layer>` runs (one layer type each); d/commands.txt: the commands.
     Per kernel: executed MFMA utilisation = SQ_VALU_MFMA_BUSY_CYCLES / (1024
     SIMDs x cycles), at the nominal 2.4 GHz over the traced duration and at the
-    clock the kernel ran at (GRBM_GUI_ACTIVE cycles over the dispatch);
+    clock the kernel ran at (GRBM_GUI_ACTIVE cycles over the dispatch, which
+    the counter reports summed over the 8 XCDs);
     VALU and MFMA instructions; HBM bytes (FETCH_SIZE, WRITE_SIZE scaled by the
     pack kernel's known bytes), GB/s, and their ratio to the compulsory bytes."""
     import collections
@@ -731,8 +733,9 @@ def rocprof_summary(d, workload):
                 gui = sqk.get("GRBM_GUI_ACTIVE")
                 mfma = sqk.get("SQ_INSTS_MFMA", 0.0)
                 u_nom = busy / (SIMDS * us * 1e-6 * PEAK_CLOCK_GHZ * 1e9) if us else None
-                u_run = busy / (SIMDS * gui) if gui else None
-                clk = gui / (us * 1e-6) / 1e9 if (gui and us) else None
+                # GRBM_GUI_ACTIVE reads the sum over the 8 XCDs' busy cycles
+                u_run = busy / (SIMDS * gui / XCDS) if gui else None
+                clk = gui / XCDS / (us * 1e-6) / 1e9 if (gui and us) else None
                 hbm = r.get("bytes_per_launch")
                 alg = alg_bytes_per_launch(case, k)
                 fmt = lambda x, p="{:.3f}": "" if x is None else p.format(x)
