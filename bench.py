@@ -596,6 +596,7 @@ def alg_bytes_per_launch(case, kernel):
 
 
 PEAK_CLOCK_GHZ = 2.4
+CUS = 256
 SIMDS = 1024  # 256 CUs x 4 SIMDs
 XCDS = 8
 
@@ -611,7 +612,8 @@ def rocprof_summary(d, workload):
     SIMDs x cycles), at the nominal 2.4 GHz over the traced duration and at the
     clock the kernel ran at (GRBM_GUI_ACTIVE cycles over the dispatch, which
     the counter reports summed over the 8 XCDs);
-    VALU and MFMA instructions; HBM bytes (FETCH_SIZE, WRITE_SIZE scaled by the
+    VALU and MFMA instructions; the LDS's busy fraction (SQ_LDS_IDX_ACTIVE, summed
+    over the CUs) and bytes read from it per MFMA; HBM bytes (FETCH_SIZE, WRITE_SIZE scaled by the
     pack kernel's known bytes), GB/s, and their ratio to the compulsory bytes."""
     import collections
     import csv
@@ -628,10 +630,25 @@ def rocprof_summary(d, workload):
             return list(csv.DictReader(f))
 
     def counters(sub):
-        agg = collections.defaultdict(lambda: collections.defaultdict(list))
+        """Per kernel: each counter's average per dispatch, and the dispatches'
+        average duration in that pass ("_us").  For GRBM_GUI_ACTIVE and the
+        duration a kernel's first dispatch in the process is left out when
+        there are others: its busy cycles also count the code object's first
+        load."""
+        agg = collections.defaultdict(lambda: collections.defaultdict(dict))
         for r in rows(sub, "counter_collection.csv"):
-            agg[_rocprof_name(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
-        return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in agg.items()}
+            k, disp = _rocprof_name(r["Kernel_Name"]), int(r["Dispatch_Id"])
+            agg[k][disp][r["Counter_Name"]] = float(r["Counter_Value"])
+            agg[k][disp]["_us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        out = {}
+        for k, by_disp in agg.items():
+            every = sorted(by_disp)
+            out[k] = {}
+            for c in {c for dd in every for c in by_disp[dd]}:
+                ds = every[1:] if (c in ("GRBM_GUI_ACTIVE", "_us") and len(every) > 1) else every
+                vals = [by_disp[dd][c] for dd in ds if c in by_disp[dd]]
+                out[k][c] = sum(vals) / len(vals)
+        return out
 
     # scale factors: every thread of the pack kernel reads and writes
     # kPermUnroll 16-byte vectors (grids are a whole number of blocks for
@@ -651,10 +668,14 @@ def rocprof_summary(d, workload):
                 got += float(r["Counter_Value"]) * 1024
         return known / got
 
+    def averages(sub):
+        out = {}
+        for r in rows(sub, "kernel_stats.csv"):
+            out.setdefault(_rocprof_name(r["Name"]), float(r["AverageNs"]) / 1e3)
+        return out
+
     stats = rows("trace", "kernel_stats.csv")
-    avg_us = {}
-    for r in stats:
-        avg_us.setdefault(_rocprof_name(r["Name"]), float(r["AverageNs"]) / 1e3)
+    avg_all = averages("trace")
     with open(os.path.join(d, "commands.txt")) as f:
         commands = [ln.rstrip() for ln in f if ln.strip()]
 
@@ -666,8 +687,12 @@ def rocprof_summary(d, workload):
         # per-dispatch durations of this layer's counter pass are not the traced
         # ones (counters serialise dispatches); the traced average is used
         lay = {"fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4), "kernels": {}}
+        # durations: this layer type's own kernel trace where the workload has
+        # several (one kernel name serves all of them), else the benchmark's
+        lay["avg_us"] = (averages(f"{sub}/trace") if os.path.isdir(os.path.join(d, sub, "trace"))
+                         else avg_all)
         for k in sorted(sq):
-            if k.startswith("torch"):
+            if k.startswith("torch") or k.startswith("__amd"):
                 continue
             rec = {"sq": sq[k]}
             if k in fe and k in wr:
@@ -717,35 +742,49 @@ def rocprof_summary(d, workload):
                     f"{float(r['Percentage']):.1f} |\n")
         for lname, lay in per_layer.items():
             f.write(f"\n## layer `{lname}`: utilisation per kernel (counter passes of this layer type)\n\n")
-            f.write("MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles): over the traced "
+            src = (f"a kernel trace of this layer type alone (`{lname}/trace`)"
+                   if lay["avg_us"] is not avg_all else "the benchmark's kernel trace")
+            f.write(f"Durations (avg us) from {src}.  "
+                    "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles): over the traced "
                     "average duration at the nominal 2.4 GHz, and over GRBM_GUI_ACTIVE cycles (the "
-                    "clock the dispatch ran at).  HBM bytes: FETCH_SIZE x "
+                    "clock the dispatch ran at: GRBM_GUI_ACTIVE over the counter pass's own durations of "
+                    "the same dispatches; each kernel's first dispatch left out; for dispatches of a few "
+                    "tens of us the counter also takes in the dispatch's set-up, and the clock it gives "
+                    "exceeds the chip's 2.4 GHz).  HBM bytes: FETCH_SIZE x "
                     f"{lay['fetch_scale']} + WRITE_SIZE x {lay['write_scale']} (KiB, scaled by the "
                     "pack kernel's known bytes).  Compulsory bytes: every operand read and every "
                     "result written once.\n\n")
+            f.write("LDS busy = SQ_LDS_IDX_ACTIVE / (256 CUs x cycles at the run clock); LDS bytes "
+                    "read = SQ_INSTS_LDS_LOAD_BANDWIDTH x 64.\n\n")
             f.write("| kernel | avg us | MFMA busy @2.4 GHz | MFMA busy @run clock | run clock GHz | "
-                    "VALU / MFMA instr | LDS instr / MFMA | LDS bank conflicts | HBM MB/launch | "
-                    "HBM GB/s | HBM / compulsory bytes |\n|" + "---|" * 11 + "\n")
+                    "VALU / MFMA instr | LDS instr / MFMA | LDS busy | LDS bytes read / MFMA | "
+                    "LDS bank conflicts | HBM MB/launch | "
+                    "HBM GB/s | HBM / compulsory bytes |\n|" + "---|" * 13 + "\n")
             for k, r in lay["kernels"].items():
                 sqk = r["sq"]
-                us = avg_us.get(k)
+                us = lay["avg_us"].get(k)
                 busy = sqk.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
                 gui = sqk.get("GRBM_GUI_ACTIVE")
                 mfma = sqk.get("SQ_INSTS_MFMA", 0.0)
                 u_nom = busy / (SIMDS * us * 1e-6 * PEAK_CLOCK_GHZ * 1e9) if us else None
                 # GRBM_GUI_ACTIVE reads the sum over the 8 XCDs' busy cycles
                 u_run = busy / (SIMDS * gui / XCDS) if gui else None
-                clk = gui / XCDS / (us * 1e-6) / 1e9 if (gui and us) else None
+                cus = sqk.get("_us")  # the same dispatches' own durations
+                clk = gui / XCDS / (cus * 1e-6) / 1e9 if (gui and cus) else None
+                lds_act, lds_rd = sqk.get("SQ_LDS_IDX_ACTIVE"), sqk.get("SQ_INSTS_LDS_LOAD_BANDWIDTH")
+                u_lds = lds_act / (CUS * gui / XCDS) if (gui and lds_act is not None) else None
+                rd_mfma = 64 * lds_rd / mfma if (mfma and lds_rd is not None) else None
                 hbm = r.get("bytes_per_launch")
                 alg = alg_bytes_per_launch(case, k)
                 fmt = lambda x, p="{:.3f}": "" if x is None else p.format(x)
                 f.write(f"| {k} | {fmt(us, '{:.1f}')} | {fmt(u_nom)} | {fmt(u_run)} | {fmt(clk, '{:.2f}')} | "
                         f"{fmt(sqk.get('SQ_INSTS_VALU', 0) / mfma if mfma else None, '{:.2f}')} | "
                         f"{fmt(sqk.get('SQ_INSTS_LDS', 0) / mfma if mfma else None, '{:.2f}')} | "
+                        f"{fmt(u_lds)} | {fmt(rd_mfma, '{:.0f}')} | "
                         f"{sqk.get('SQ_LDS_BANK_CONFLICT', 0):.0f} | {fmt(hbm / 1e6 if hbm else None, '{:.1f}')} | "
                         f"{fmt(hbm / (us * 1e-6) / 1e9 if (hbm and us) else None, '{:.0f}')} | "
                         f"{fmt(hbm / alg if (hbm and alg) else None, '{:.2f}')} |\n")
-            cols = sorted({c for r in lay["kernels"].values() for c in r["sq"]})
+            cols = sorted({c for r in lay["kernels"].values() for c in r["sq"] if not c.startswith("_")})
             f.write("\nRaw counters, average per dispatch:\n\n| kernel | " + " | ".join(cols) +
                     " | FETCH_SIZE KiB | WRITE_SIZE KiB |\n|" + "---|" * (len(cols) + 3) + "\n")
             for k, r in lay["kernels"].items():
