@@ -139,7 +139,7 @@ int ulysses_cu_seqlens_from_positions(const void* pos_shards, int pos_bytes, int
 
 /* The cu_capacity at which ulysses_cu_seqlens_from_positions runs its scan on
  * many work-groups, in two passes: B*S + 1 plus 4 int32 per chunk of at least
- * 2048 tokens (at most 1024 chunks).  Those slots past B*S are its scratch:
+ * 512 tokens (at most 1024 chunks).  Those slots past B*S are its scratch:
  * their contents on return are unspecified.  With a smaller (still valid)
  * capacity the scan runs in one work-group.  Both give the same result.
  * 0 for sizes the scan rejects. */

@@ -256,10 +256,11 @@ def test_bwd_status_words_sit_inside_the_workspace(lib):
 
 
 def test_cu_seqlens_capacity(lib):
-    """B*S + 1 plus 4 slots per chunk of at least 2048 tokens, at most 1024 chunks."""
+    """B*S + 1 plus 4 slots per chunk of at least 512 tokens, at most 1024 chunks."""
     f = lib.ulysses_cu_seqlens_capacity
     assert f(1, 512) == 512 + 1 + 4
-    assert f(1, 131072) == 131072 + 1 + 4 * 64
+    assert f(1, 4096) == 4096 + 1 + 4 * 8
+    assert f(1, 131072) == 131072 + 1 + 4 * 256
     assert f(2, 4194304) == 8388608 + 1 + 4 * 1024
     assert f(0, 512) == 0 and f(1, 0) == 0
 

@@ -89,9 +89,9 @@ SEG_CASES = [
     ("b3_ragged_chunks", 3, 3, 2997, "docs", torch.int64),      # T not a multiple of the threads
     ("long_chunks_int32", 4, 1, 262144, "docs", torch.int32),   # 256 tokens a thread: many batches
     ("dense_restarts", 2, 2, 20000, "dense", torch.int64),
-    # many-work-group scan: 1024 chunks of two rounds each, documents spanning chunks
+    # many-work-group scan: 1024 chunks of eight 512-token rounds, documents spanning chunks
     ("multi_round_chunks", 2, 1, 4194304, "docs", torch.int64),
-    # 977 chunks of three rounds, short documents, two batch rows, int32
+    # 977 chunks of twelve rounds, short documents, two batch rows, int32
     ("multi_round_dense_b2", 1, 2, 3000000, "dense", torch.int32),
 ]
 

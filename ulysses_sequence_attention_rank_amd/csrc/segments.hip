@@ -121,9 +121,9 @@ __global__ __launch_bounds__(kSegThreads) void segments_kernel(SegArgs a) {
 // The same result from many work-groups, when the caller's cu_seqlens buffer
 // has room for scratch after slot B*S (4 int32 per chunk).  Each work-group
 // owns a contiguous chunk of C tokens (C a multiple of kSegRound, at most
-// kSegWideBlocks chunks), taken kSegRound at a time: 8 tiles of 256 tokens,
+// kSegWideBlocks chunks), taken kSegRound at a time: 2 tiles of 256 tokens,
 // thread j reading token tile*256 + j, so a wave reads 64 consecutive
-// positions per load (coalesced, 8 loads in flight per thread).  The start
+// positions per load (coalesced, both loads in flight together).  The start
 // flags of a round are wave ballots kept in LDS in token order; a start's
 // rank among the chunk's starts is then a sum of popcounts.
 //   pass 1 (segments_part_kernel): per chunk, the number of starts, the first
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(kSegThreads) void segments_kernel(SegArgs a) {
 //     last one) and cu[n] = B*S.
 // Pass 2 writes only slots 0..n <= B*S, never the scratch it reads.
 
-constexpr int kSegRound = 2048;  // tokens per round: 8 tiles of 256 threads
+constexpr int kSegRound = 512;  // tokens per round: 2 tiles of 256 threads
 constexpr int kSegTiles = kSegRound / 256;
 constexpr int32_t kNoStart = -1;
 
@@ -159,7 +159,7 @@ __device__ __forceinline__ bool wide_is_start(const WideArgs& a, u32 t) {
   return reinterpret_cast<const PosT*>(a.pos)[((uint64_t)r * a.B + b) * a.Sl.d + s] == 0;
 }
 
-// The start flags of tokens [base, base + kSegRound) as 32 masks in token
+// The start flags of tokens [base, base + kSegRound) as 4 kSegTiles masks in token
 // order (mask 4 k + w holds tile k, wave w); returns this thread's flags.
 template <typename PosT>
 __device__ __forceinline__ unsigned round_masks(const WideArgs& a, u32 base, unsigned long long* masks) {
@@ -206,10 +206,41 @@ __device__ __forceinline__ int32_t block_reduce(int32_t x, int32_t* red, int op)
   return x;
 }
 
+// The chunk's count (sum), first start (min), last start and longest inner
+// document (max) over the work-group, in one pass.
+__device__ __forceinline__ void block_reduce_part(int32_t& cnt, int32_t& first, int32_t& last,
+                                                  int32_t& gap, int32_t* red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    cnt += __shfl_xor(cnt, off, 64);
+    first = min(first, __shfl_xor(first, off, 64));
+    last = max(last, __shfl_xor(last, off, 64));
+    gap = max(gap, __shfl_xor(gap, off, 64));
+  }
+  if (lane == 0) {
+    red[4 * w] = cnt;
+    red[4 * w + 1] = first;
+    red[4 * w + 2] = last;
+    red[4 * w + 3] = gap;
+  }
+  __syncthreads();
+  cnt = red[0];
+  first = red[1];
+  last = red[2];
+  gap = red[3];
+  for (int i = 1; i < 4; ++i) {
+    cnt += red[4 * i];
+    first = min(first, red[4 * i + 1]);
+    last = max(last, red[4 * i + 2]);
+    gap = max(gap, red[4 * i + 3]);
+  }
+}
+
 template <typename PosT>
 __global__ __launch_bounds__(256) void segments_part_kernel(WideArgs a) {
   __shared__ unsigned long long masks[4 * kSegTiles];
-  __shared__ int32_t red[4];
+  __shared__ int32_t red[16];
   const u32 c0 = blockIdx.x * a.C, c1 = min(a.T, c0 + a.C);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   int32_t cnt = 0, first = 0x7fffffff, last = kNoStart, gap = 0;
@@ -234,10 +265,7 @@ __global__ __launch_bounds__(256) void segments_part_kernel(WideArgs a) {
     const int32_t l = last_start_upto(masks, base, 4 * kSegTiles - 1);
     if (l != kNoStart) carry = l;
   }
-  cnt = block_reduce(cnt, red, 0);
-  first = block_reduce(first, red, 2);
-  last = block_reduce(last, red, 1);
-  gap = block_reduce(gap, red, 1);
+  block_reduce_part(cnt, first, last, gap, red);
   if (threadIdx.x == 0) {
     int32_t* p = a.part + 4 * blockIdx.x;
     p[0] = cnt;
