@@ -22,7 +22,13 @@ namespace uly {
 // dV += P^T dO and dK += dS^T Q through the transposing reads), so a SIMD
 // runs two independent waves whose products and softmax overlap.  Each wave
 // accumulates its block's share of its keys' dK and dV; the two shares are
-// added once, through LDS, after the last tile.
+// added once, through LDS, after the last tile.  At D = 64 each wave also
+// keeps its keys' K and V operands in registers (32 VGPRs, read from LDS once
+// per item), which the D = 128 kernel's register budget does not allow.
+
+// K and V operands in registers (else read from LDS for every tile)
+template <int D>
+constexpr bool kKvInRegs = D <= 64;
 
 template <int D, int KG>
 struct DkdvSmem {
@@ -41,6 +47,7 @@ struct DkdvSmem {
 template <int D, int KG>
 __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, const char* buf, const char* kvs,
                                           SwzOffsets<D>& so, int (&kvo)[D / 16],
+                                          const bf16x8 (&kf)[D / 16], const bf16x8 (&vf)[D / 16],
                                           f32x16 (&dkacc)[D / 32], f32x16 (&dvacc)[D / 32],
                                           int qa, int qb, int full_lo, int full_hi, int qlo, int qhi,
                                           int lane) {
@@ -65,10 +72,17 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, const char* buf, co
   // from them (plus an immediate) instead of the compiler keeping one
   // register per distinct address across the loop
   so.refresh();
+  if constexpr (!kKvInRegs<D>) {
 #pragma unroll
-  for (int s = 0; s < KS; ++s) asm volatile("" : "+v"(kvo[s]));
-  auto kv_at = [&](const char* base, int s) {
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + kvo[s]));
+    for (int s = 0; s < KS; ++s) asm volatile("" : "+v"(kvo[s]));
+  }
+  auto k_at = [&](int s) {
+    if constexpr (kKvInRegs<D>) return kf[s];
+    else return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ks + kvo[s]));
+  };
+  auto v_at = [&](int s) {
+    if constexpr (kKvInRegs<D>) return vf[s];
+    else return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vs + kvo[s]));
   };
 
   // dP - delta: the sums start from the rows' -delta (value 4 i + j of a lane
@@ -83,8 +97,8 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, const char* buf, co
   f32x16 sacc, dpacc;
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
-    sacc = mfma32h(so.nat_at(qs, 0, s), kv_at(ks, s), s == 0 ? zero : sacc);
-    dpacc = mfma32h(so.nat_at(dos, 0, s), kv_at(vs, s), s == 0 ? dinit : dpacc);
+    sacc = mfma32h(so.nat_at(qs, 0, s), k_at(s), s == 0 ? zero : sacc);
+    dpacc = mfma32h(so.nat_at(dos, 0, s), v_at(s), s == 0 ? dinit : dpacc);
   }
   // a fully visible tile (wave-uniform) skips the per-element mask
   if (__builtin_amdgcn_readfirstlane((int)full)) {
@@ -226,8 +240,21 @@ __global__ __launch_bounds__(KG * 128) void attn_bwd_dkdv_kernel(AttnArgs a) {
     }
     return qa;
   };
+  // K/V operands in registers: read once the work-group's K/V rows have
+  // landed (after the loop's first barrier)
+  bf16x8 kf[D / 16], vf[D / 16];
+  auto read_kv = [&]() {
+    if constexpr (kKvInRegs<D>) {
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        kf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kvs + kvo[s]));
+        vf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kvs + SM::kKV + kvo[s]));
+      }
+    }
+  };
   auto compute = [&](const char* buf, int qa) {
-    dkdv_tile<D, KG>(a, buf, kvs, so, kvo, dkacc, dvacc, qa, qb, full_lo, full_hi, qlo, qhi, lane);
+    dkdv_tile<D, KG>(a, buf, kvs, so, kvo, kf, vf, dkacc, dvacc, qa, qb, full_lo, full_hi, qlo, qhi,
+                     lane);
   };
 
   // this split's (or segment's) share of the (query tile, head) iterations
@@ -247,6 +274,7 @@ __global__ __launch_bounds__(KG * 128) void attn_bwd_dkdv_kernel(AttnArgs a) {
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile `it` have landed
     __syncthreads();                // everyone's have, and stage 1 is free
     if (it + 1 < it_hi) qa1 = issue(st1);
+    if (it == it_lo) read_kv();
     compute(st0, qa0);
     if (it + 1 < it_hi) {
       __builtin_amdgcn_s_waitcnt(0);
