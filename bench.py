@@ -276,6 +276,11 @@ def main():
         if k in kern:
             rows[k]["tflops"] = fl / (kern[k][1] * 1e-3) / 1e12
             rows[k]["frac_of_peak"] = rows[k]["tflops"] / PEAK_BF16_TFLOPS
+            # what the kernel's products compute per visible pair (masked
+            # parts of diagonal tiles not counted): credited / executed
+            cr, ex = EXECUTED_PER_PAIR[k]
+            rows[k]["executed_flop_per_pair"] = f"{ex}*D (credited {cr}*D)"
+            rows[k]["executed_tflops"] = rows[k]["tflops"] * ex / cr
     # layout permutation inside the step (every element read once and written
     # once; the step's buffers may sit in the Infinity Cache)
     elem_q = case.B * case.S * case.Hq * case.D
@@ -347,6 +352,9 @@ def main():
                    "sink": case.sink, "packed_docs": len(docs) if inp.doc_lengths else None},
         "execution": "hip_graph" if graph is not None else "eager",
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "fa_convention": {"value": round(value * 14 / 12, 2),
+                          "note": "the same step credited 14*D per pair (backward = 2.5 x forward, "
+                                  "its recompute of QK^T included); not the reported value"},
         "fused_layout": {"ms_per_step": round(fused_ms, 4),
                          "value": round(step_flops / (fused_ms * 1e-3) / 1e12, 2),
                          "note": "attention reads Q/K/V and writes O/dQ/dK/dV in the sequence "
@@ -364,8 +372,38 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if cpu is not None:
+        cpu.update(host_cpus())
+        cpu["gpu_over_cpu"] = round(value / cpu["value"], 1) if cpu["value"] else None
     print(json.dumps(line), flush=True)
 
+
+def host_cpus():
+    """Logical CPUs, those this process may run on, and physical cores (distinct
+    (package, core) pairs in /proc/cpuinfo) of the host."""
+    out = {"logical_cpus": os.cpu_count()}
+    try:
+        out["usable_cpus"] = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        pass
+    try:
+        pairs, phys = set(), None
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("physical id"):
+                    phys = ln.split(":")[1].strip()
+                elif ln.startswith("core id"):
+                    pairs.add((phys, ln.split(":")[1].strip()))
+        if pairs:
+            out["physical_cores"] = len(pairs)
+    except OSError:
+        pass
+    return out
+
+
+# (credited, executed) multiples of D per visible pair: the forward's QK^T
+# and PV; dK/dV recomputes QK^T; dQ recomputes QK^T and dP
+EXECUTED_PER_PAIR = {"attn_fwd": (4, 4), "attn_bwd_dkdv": (6, 8), "attn_bwd_dq": (2, 6)}
 
 ATTN_KERNELS = ("attn_fwd", "attn_fwd_merge", "attn_bwd_stats", "attn_bwd_prep", "attn_bwd_dkdv",
                 "attn_bwd_dkdv_reduce", "attn_bwd_dq", "attn_bwd_dq_reduce", "attn_bwd_dsink")
