@@ -150,7 +150,7 @@ def main():
     import torch
 
     import ulysses_sequence_attention_rank_amd as uly
-    from ulysses_inputs import CONFIGS, make_inputs, seq_shards
+    from ulysses_inputs import WORKLOADS, make_inputs, seq_shards
     from ulysses_sequence_attention_rank_amd import sim
 
     if not os.path.exists(uly.lib_path()):
@@ -158,7 +158,7 @@ def main():
         build.build()
     uly.load()
 
-    case = CONFIGS[args.workload]
+    case = WORKLOADS[args.workload]
     if args.layer is not None:
         import dataclasses
         keep = tuple(v for v in case.variants if v.name == args.layer)
@@ -657,8 +657,8 @@ def rocprof_summary(d, workload):
     import csv
     import glob
     import re
-    from ulysses_inputs import CONFIGS
-    case = CONFIGS[workload]
+    from ulysses_inputs import WORKLOADS
+    case = WORKLOADS[workload]
 
     def rows(sub, suffix):
         fs = sorted(glob.glob(os.path.join(d, sub, "**", f"*{suffix}"), recursive=True))

@@ -11,11 +11,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, os.path.dirname(os.path.dirname(HERE)))
 
 import oracle  # noqa: E402
-from ulysses_inputs import CONFIGS, make_inputs, seq_shards  # noqa: E402
+from ulysses_inputs import WORKLOADS, make_inputs, seq_shards  # noqa: E402
 
 
 def segments_packed():
-    case = CONFIGS[3]
+    case = WORKLOADS[3]
     inp = make_inputs(case, with_dout=False)
     cu, n, mx = oracle.segments(oracle.gather_positions(seq_shards(inp.positions, case.P)))
     return {

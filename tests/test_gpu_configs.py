@@ -18,15 +18,15 @@ import torch
 
 import oracle
 from gpu_util import LSE_MAX, LSE_MEAN, assert_close_tol, bits_equal, say
-from ulysses_inputs import CONFIGS, make_inputs, seq_shards
+from ulysses_inputs import WORKLOADS, make_inputs, seq_shards
 
 pytestmark = pytest.mark.gpu
 
 
 @functools.lru_cache(maxsize=1)
 def _inputs(cfg):
-    say(f"generating inputs of workload {cfg} ({CONFIGS[cfg].name})")
-    return make_inputs(CONFIGS[cfg])
+    say(f"generating inputs of workload {cfg} ({WORKLOADS[cfg].name})")
+    return make_inputs(WORKLOADS[cfg])
 
 
 @functools.lru_cache(maxsize=1)
@@ -54,7 +54,7 @@ def _device_step(cfg, variant):
 
 
 def _sample_rows(cfg, cu, n, count=96):
-    c = CONFIGS[cfg]
+    c = WORKLOADS[cfg]
     S = c.S
     rows = set(range(0, 16)) | set(range(S - 16, S))
     for r in range(1, c.P):
@@ -74,7 +74,7 @@ def _sample_keys(cfg, cu, n, variant):
     oracle then needs rows >= S - 2048 only), and the first keys of a document
     when the document is short enough.  (Keys with the longest walks are
     compared at 16k-32k tokens in test_gpu_long.py.)"""
-    c = CONFIGS[cfg]
+    c = WORKLOADS[cfg]
     S = c.S
     keys = set(range(S - 48, S))
     if S >= 65536:
@@ -89,7 +89,7 @@ def _sample_keys(cfg, cu, n, variant):
     return sorted(k for k in keys if 0 <= k < S)
 
 
-CASES = [(cfg, v) for cfg in (1, 2, 3, 4, 5) for v in CONFIGS[cfg].variants]
+CASES = [(cfg, v) for cfg in (1, 2, 3, 4, 5) for v in WORKLOADS[cfg].variants]
 
 
 @pytest.mark.parametrize("cfg,variant", CASES, ids=[f"w{c}-{v.name}" for c, v in CASES])

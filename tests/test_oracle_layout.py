@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import oracle
-from ulysses_inputs import (CONFIGS, doc_lengths_uniform, make_inputs,
+from ulysses_inputs import (WORKLOADS, doc_lengths_uniform, make_inputs,
                             positions_from_doc_lengths, seq_shards)
 
 
@@ -102,7 +102,7 @@ def test_segments_int32_and_int64_positions_agree():
 
 def test_segments_packed_config_equals_drawn_lengths():
     """The packed 32768-token workload: cu is the running sum of the drawn lengths."""
-    inp = make_inputs(CONFIGS[3], with_dout=False)
+    inp = make_inputs(WORKLOADS[3], with_dout=False)
     lens = inp.doc_lengths
     cu, n, mx = oracle.segments(oracle.gather_positions(seq_shards(inp.positions, 4)))
     expect = [0] + torch.cumsum(torch.tensor(lens), 0).tolist()
@@ -116,7 +116,7 @@ def test_segments_golden_fixture():
     import os
     path = os.path.join(os.path.dirname(__file__), "golden", "segments_packed_s32768.json")
     gold = json.load(open(path))
-    inp = make_inputs(CONFIGS[3], with_dout=False)
+    inp = make_inputs(WORKLOADS[3], with_dout=False)
     cu, n, mx = oracle.segments(oracle.gather_positions(seq_shards(inp.positions, 4)))
     assert cu.tolist() == gold["cu_seqlens"] and mx == gold["max_len"] and n == gold["n_seqs"]
 
@@ -131,7 +131,7 @@ def test_doc_length_draw_rule():
 def test_local_shard_cu_seqlens_differ_from_gathered():
     """Negative control: cu_seqlens computed from one rank's local position shard
     do not describe the gathered sequence (the PR's 41.8% mismatch finding, in kind)."""
-    inp = make_inputs(CONFIGS[3], with_dout=False)
+    inp = make_inputs(WORKLOADS[3], with_dout=False)
     shards = seq_shards(inp.positions, 4)
     good, _, _ = oracle.segments(oracle.gather_positions(shards))
     local, _, _ = oracle.segments(shards[0])

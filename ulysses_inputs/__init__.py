@@ -29,7 +29,7 @@ from typing import List, Optional, Sequence, Tuple
 
 import torch
 
-__all__ = ["Case", "CONFIGS", "config_case", "make_inputs", "doc_lengths_uniform", "MlpInputs",
+__all__ = ["Case", "WORKLOADS", "config_case", "make_inputs", "doc_lengths_uniform", "MlpInputs",
            "make_mlp_inputs",
            "positions_from_doc_lengths", "seq_shards"]
 
@@ -77,7 +77,7 @@ FULL = Variant("full", False)
 
 # The five workloads: shapes, head counts, masks and sinks as listed for the
 # simulated configurations (sequence lengths 512 .. 131072).
-CONFIGS = {
+WORKLOADS = {
     1: Case("s512_h8_d64_causal", 1, P=2, B=1, S=512, Hq=8, Hkv=8, D=64, variants=(CAUSAL,)),
     2: Case("s4096_h12_d128", 2, P=2, B=1, S=4096, Hq=12, Hkv=12, D=128, variants=(FULL, CAUSAL)),
     3: Case("s32768_varlen_gqa32x8_d128", 3, P=4, B=1, S=32768, Hq=32, Hkv=8, D=128,
@@ -94,7 +94,7 @@ CONFIGS = {
 
 
 def config_case(cfg_id: int) -> Case:
-    return CONFIGS[cfg_id]
+    return WORKLOADS[cfg_id]
 
 
 def doc_lengths_uniform(g: torch.Generator, total: int, lo: int, hi: int) -> List[int]:
