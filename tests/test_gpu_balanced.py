@@ -1,11 +1,13 @@
 """GPU parity of the dK/dV balanced schedule, which the library uses for long
 sequences on small grids (at least 256 key tiles of 128 keys, at most 512
-(key tile, KV head) items).  The cases below sit in that range and add what the
-five workloads do not: a ragged total length (a partial last key tile and
-ragged last documents), two batch rows, non-causal packed attention and the
-fp32 replica-gradient path.  dK/dV are compared with the fp64 oracle on
-sampled keys (every key of the ragged tail, document starts and ends, random
-keys), O and dQ on sampled rows."""
+(key tile, KV head) items, unless a sliding window narrower than 256 keys
+makes every key tile's walk short).  The cases below sit in that range and add
+what the five workloads do not: a ragged total length (a partial last key tile
+and ragged last documents), two batch rows, non-causal packed attention, the
+fp32 replica-gradient path, and the narrow-window grid at the same sizes.
+dK/dV are compared with the fp64 oracle on sampled keys (every key of the
+ragged tail, document starts and ends, random keys), O and dQ on sampled
+rows."""
 import zlib
 
 import pytest
@@ -19,7 +21,9 @@ pytestmark = pytest.mark.gpu
 CASES = [
     # id, B, S, hq, hkv, D, causal, window_left, packed docs, sink, fp32 dK/dV
     ("packed_ragged_causal_d128_gqa2_sink", 1, 32832, 2, 1, 128, True, -1, True, True, False),
-    ("b2_window127_d64_gqa4", 2, 16448, 4, 1, 64, True, 127, False, False, False),
+    ("b2_window511_d64_gqa4", 2, 16448, 4, 1, 64, True, 511, False, False, False),
+    # a window narrower than 256 keys takes the unsplit grid instead (same sizes)
+    ("b2_window127_d64_gqa4_unsplit", 2, 16448, 4, 1, 64, True, 127, False, False, False),
     ("packed_ragged_full_d128_gqa2_f32kv", 1, 32832, 2, 1, 128, False, -1, True, False, True),
 ]
 

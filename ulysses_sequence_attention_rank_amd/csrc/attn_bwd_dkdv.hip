@@ -462,6 +462,11 @@ template <int D, int KG>
 static void launch_dkdv_t(const AttnArgs& args, hipStream_t st) {
   AttnArgs b = args;
   b.n_tiles = (b.T + 32 * KG - 1) / (32 * KG);
+  // under a window narrower than 256 keys every key tile walks about the same
+  // few query tiles: the grid needs neither the balanced schedule nor splits
+  // (so no reduce launch)
+  const bool narrow = (b.wl >= 0 && b.wl < 256) || (b.wr >= 0 && b.wr < 256 && !b.causal);
+  if (narrow) b.bal_W = 0;
   if (b.bal_W > 0) {  // balanced schedule: parts in 2 bal_W slots, then their sum
     {
       ProfScope prof("attn_bwd_dkdv", st);
@@ -472,7 +477,7 @@ static void launch_dkdv_t(const AttnArgs& args, hipStream_t st) {
     hipLaunchKernelGGL((dkdv_reduce_bal_kernel<D, 32 * KG>), dim3((n / 4 + 255) / 256), dim3(256), 0, st, b, n);
     return;
   }
-  b.nsplit = dkdv_splits(b.B, b.S, b.hkv, D, uneven_layer(b.causal, b.wl, b.wr));
+  b.nsplit = dkdv_splits(b.B, b.S, b.hkv, D, uneven_layer(b.causal, b.wl, b.wr) && !narrow);
   {
     ProfScope prof("attn_bwd_dkdv", st);
     const int items = b.n_tiles * b.hkv;
