@@ -465,7 +465,7 @@ static void launch_dkdv_t(const AttnArgs& args, hipStream_t st) {
   // under a window narrower than 256 keys every key tile walks about the same
   // few query tiles: the grid needs neither the balanced schedule nor splits
   // (so no reduce launch)
-  const bool narrow = (b.wl >= 0 && b.wl < 256) || (b.wr >= 0 && b.wr < 256 && !b.causal);
+  const bool narrow = narrow_window(b.causal, b.wl, b.wr);
   if (narrow) b.bal_W = 0;
   if (b.bal_W > 0) {  // balanced schedule: parts in 2 bal_W slots, then their sum
     {

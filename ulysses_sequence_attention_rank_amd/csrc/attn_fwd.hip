@@ -463,9 +463,9 @@ hipError_t attn_fwd_launch(const AttnArgs& a, int D, hipStream_t st) {
   // a window narrower than 256 keys: 128-row work-groups (each walks the
   // union of its rows' windows, so 256 rows would multiply masked products;
   // the split partials do not depend on the rows per work-group)
-  const bool narrow = (a.wl >= 0 && a.wl < 256) || (a.wr >= 0 && a.wr < 256 && !a.causal);
-  return fwd_block_rows(a.B, a.S, a.hq, D) == 256 && !narrow ? launch_fwd_t<64, 4, 2>(a, st)
-                                                             : launch_fwd_t<64, 4, 1>(a, st);
+  return fwd_block_rows(a.B, a.S, a.hq, D) == 256 && !narrow_window(a.causal, a.wl, a.wr)
+             ? launch_fwd_t<64, 4, 2>(a, st)
+             : launch_fwd_t<64, 4, 1>(a, st);
 }
 
 }  // namespace uly

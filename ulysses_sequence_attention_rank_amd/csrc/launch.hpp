@@ -113,6 +113,11 @@ inline int dkdv_bal_workgroups(int B, int S, int hkv) {
 // counts never fall when `uneven` is set, so workspaces sized with it serve
 // every layer.
 inline bool uneven_layer(int causal, int wl, int wr) { return causal || wl >= 0 || wr >= 0; }
+// A sliding window whose span (keys a row sees, queries a key is seen by) is
+// under 256: bounded on the left and, unless causal, on the right.
+inline bool narrow_window(int causal, int wl, int wr) {
+  return wl >= 0 && (causal || wr >= 0) && wl + (causal ? 0 : wr) < 256;
+}
 // Rows of a forward query tile for head dim D (the launcher's variant choice).
 inline int fwd_block_rows(int B, int S, int hq, int D) {
   if (D == 128) return 128;
