@@ -70,3 +70,27 @@ def test_host_cpu_counts():
     assert c["logical_cpus"] >= 1
     assert 1 <= c.get("usable_cpus", 1) <= c["logical_cpus"]
     assert 1 <= c.get("physical_cores", 1) <= c["logical_cpus"]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_visible_counts_per_row_and_key(seed):
+    """The CPU baseline credits its sampled rows and keys with these counts."""
+    rnd = random.Random(100 + seed)
+    docs = [rnd.randint(1, 60) for _ in range(rnd.randint(1, 3))]
+    T = sum(docs)
+    doc_of = [d for d, L in enumerate(docs) for _ in range(L)]
+    idx = sorted(rnd.sample(range(T), min(T, 12)))
+    for causal in (False, True):
+        for wl, wr in ((-1, -1), (4, -1), (9, 3), (-1, 2)):
+            def vis(i, j):
+                if doc_of[i] != doc_of[j]:
+                    return False
+                if causal and j > i:
+                    return False
+                if wl >= 0 and i - j > wl:
+                    return False
+                return not (wr >= 0 and j - i > wr)
+            rows = bench._visible_counts(docs, T, causal, wl, wr, idx, False)
+            keys = bench._visible_counts(docs, T, causal, wl, wr, idx, True)
+            assert rows == [sum(vis(i, j) for j in range(T)) for i in idx], (docs, causal, wl, wr)
+            assert keys == [sum(vis(i, j) for i in range(T)) for j in idx], (docs, causal, wl, wr)
