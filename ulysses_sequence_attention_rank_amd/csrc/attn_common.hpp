@@ -169,10 +169,8 @@ __device__ __forceinline__ void query_interval(const AttnArgs& a, int j, int& ql
   if (qhi < qlo) qhi = qlo;
 }
 
-// Per-row statistics [B][hq][S] of flattened token t (the query map's S, a
-// FastDiv: the dK/dV kernel computes this for every staged tile)
 __device__ __forceinline__ int lse_index(const AttnArgs& a, int t, int h) {
-  const int b = (int)fdiv((u32)t, a.mq.S);
+  const int b = t / a.S;
   return (b * a.hq + h) * a.S + (t - b * a.S);
 }
 
