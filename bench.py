@@ -132,6 +132,11 @@ def main():
     ap.add_argument("--profile-pass", action="store_true",
                     help="for counter collection: warm-up and --steps eager steps only, no other "
                          "measurement; prints a short JSON line")
+    ap.add_argument("--no-gemm-reference", action="store_true",
+                    help="skip the vendor-library bf16 GEMM measured beside the step")
+    ap.add_argument("--gemm-reference-only", action="store_true",
+                    help="measure only the vendor-library bf16 GEMM (for counter collection) and "
+                         "print its JSON object")
     ap.add_argument("--rocprof-summary", metavar="DIR",
                     help="no GPU run: summarise rocprofv3 CSV output under DIR (trace/, sq/, "
                          "fetch/, write/ and commands.txt) of a run of this script on --workload "
@@ -148,6 +153,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.gemm_reference_only:
+        print(json.dumps(measure_gemm_reference(torch.device("cuda", 0))), flush=True)
+        return
 
     import ulysses_sequence_attention_rank_amd as uly
     from ulysses_inputs import WORKLOADS, make_inputs, seq_shards
@@ -320,6 +329,7 @@ def main():
 
     ring = measure_ring(case, b, credit) if case.Hkv >= case.P else None
     mlp = None if args.no_mlp else measure_tiled_mlp(dev)
+    gemm_ref = None if args.no_gemm_reference else measure_gemm_reference(dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -369,6 +379,7 @@ def main():
                     for k, r in rows.items()},
         "ring_inner_step": ring,
         "tiled_mlp": mlp,
+        "gemm_reference": gemm_ref,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
@@ -531,6 +542,34 @@ def measure_ring(case, b, credit, chunks=4, reps=5):
         res["ring_fwd_tflops"] = round(credit[var.name]["attn_fwd"] / (res["ring_ms"] * 1e-3) / 1e12, 1)
         out["layers"][var.name] = res
     return out
+
+
+def measure_gemm_reference(dev, n=16384, reps=20):
+    """What this GPU sustains on a plain dense bf16 contraction in the same
+    run: torch.matmul (the vendor BLAS) on n x n x n bf16 operands, fp32
+    accumulation, timed with HIP events over `reps` products after three
+    untimed ones.  Context for the attention kernels' figures (the chip's
+    clock falls under sustained MFMA load); not part of the step."""
+    import torch
+    g = torch.Generator(device=dev).manual_seed(7)
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16, generator=g)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16, generator=g)
+    c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    tflops = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    del a, b, c
+    return {"kind": "torch.matmul bf16 (vendor BLAS)", "m": n, "n": n, "k": n, "reps": reps,
+            "ms": round(ms, 4), "tflops": round(tflops, 1),
+            "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4)}
 
 
 def measure_tiled_mlp(dev, T=32768, H=2048, I=8192, tile=8192, reps=3):
