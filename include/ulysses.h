@@ -313,15 +313,15 @@ int ulysses_attn_merge_finish(const float* acc_out, const float* acc_lse, const 
  * x, y, dy, dx: bf16 [T][H] (row-major, token-major); w_gate, w_up: bf16
  * [I][H]; w_down: bf16 [H][I]; dw_gate, dw_up: fp32 [I][H]; dw_down: fp32
  * [H][I].  `tile` tokens per tile (the last tile may be shorter).  H and I
- * must be multiples of 128; T >= 1, tile >= 1.  The forward rounds the gated
+ * must be multiples of 128 and at most 2^20; T >= 1, tile >= 1.  The forward rounds the gated
  * activation to bf16 before the down projection; the backward recomputes
  * each tile's projections from x, rounds them and the gated derivatives to
  * bf16, accumulates the weight gradients in fp32 over the tiles and
  * overwrites dw_* with the sums.  The caller owns all buffers (16-byte
  * aligned), including `workspace` (ulysses_tiled_mlp_workspace_bytes; one
- * tile's activations).  Errors: ULY_ERR_NULL, ULY_ERR_SHAPE (sizes),
- * ULY_ERR_UNSUPPORTED (H or I not a multiple of 128), ULY_ERR_ALIGN,
- * ULY_ERR_CAPACITY (workspace), ULY_ERR_HIP.
+ * tile's activations).  Errors: ULY_ERR_NULL, ULY_ERR_SHAPE (sizes, H or I
+ * above 2^20), ULY_ERR_UNSUPPORTED (H or I not a multiple of 128),
+ * ULY_ERR_ALIGN, ULY_ERR_CAPACITY (workspace), ULY_ERR_HIP.
  * ---------------------------------------------------------------------- */
 size_t ulysses_tiled_mlp_workspace_bytes(int T, int H, int I, int tile);
 int ulysses_tiled_mlp_fwd(const void* x, const void* w_gate, const void* w_up, const void* w_down,

@@ -233,6 +233,8 @@ def test_tiled_mlp_argument_errors(lib):
     assert fwd(200, 128, 256, 0) == SHAPE
     assert fwd(200, 96, 256, 128) == UNSUP
     assert fwd(200, 128, 200, 128) == UNSUP
+    assert fwd(200, 128, (1 << 20) + 128, 128) == SHAPE
+    assert fwd(1, (1 << 20) + 128, 128, 1) == SHAPE
     assert fwd(200, 128, 256, 128, ws_ptr=0) == NULL
     assert fwd(200, 128, 256, 128, ws_bytes=ws - 1) == CAP
     assert fwd(200, 128, 256, 128, x=A + 2) == ALIGN

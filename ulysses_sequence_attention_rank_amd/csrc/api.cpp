@@ -305,8 +305,11 @@ static int check_mlp(const void* x, const void* wg, const void* wu, const void* 
     return fail(ULY_ERR_SHAPE, "sizes must be positive (T=%d H=%d I=%d tile=%d)", T, H, I, tile);
   if (H % 128 || I % 128)
     return fail(ULY_ERR_UNSUPPORTED, "H=%d and I=%d must be multiples of 128", H, I);
-  if ((int64_t)T * H >= kMaxI32 * 8ll || (int64_t)I * H >= kMaxI32 * 8ll || I >= (1 << 22))
-    return fail(ULY_ERR_SHAPE, "problem too large");
+  // a 256-row operand tile of the widest operand (4 I bytes a row) must span
+  // fewer than 2^31 bytes
+  if ((int64_t)T * H >= kMaxI32 * 8ll || (int64_t)I * H >= kMaxI32 * 8ll || H > (1 << 20) ||
+      I > (1 << 20))
+    return fail(ULY_ERR_SHAPE, "problem too large (H=%d, I=%d: at most 2^20 each)", H, I);
   const size_t need = ulysses_tiled_mlp_workspace_bytes(T, H, I, tile);
   if (!ws) return fail(ULY_ERR_NULL, "NULL workspace (%zu bytes needed)", need);
   if (ws_bytes < need) return fail(ULY_ERR_CAPACITY, "workspace of %zu bytes < %zu needed", ws_bytes, need);

@@ -6,17 +6,21 @@
 // Every product is one MFMA GEMM kernel, C[m][n] = sum_k A(m,k) B(n,k), with
 // each operand stored either k-contiguous ("natural": A [M][lda], B [N][ldb])
 // or k-major ("transposed": A [K][lda] holding A(m,k) at k*lda + m, B
-// likewise).  Block tile 128 (m) x 128 (n) x 64 (k), four waves of 64 x 64.
-// Operand tiles arrive by buffer-resource direct-to-LDS loads into the
-// swizzled LDS tiles of the attention kernels (rows past the matrix end read
-// as zero, so the token dimension may be ragged) and are read back in the two
-// forms those tiles serve: natural 16-byte reads, or transposing reads for
-// k-major storage.  The transposing reads deliver k in the slot order of
-// attn_common.hpp (4 hf + e, then 8 + 4 hf + e); a natural operand paired
-// with a transposed one is read in that same order (two 8-byte reads), so
-// both operands of every product contract the same k.  The kernel computes
-// C^T tiles (the B operand as the MFMA's A), which leaves each lane four
-// consecutive n of one row m: one 8- or 16-byte store per four outputs.
+// likewise).  Block tile 256 (m) x 256 (n) x 64 (k), eight waves of 128 x 64,
+// one work-group per CU: at 128 FLOPs per byte staged, the operand stream
+// from L2 stays near half of what the L2 delivers at full MFMA rate (a
+// 128 x 128 tile needs all of it).  Operand tiles arrive by buffer-resource
+// direct-to-LDS loads into the swizzled LDS tiles of the attention kernels
+// (rows past the matrix end read as zero, so the token dimension may be
+// ragged) and are read back in the two forms those tiles serve: natural
+// 16-byte reads, or transposing reads for k-major storage, the latter
+// addressed so that they deliver k in the natural read's order, so both
+// operands of every product contract the same k.  The kernel computes C^T
+// tiles (the B operand as the MFMA's A); the results leave through LDS in
+// whole-row segments.  Consecutive work-groups go to different XCDs, so
+// the tiles are handed out in eight contiguous ranges, one per XCD, each
+// walked in groups of four m tiles: the work-groups an XCD runs together
+// share their A and B rows in its L2.
 #include "attn_common.hpp"
 #include "launch.hpp"
 
@@ -24,8 +28,12 @@ namespace uly {
 
 namespace mlp {
 
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int TILE = BM * BK * 2;  // bytes of an A or B stage (both 128 x 64)
+constexpr int BM = 256, BN = 256, BK = 64, NW = 8;
+// an operand stage is 256 rows x 64 k (natural, Swz<64>) or two 64 k x 128
+// column halves (transposed, Swz<128>); either way 32 KiB, its halves 16 KiB
+constexpr int HALF = 128 * BK * 2;
+constexpr int STAGE = 2 * HALF;
+constexpr int kGroupM = 4;  // m tiles per group of the tile order
 
 enum Epi {
   kStoreBf16 = 0,  // C bf16 [M][ldc]
@@ -52,82 +60,140 @@ struct GemmArgs {
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.f + __expf(-g)); }
 
-// Natural operand read in the transposing reads' k order: lane l of half hf
-// gets row r0 + l%32, k = 16 s + 4 hf .. +3 and 16 s + 8 + 4 hf .. +3.
-template <int D>
-__device__ __forceinline__ bf16x8 nat_perm(const char* lds, int r0, int s, int lane) {
-  const int r = r0 + (lane & 31), hf = lane >> 5;
-  typedef unsigned u32x2v __attribute__((ext_vector_type(2)));
-  const u32x2v lo = *reinterpret_cast<const u32x2v*>(lds + Swz<D>::off(r, 2 * s) + 8 * hf);
-  const u32x2v hi = *reinterpret_cast<const u32x2v*>(lds + Swz<D>::off(r, 2 * s + 1) + 8 * hf);
-  u32x4 x = {lo[0], lo[1], hi[0], hi[1]};
+// Transposed operand for the 16 k rows at r0 of a k-major stage, columns
+// d0 + l%32, with k in natural order: lane half hf gets k = r0 + 8 hf .. +7,
+// which is what the natural 16-byte read of slot 2 s + hf delivers, so the
+// two storage forms pair freely.  (The attention kernels' transposing read
+// takes rows 4 hf + e and 8 + 4 hf + e instead, the order of the MFMA
+// accumulator they pair it with.)
+__device__ __forceinline__ bf16x8 tr_seq(const char* lds, int r0, int d0, int lane) {
+  const int j = lane & 15, grp = lane >> 4;
+  const int col = d0 + 16 * (grp & 1) + 4 * (j & 3);
+  const int kb = r0 + 8 * (grp >> 1) + (j >> 2);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(lds + Swz<128>::off(kb, col >> 3) + (col & 7) * 2));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(lds + Swz<128>::off(kb + 4, col >> 3) + (col & 7) * 2));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 x = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8, x);
 }
 
-// Operand fragment of rows/columns [r0, r0 + 32) and k-step s of a stage:
-// natural stages are 128 rows x 64 k (Swz<64>), transposed stages 64 k rows x
-// 128 columns (Swz<128>).
-template <bool T, bool PERM>
+// Operand fragment of rows/columns [r0, r0 + 32) and k-step s of a stage.
+template <bool T>
 __device__ __forceinline__ bf16x8 frag(const char* st, int r0, int s, int lane) {
-  if constexpr (T) return swz_tr<128>(st, 16 * s, r0, lane);
-  else if constexpr (PERM) return nat_perm<64>(st, r0, s, lane);
+  if constexpr (T) return tr_seq(st + (r0 >> 7) * HALF, 16 * s, r0 & 127, lane);
   else return swz_nat<64>(st, r0, s, lane);
+}
+
+// Scheduling of one k-step's eight products: R LDS reads spread over the
+// first six (the last two leave the reads time to land).
+template <int R>
+__device__ __forceinline__ void interleave_reads() {
+#define MLP_SLOT(t)                                                  \
+  {                                                                  \
+    constexpr int c = R * ((t) + 1) / 6 - R * (t) / 6;               \
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               \
+    if constexpr (c > 0) __builtin_amdgcn_sched_group_barrier(0x100, c, 0); \
+  }
+  MLP_SLOT(0) MLP_SLOT(1) MLP_SLOT(2) MLP_SLOT(3) MLP_SLOT(4) MLP_SLOT(5)
+#undef MLP_SLOT
+  __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+}
+
+// Tile (tm, tn) of work-group `bid` out of m_tiles x n_tiles: eight
+// contiguous ranges (one per XCD, which takes every eighth work-group), each
+// in groups of kGroupM m tiles walked column by column.
+__device__ __forceinline__ void tile_of(int bid, int m_tiles, int n_tiles, int& tm, int& tn) {
+  const int total = m_tiles * n_tiles;
+  const int t = total % 8 == 0 ? (bid % 8) * (total / 8) + bid / 8 : bid;
+  const int per_group = kGroupM * n_tiles;
+  const int first = (t / per_group) * kGroupM;
+  const int gm = min(m_tiles - first, kGroupM);
+  const int r = t % per_group;
+  tm = first + r % gm;
+  tn = r / gm;
 }
 
 }  // namespace mlp
 
-// The A and B stages of k tile KT into (SA, SB).
+// The A and B stages of k tile KT into (SA, SB).  A k-major operand's
+// second column half is loaded only where its columns exist (the matrix's
+// m or n extent is a multiple of 128); an unloaded half feeds only outputs
+// past that extent, which are not stored.
 #define MLP_LOAD_STAGE(SA, SB, KT)                                                                   \
   do {                                                                                               \
     const int k0_ = (KT) * BK;                                                                       \
-    if constexpr (TA) la.load((SA), g.a + (int64_t)k0_ * g.lda + m0, g.K - k0_, wave);             \
-    else la.load((SA), g.a + (int64_t)m0 * g.lda + k0_, g.M - m0, wave);                           \
+    if constexpr (TA) {                                                                              \
+      const __bf16* src_ = g.a + (int64_t)k0_ * g.lda + m0;                                         \
+      la.load((SA), src_, g.K - k0_, wave);                                                          \
+      if (m0 + 128 < g.M) la.load((SA) + HALF, src_ + 128, g.K - k0_, wave);                       \
+    } else {                                                                                         \
+      la.load((SA), g.a + (int64_t)m0 * g.lda + k0_, g.M - m0, wave);                              \
+    }                                                                                                \
     if constexpr (DUAL) {                                                                            \
-      lb_half.load((SB), g.b0 + (int64_t)n0 * g.ldb + k0_, 64, wave);                               \
-      lb_half.load((SB) + TILE / 2, g.b1 + (int64_t)n0 * g.ldb + k0_, 64, wave);                    \
+      lb.load((SB), g.b0 + (int64_t)n0 * g.ldb + k0_, 128, wave);                                  \
+      lb.load((SB) + HALF, g.b1 + (int64_t)n0 * g.ldb + k0_, 128, wave);                           \
     } else if constexpr (TB) {                                                                       \
       const __bf16* src_ = k0_ < g.ksplit ? g.b0 + (int64_t)k0_ * g.ldb                             \
                                           : g.b1 + (int64_t)(k0_ - g.ksplit) * g.ldb;               \
-      lb.load((SB), src_ + n0, (k0_ < g.ksplit ? g.ksplit : g.K) - k0_, wave);                       \
+      const int lim_ = (k0_ < g.ksplit ? g.ksplit : g.K) - k0_;                                     \
+      lb.load((SB), src_ + n0, lim_, wave);                                                          \
+      if (n0 + 128 < g.N) lb.load((SB) + HALF, src_ + n0 + 128, lim_, wave);                       \
     } else {                                                                                         \
       lb.load((SB), g.b0 + (int64_t)n0 * g.ldb + k0_, g.N - n0, wave);                              \
     }                                                                                                \
   } while (0)
 
 template <bool TA, bool TB, int EPI>
-__global__ __launch_bounds__(256, 2) void mlp_gemm_kernel(mlp::GemmArgs g) {
+__global__ __launch_bounds__(512, 1) void mlp_gemm_kernel(mlp::GemmArgs g) {
   using namespace mlp;
   constexpr bool DUAL = EPI == kSwiglu || EPI == kStoreGU;
-  constexpr bool PERM = TA != TB;  // the natural operand follows the transposed one's k order
-  __shared__ __attribute__((aligned(1024))) char sa0[TILE];
-  __shared__ __attribute__((aligned(1024))) char sa1[TILE];
-  __shared__ __attribute__((aligned(1024))) char sb0[TILE];
-  __shared__ __attribute__((aligned(1024))) char sb1[TILE];
+  __shared__ __attribute__((aligned(1024))) char sa0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char sa1[STAGE];
+  __shared__ __attribute__((aligned(1024))) char sb0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char sb1[STAGE];
 
   const int lane = threadIdx.x & 63, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave & 1, wn = wave >> 1;
-  // n tiles: 128 columns, or 64 of each matrix for a dual B
-  const int n_tiles = DUAL ? g.N / 64 : g.N / BN;
-  const int tn = blockIdx.x % n_tiles, tm = blockIdx.x / n_tiles;
-  const int m0 = tm * BM, n0 = tn * (DUAL ? 64 : BN);
+  // n tiles: 256 columns, or 128 of each matrix for a dual B
+  const int n_tiles = DUAL ? g.N / 128 : (g.N + BN - 1) / BN;
+  const int m_tiles = (g.M + BM - 1) / BM;
+  int tm, tn;
+  tile_of(blockIdx.x, m_tiles, n_tiles, tm, tn);
+  const int m0 = tm * BM, n0 = tn * (DUAL ? 128 : BN);
   const int kt_n = (g.K + BK - 1) / BK;
 
-  // A stage: rows m0.. (natural, row stride lda) or k rows (transposed)
-  constexpr int AD = TA ? 128 : 64, AR = TA ? 64 : 128, BD = TB ? 128 : 64, BR = TB ? 64 : 128;
-  const BufTileLoader<AD, AR, 4> la(g.lda, wave, lane);
-  const BufTileLoader<BD, BR, 4> lb(g.ldb, wave, lane);
-  const BufTileLoader<64, 64, 4> lb_half(g.ldb, wave, lane);  // dual: 64 rows of each matrix
+  // A stage: 256 rows m0.. (natural, row stride lda) or 64 k rows of two
+  // 128-column halves (transposed); B likewise, or for a dual B 128 gate
+  // rows then 128 up rows
+  constexpr int AD = TA ? 128 : 64, AR = TA ? 64 : 256;
+  constexpr int BD = TB ? 128 : 64, BR = TB ? 64 : (DUAL ? 128 : 256);
+  const BufTileLoader<AD, AR, NW> la(g.lda, wave, lane);
+  const BufTileLoader<BD, BR, NW> lb(g.ldb, wave, lane);
 
-  f32x16 acc[2][2];
+  f32x16 acc[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
   // B rows of this wave's two n blocks within the B stage
-  const int rb0 = DUAL ? wn * 32 : wn * 64, rb1 = DUAL ? 64 + wn * 32 : wn * 64 + 32;
+  const int rb0 = DUAL ? wn * 32 : wn * 64, rb1 = DUAL ? 128 + wn * 32 : wn * 64 + 32;
+  // LDS read instructions per k-step: a natural fragment is one 16-byte
+  // read (or two 8-byte ones merged into one instruction), a transposed
+  // one two 8-byte transposing reads
+  constexpr int kReads = 2 * (TB ? 2 : 1) + 4 * (TA ? 2 : 1);
+  // the wave's two B and four A operands of k-step s of a stage (B first:
+  // every product of the step needs one of them)
+  auto read_frags = [&](bf16x8 (&fa)[4], bf16x8 (&fb)[2], const char* sa, const char* sb, int s) {
+    fb[0] = frag<TB>(sb, rb0, s, lane);
+    fb[1] = frag<TB>(sb, rb1, s, lane);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) fa[mb] = frag<TA>(sa, wm * 128 + 32 * mb, s, lane);
+  };
 
   // one k tile: stage (SA, SB) holds tile KT, tile KT+1 goes to (NA, NB)
 #define MLP_STEP(KT, SA, SB, NA, NB)                                                                 \
@@ -135,16 +201,21 @@ __global__ __launch_bounds__(256, 2) void mlp_gemm_kernel(mlp::GemmArgs g) {
     __builtin_amdgcn_s_waitcnt(0); /* this wave's loads of stage KT have landed */                   \
     __syncthreads();               /* everyone's have; stage KT-1 is no longer read */              \
     if ((KT) + 1 < kt_n) MLP_LOAD_STAGE(NA, NB, (KT) + 1);                                          \
+    bf16x8 fa[2][4], fb[2][2];                                                                       \
+    read_frags(fa[0], fb[0], (SA), (SB), 0);                                                         \
     _Pragma("unroll") for (int s = 0; s < BK / 16; ++s) {                                            \
-      const bf16x8 fa0 = frag<TA, PERM>((SA), wm * 64, s, lane);                                    \
-      const bf16x8 fa1 = frag<TA, PERM>((SA), wm * 64 + 32, s, lane);                               \
-      const bf16x8 fb0 = frag<TB, PERM>((SB), rb0, s, lane);                                        \
-      const bf16x8 fb1 = frag<TB, PERM>((SB), rb1, s, lane);                                        \
-      acc[0][0] = mfma32(fb0, fa0, acc[0][0]);                                                       \
-      acc[0][1] = mfma32(fb0, fa1, acc[0][1]);                                                       \
-      acc[1][0] = mfma32(fb1, fa0, acc[1][0]);                                                       \
-      acc[1][1] = mfma32(fb1, fa1, acc[1][1]);                                                       \
+      if (s + 1 < BK / 16) read_frags(fa[(s + 1) & 1], fb[(s + 1) & 1], (SA), (SB), s + 1);        \
+      _Pragma("unroll") for (int mb = 0; mb < 4; ++mb) {                                             \
+        acc[0][mb] = mfma32(fb[s & 1][0], fa[s & 1][mb], acc[0][mb]);                                \
+        acc[1][mb] = mfma32(fb[s & 1][1], fa[s & 1][mb], acc[1][mb]);                                \
+      }                                                                                              \
     }                                                                                                \
+    /* the next k-step's operand reads issue under this one's products: */                          \
+    /* the first step's reads, then the next step's spread over the */                             \
+    /* first six products of steps 0-2 */                                                           \
+    __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);                                          \
+    _Pragma("unroll") for (int s = 0; s < BK / 16 - 1; ++s) interleave_reads<kReads>();            \
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);                                               \
   } while (0)
   MLP_LOAD_STAGE(sa0, sb0, 0);
   for (int kt = 0; kt < kt_n; kt += 2) {
@@ -153,45 +224,80 @@ __global__ __launch_bounds__(256, 2) void mlp_gemm_kernel(mlp::GemmArgs g) {
   }
 #undef MLP_STEP
 
-  // lane l: m = m0 + 64 wm + 32 mb + l%32; block nb's n = nbase + 8 i + 4 hf + j
+  // Epilogue through LDS, so that each global access is a whole row segment
+  // (lane l: columns 4 l .. 4 l + 3) instead of 32 rows x 16 bytes: in two
+  // passes, one per m half (wm), the half's four 32-row blocks (mb) go as
+  // fp32 to the four stage arrays, then every wave reads back rows of them.
+  // Row r of a staging array holds 64 16-byte slots, slot c at (c ^ r): the
+  // MFMA layout's writes (32 rows, one slot each) and the row reads are
+  // both free of bank conflicts.
+  char* const stg[4] = {sa0, sa1, sb0, sb1};
+  auto slot_at = [](char* base, int r, int c) -> f32x4* {
+    return reinterpret_cast<f32x4*>(base + r * 1024 + ((c ^ r) << 4));
+  };
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();  // every wave is done with the operand stages
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    const int m = m0 + wm * 64 + mb * 32 + (lane & 31);
-    if (m >= g.M) continue;
+  for (int h = 0; h < 2; ++h) {
+    if (wm == h) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (EPI == kSwiglu || EPI == kStoreGU) {
-        const int n = n0 + wn * 32 + 8 * i + 4 * hf;
-        const f32x16& G = acc[0][mb];
-        const f32x16& U = acc[1][mb];
-        u32x2 w, w1;
-        if constexpr (EPI == kSwiglu) {
-          w[0] = pack_bf16x2(silu_f(G[4 * i + 0]) * U[4 * i + 0], silu_f(G[4 * i + 1]) * U[4 * i + 1]);
-          w[1] = pack_bf16x2(silu_f(G[4 * i + 2]) * U[4 * i + 2], silu_f(G[4 * i + 3]) * U[4 * i + 3]);
-        } else {
-          w[0] = pack_bf16x2(G[4 * i + 0], G[4 * i + 1]);
-          w[1] = pack_bf16x2(G[4 * i + 2], G[4 * i + 3]);
-          w1[0] = pack_bf16x2(U[4 * i + 0], U[4 * i + 1]);
-          w1[1] = pack_bf16x2(U[4 * i + 2], U[4 * i + 3]);
-          *reinterpret_cast<u32x2*>(reinterpret_cast<__bf16*>(g.c1) + (int64_t)m * g.ldc + n) = w1;
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            // column (8 i + 4 hf) of block nb: G | U halves for a dual B
+            const int c = (DUAL ? nb * 32 + wn * 8 : wn * 16 + nb * 8) + 2 * i + hf;
+            const f32x16& C = acc[nb][mb];
+            *slot_at(stg[mb], lane & 31, c) = f32x4{C[4 * i], C[4 * i + 1], C[4 * i + 2], C[4 * i + 3]};
+          }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      if constexpr (DUAL) {
+        // lanes 0-31 row r, lanes 32-63 row r + 1; G slot l % 32, U slot 32 + l % 32
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int r = 4 * wave + 2 * q + hf;
+          const int m = m0 + 128 * h + 32 * mb + r;
+          const int n = n0 + 4 * (lane & 31);
+          const f32x4 G = *slot_at(stg[mb], r, lane & 31);
+          const f32x4 U = *slot_at(stg[mb], r, 32 + (lane & 31));
+          if (m >= g.M) continue;
+          u32x2 w;
+          if constexpr (EPI == kSwiglu) {
+            w[0] = pack_bf16x2(silu_f(G[0]) * U[0], silu_f(G[1]) * U[1]);
+            w[1] = pack_bf16x2(silu_f(G[2]) * U[2], silu_f(G[3]) * U[3]);
+          } else {
+            w[0] = pack_bf16x2(G[0], G[1]);
+            w[1] = pack_bf16x2(G[2], G[3]);
+            u32x2 w1;
+            w1[0] = pack_bf16x2(U[0], U[1]);
+            w1[1] = pack_bf16x2(U[2], U[3]);
+            *reinterpret_cast<u32x2*>(reinterpret_cast<__bf16*>(g.c1) + (int64_t)m * g.ldc + n) = w1;
+          }
+          *reinterpret_cast<u32x2*>(reinterpret_cast<__bf16*>(g.c) + (int64_t)m * g.ldc + n) = w;
         }
-        *reinterpret_cast<u32x2*>(reinterpret_cast<__bf16*>(g.c) + (int64_t)m * g.ldc + n) = w;
       } else {
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const int n = n0 + wn * 64 + nb * 32 + 8 * i + 4 * hf;
-          const f32x16& C = acc[nb][mb];
+        for (int q = 0; q < 4; ++q) {
+          const int r = 4 * wave + q;
+          const int m = m0 + 128 * h + 32 * mb + r;
+          const int n = n0 + 4 * lane;
+          const f32x4 C = *slot_at(stg[mb], r, lane);
+          if (m >= g.M || n >= g.N) continue;
           if constexpr (EPI == kStoreBf16) {
             u32x2 w;
-            w[0] = pack_bf16x2(C[4 * i + 0], C[4 * i + 1]);
-            w[1] = pack_bf16x2(C[4 * i + 2], C[4 * i + 3]);
+            w[0] = pack_bf16x2(C[0], C[1]);
+            w[1] = pack_bf16x2(C[2], C[3]);
             *reinterpret_cast<u32x2*>(reinterpret_cast<__bf16*>(g.c) + (int64_t)m * g.ldc + n) = w;
           } else if constexpr (EPI == kGatedGrad) {
             // dH = C; h = silu(G) U; dG = dH U silu'(G); dU = dH silu(G)
             const int64_t o = (int64_t)m * g.ldc + n;
             const u32x2 gw = *reinterpret_cast<const u32x2*>(g.g_in + o);
             const u32x2 uw = *reinterpret_cast<const u32x2*>(g.u_in + o);
-            float h[4], dg[4], du[4];
+            float hv[4], dg[4], du[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const unsigned gb = (gw[j >> 1] >> (16 * (j & 1))) & 0xffffu;
@@ -199,13 +305,13 @@ __global__ __launch_bounds__(256, 2) void mlp_gemm_kernel(mlp::GemmArgs g) {
               const float gv = __uint_as_float(gb << 16), uv = __uint_as_float(ub << 16);
               const float sg = 1.f / (1.f + __expf(-gv));
               const float sl = gv * sg;
-              h[j] = sl * uv;
-              dg[j] = C[4 * i + j] * uv * (sg * (1.f + gv * (1.f - sg)));
-              du[j] = C[4 * i + j] * sl;
+              hv[j] = sl * uv;
+              dg[j] = C[j] * uv * (sg * (1.f + gv * (1.f - sg)));
+              du[j] = C[j] * sl;
             }
             u32x2 wh, wg2, wu2;
-            wh[0] = pack_bf16x2(h[0], h[1]);
-            wh[1] = pack_bf16x2(h[2], h[3]);
+            wh[0] = pack_bf16x2(hv[0], hv[1]);
+            wh[1] = pack_bf16x2(hv[2], hv[3]);
             wg2[0] = pack_bf16x2(dg[0], dg[1]);
             wg2[1] = pack_bf16x2(dg[2], dg[3]);
             wu2[0] = pack_bf16x2(du[0], du[1]);
@@ -218,15 +324,16 @@ __global__ __launch_bounds__(256, 2) void mlp_gemm_kernel(mlp::GemmArgs g) {
             float* row = m < g.msplit ? reinterpret_cast<float*>(g.c) + (int64_t)m * g.ldc
                                       : g.c_hi + (int64_t)(m - g.msplit) * g.ldc;
             f32x4 v = *reinterpret_cast<const f32x4*>(row + n);
-            v[0] += C[4 * i + 0];
-            v[1] += C[4 * i + 1];
-            v[2] += C[4 * i + 2];
-            v[3] += C[4 * i + 3];
+            v[0] += C[0];
+            v[1] += C[1];
+            v[2] += C[2];
+            v[3] += C[3];
             *reinterpret_cast<f32x4*>(row + n) = v;
           }
         }
       }
     }
+    if (h == 0) __syncthreads();  // the second half overwrites the staging arrays
   }
 }
 
@@ -249,11 +356,11 @@ __global__ __launch_bounds__(256) void mlp_zero_kernel(float* p, int64_t n) {
 template <bool TA, bool TB, int EPI>
 static hipError_t gemm(const mlp::GemmArgs& g, const char* name, hipStream_t st) {
   constexpr bool DUAL = EPI == mlp::kSwiglu || EPI == mlp::kStoreGU;
-  const int n_tiles = DUAL ? g.N / 64 : g.N / mlp::BN;
+  const int n_tiles = DUAL ? g.N / 128 : (g.N + mlp::BN - 1) / mlp::BN;
   const int blocks = n_tiles * ((g.M + mlp::BM - 1) / mlp::BM);
   if (blocks == 0) return hipSuccess;
   ProfScope prof(name, st);
-  hipLaunchKernelGGL((mlp_gemm_kernel<TA, TB, EPI>), dim3(blocks), dim3(256), 0, st, g);
+  hipLaunchKernelGGL((mlp_gemm_kernel<TA, TB, EPI>), dim3(blocks), dim3(mlp::NW * 64), 0, st, g);
   return hipGetLastError();
 }
 
