@@ -627,6 +627,8 @@ def _rocprof_name(full):
     import re
     if "at::native" in full:
         return "torch (buffer fill)"
+    if full.startswith("Cijk_"):
+        return "gemm_reference (vendor BLAS)"
     m = re.search(r"uly::(\w+?)_kernel(<[^>]*>)?", full)
     if not m:
         return full
