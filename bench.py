@@ -361,6 +361,7 @@ def main():
                    "Hkv": case.Hkv, "D": case.D, "layers": [v.name for v in case.variants],
                    "sink": case.sink, "packed_docs": len(docs) if inp.doc_lengths else None},
         "execution": "hip_graph" if graph is not None else "eager",
+        "device": device_info(dev),
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "fa_convention": {"value": round(value * 14 / 12, 2),
                           "note": "the same step credited 14*D per pair (backward = 2.5 x forward, "
@@ -407,6 +408,32 @@ def host_cpus():
                     pairs.add((phys, ln.split(":")[1].strip()))
         if pairs:
             out["physical_cores"] = len(pairs)
+    except OSError:
+        pass
+    return out
+
+
+def device_info(dev):
+    """The GPU as the runtime reports it: name, architecture, compute units
+    and peak shader clock (hipDeviceGetAttribute), and the dense bf16 MFMA
+    peak those give at 4096 FLOP per clock per CU (32x32x16 products, one per
+    32 clocks on each of a CU's four SIMDs)."""
+    import ctypes
+
+    import torch
+    p = torch.cuda.get_device_properties(dev)
+    out = {"name": p.name, "arch": p.gcnArchName, "cus": p.multi_processor_count,
+           "hbm_gib": round(p.total_memory / 2 ** 30, 1)}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        val = ctypes.c_int(0)
+        # hipDeviceAttributeClockRate (kHz) and hipDeviceAttributeMultiprocessorCount
+        # of hip_runtime_api.h; the second must agree with torch's count
+        if (hip.hipDeviceGetAttribute(ctypes.byref(val), 63, dev.index or 0) == 0
+                and val.value == p.multi_processor_count
+                and hip.hipDeviceGetAttribute(ctypes.byref(val), 5, dev.index or 0) == 0):
+            out["peak_sclk_mhz"] = val.value // 1000
+            out["peak_bf16_tflops"] = round(p.multi_processor_count * val.value * 1e3 * 4096 / 1e12, 1)
     except OSError:
         pass
     return out
