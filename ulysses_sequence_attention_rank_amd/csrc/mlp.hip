@@ -54,6 +54,7 @@ struct GemmArgs {
   float* c_hi;
   int64_t ldc;
   int msplit;
+  int split_m;  // tile order (see tile_of): set by the launch when A outweighs B
   const __bf16* g_in;  // kGatedGrad: G and U, [M][ldc] bf16
   const __bf16* u_in;
 };
@@ -101,12 +102,23 @@ __device__ __forceinline__ void interleave_reads() {
   __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
 }
 
-// Tile (tm, tn) of work-group `bid` out of m_tiles x n_tiles: eight
-// contiguous ranges (one per XCD, which takes every eighth work-group), each
-// in groups of kGroupM m tiles walked column by column.
-__device__ __forceinline__ void tile_of(int bid, int m_tiles, int n_tiles, int& tm, int& tn) {
+// Tile (tm, tn) of work-group `bid` out of m_tiles x n_tiles.  Work-group
+// i runs on XCD i mod 8.  Row-major order (`split_m` false) gives XCD x the
+// n tiles = x mod 8 of every m row, so each XCD streams an eighth of B and
+// all of A, and the eight XCDs work on neighbouring tiles of the same rows
+// at once.  With `split_m` the tiles are dealt in eight contiguous ranges,
+// one per XCD, each in groups of kGroupM m tiles walked column by column:
+// each XCD streams an eighth of A and all of B, which is less traffic when
+// A is the larger operand.
+__device__ __forceinline__ void tile_of(int bid, int m_tiles, int n_tiles, bool split_m, int& tm,
+                                        int& tn) {
   const int total = m_tiles * n_tiles;
-  const int t = total % 8 == 0 ? (bid % 8) * (total / 8) + bid / 8 : bid;
+  if (!split_m || total % kXcds != 0) {
+    tm = bid / n_tiles;
+    tn = bid % n_tiles;
+    return;
+  }
+  const int t = (bid % kXcds) * (total / kXcds) + bid / kXcds;
   const int per_group = kGroupM * n_tiles;
   const int first = (t / per_group) * kGroupM;
   const int gm = min(m_tiles - first, kGroupM);
@@ -161,7 +173,7 @@ __global__ __launch_bounds__(512, 1) void mlp_gemm_kernel(mlp::GemmArgs g) {
   const int n_tiles = DUAL ? g.N / 128 : (g.N + BN - 1) / BN;
   const int m_tiles = (g.M + BM - 1) / BM;
   int tm, tn;
-  tile_of(blockIdx.x, m_tiles, n_tiles, tm, tn);
+  tile_of(blockIdx.x, m_tiles, n_tiles, g.split_m != 0, tm, tn);
   const int m0 = tm * BM, n0 = tn * (DUAL ? 128 : BN);
   const int kt_n = (g.K + BK - 1) / BK;
 
@@ -354,8 +366,14 @@ __global__ __launch_bounds__(256) void mlp_zero_kernel(float* p, int64_t n) {
 }
 
 template <bool TA, bool TB, int EPI>
-static hipError_t gemm(const mlp::GemmArgs& g, const char* name, hipStream_t st) {
+static hipError_t gemm(mlp::GemmArgs g, const char* name, hipStream_t st) {
   constexpr bool DUAL = EPI == mlp::kSwiglu || EPI == mlp::kStoreGU;
+  // A has M rows of K, B has N (twice N for a dual B): split the larger one
+  // over the XCDs.  Measured on the 8192-token tiles of the H=2048, I=8192
+  // MLP: the split by m rows took dx from 0.68 to 0.45 ms and the down
+  // projection from 0.26 to 0.23 ms, while the row-major order was faster
+  // for the dual and gated products (B as large as A or larger).
+  g.split_m = (int64_t)g.M > (DUAL ? 2ll : 1ll) * g.N;
   const int n_tiles = DUAL ? g.N / 128 : (g.N + mlp::BN - 1) / mlp::BN;
   const int blocks = n_tiles * ((g.M + mlp::BM - 1) / mlp::BM);
   if (blocks == 0) return hipSuccess;
