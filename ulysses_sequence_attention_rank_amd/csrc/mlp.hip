@@ -17,10 +17,9 @@
 // addressed so that they deliver k in the natural read's order, so both
 // operands of every product contract the same k.  The kernel computes C^T
 // tiles (the B operand as the MFMA's A); the results leave through LDS in
-// whole-row segments.  Consecutive work-groups go to different XCDs, so
-// the tiles are handed out in eight contiguous ranges, one per XCD, each
-// walked in groups of four m tiles: the work-groups an XCD runs together
-// share their A and B rows in its L2.
+// whole-row segments.  Consecutive work-groups go to different XCDs; the
+// tile order (tile_of) gives each XCD an eighth of the larger operand, so
+// that operand crosses the XCDs' L2s once.
 #include "attn_common.hpp"
 #include "launch.hpp"
 
@@ -195,8 +194,7 @@ __global__ __launch_bounds__(512, 1) void mlp_gemm_kernel(mlp::GemmArgs g) {
   // B rows of this wave's two n blocks within the B stage
   const int rb0 = DUAL ? wn * 32 : wn * 64, rb1 = DUAL ? 128 + wn * 32 : wn * 64 + 32;
   // LDS read instructions per k-step: a natural fragment is one 16-byte
-  // read (or two 8-byte ones merged into one instruction), a transposed
-  // one two 8-byte transposing reads
+  // read, a transposed one two 8-byte transposing reads
   constexpr int kReads = 2 * (TB ? 2 : 1) + 4 * (TA ? 2 : 1);
   // the wave's two B and four A operands of k-step s of a stage (B first:
   // every product of the step needs one of them)
