@@ -47,6 +47,10 @@ CASES = [
     (64, 128, 128, 64),
     (129, 256, 128, 1000),
     (1, 128, 128, 1),
+    # m tiles dealt to the XCDs in ranges (eight tiles of 256 tokens), and
+    # operand widths of an odd number of 128-column halves
+    (2048, 256, 1024, 2048),
+    (1000, 384, 640, 512),
 ]
 
 
