@@ -133,10 +133,14 @@ def main():
                     help="for counter collection: warm-up and --steps eager steps only, no other "
                          "measurement; prints a short JSON line")
     ap.add_argument("--no-gemm-reference", action="store_true",
-                    help="skip the vendor-library bf16 GEMM measured beside the step")
+                    help="skip the vendor-library bf16 GEMM and the matrix-core calibration "
+                         "measured beside the step")
     ap.add_argument("--gemm-reference-only", action="store_true",
                     help="measure only the vendor-library bf16 GEMM (for counter collection) and "
                          "print its JSON object")
+    ap.add_argument("--mfma-calibration-only", action="store_true",
+                    help="run only the matrix-core calibration (for counter collection) and print "
+                         "its JSON object")
     ap.add_argument("--rocprof-summary", metavar="DIR",
                     help="no GPU run: summarise rocprofv3 CSV output under DIR (trace/, sq/, "
                          "fetch/, write/ and commands.txt) of a run of this script on --workload "
@@ -156,6 +160,13 @@ def main():
 
     if args.gemm_reference_only:
         print(json.dumps(measure_gemm_reference(torch.device("cuda", 0))), flush=True)
+        return
+    if args.mfma_calibration_only:
+        import ulysses_sequence_attention_rank_amd as uly_
+        if not os.path.exists(uly_.lib_path()):
+            from ulysses_sequence_attention_rank_amd import build
+            build.build()
+        print(json.dumps(measure_mfma_calibration(torch.device("cuda", 0))), flush=True)
         return
 
     import ulysses_sequence_attention_rank_amd as uly
@@ -330,6 +341,7 @@ def main():
     ring = measure_ring(case, b, credit) if case.Hkv >= case.P else None
     mlp = None if args.no_mlp else measure_tiled_mlp(dev)
     gemm_ref = None if args.no_gemm_reference else measure_gemm_reference(dev)
+    mfma_cal = None if args.no_gemm_reference else measure_mfma_calibration(dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -381,6 +393,7 @@ def main():
         "ring_inner_step": ring,
         "tiled_mlp": mlp,
         "gemm_reference": gemm_ref,
+        "mfma_calibration": mfma_cal,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
@@ -599,6 +612,35 @@ def measure_gemm_reference(dev, n=16384, reps=20):
             "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4)}
 
 
+def measure_mfma_calibration(dev, iters=160000, reps=2):
+    """The library's matrix-core calibration: bf16 32x32x16 products on
+    register operands (pseudo-random, changing) with nothing else to do,
+    then with 8 fp32 FMAs beside each product; two CUs' worth of waves per
+    SIMD.  What the GPU sustains on products alone, at the clock it settles
+    at under that load.  Context only, not part of the step."""
+    import torch
+
+    import ulysses_sequence_attention_rank_amd as uly
+    out = torch.empty(512 * 256, dtype=torch.float32, device=dev)
+    res = {"kind": "bf16 32x32x16 MFMA on register operands (library calibration)",
+           "iters": iters}
+    for name, valu in (("mfma_only", 0), ("with_8_fma_per_mfma", 8)):
+        uly.calibrate_mfma(iters // 10 // 8 * 8, valu, out)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        flops = 0
+        for _ in range(reps):
+            flops += uly.calibrate_mfma(iters, valu, out)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        tflops = flops / (ms * 1e-3) / 1e12
+        res[name] = {"ms": round(ms / reps, 3), "tflops": round(tflops, 1),
+                     "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4)}
+    return res
+
+
 def measure_tiled_mlp(dev, T=32768, H=2048, I=8192, tile=8192, reps=3):
     """The sequence-tiled gated MLP of one rank: a Llama-3.2-1B-sized MLP
     (hidden 2048, intermediate 8192) over the 32768 tokens a rank holds in the
@@ -656,6 +698,8 @@ def _rocprof_name(full):
         return "torch (buffer fill)"
     if full.startswith("Cijk_"):
         return "gemm_reference (vendor BLAS)"
+    if "calib_mfma_kernel" in full:
+        return "mfma_calibration"
     m = re.search(r"uly::(\w+?)_kernel(<[^>]*>)?", full)
     if not m:
         return full

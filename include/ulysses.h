@@ -410,6 +410,27 @@ int ulysses_profile_start(int max_launches);
 int ulysses_profile_stop(void);
 int ulysses_profile_report(char* buf, size_t buf_bytes);
 
+/* ------------------------------------------------------------------------
+ * Matrix-core calibration (a measurement aid, not part of the computation):
+ * what the GPU's MFMA units sustain with nothing else to do, as context for
+ * the attention kernels' rates against the published dense peak.
+ * ulysses_calibrate_mfma(out, out_bytes, iters, valu_per, stream): one launch
+ *   of 512 work-groups of 256 threads (two per CU); every wave runs iters
+ *   32x32x16 bf16 products (bf16 in, fp32 accumulate) on each of eight
+ *   independent accumulators, the operands eight pseudo-random pairs per
+ *   lane held in registers and cycled (changing data draws the power real
+ *   tensors do), followed by valu_per (0, 4 or 8) independent fp32 FMAs per
+ *   product.  No memory traffic in the loop.  out: device, at least
+ *   512*256 floats (one checksum a thread, caller-owned scratch).  iters: a
+ *   positive multiple of 8.  Asynchronous on `stream`.  Errors:
+ *   ULY_ERR_NULL, ULY_ERR_CAPACITY (out_bytes), ULY_ERR_SHAPE (iters),
+ *   ULY_ERR_UNSUPPORTED (valu_per), ULY_ERR_ALIGN, ULY_ERR_HIP.
+ * ulysses_calibrate_mfma_flops(iters): the FLOPs one such launch executes
+ *   (0 for iters <= 0).
+ * ---------------------------------------------------------------------- */
+int ulysses_calibrate_mfma(float* out, size_t out_bytes, int iters, int valu_per, void* stream);
+size_t ulysses_calibrate_mfma_flops(int iters);
+
 /* Reason for the last non-zero status returned on this thread ("" if none). */
 const char* ulysses_last_error(void);
 

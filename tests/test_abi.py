@@ -46,7 +46,8 @@ def test_header_declares_the_boundary():
                           "ulysses_tiled_mlp_workspace_bytes", "ulysses_tiled_mlp_fwd",
                           "ulysses_tiled_mlp_bwd",
                           "ulysses_profile_start", "ulysses_profile_stop",
-                          "ulysses_profile_report", "ulysses_last_error"}
+                          "ulysses_profile_report", "ulysses_calibrate_mfma",
+                          "ulysses_calibrate_mfma_flops", "ulysses_last_error"}
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -278,3 +279,21 @@ def test_noalloc_forward_rejects_sizes_beyond_its_scratch(lib):
     rc = lib.ulysses_attn_fwd_noalloc(_p(A), _p(A), _p(A), _p(A), _p(A), None, None, None, 1, 8192,
                                       12, 12, 128, ctypes.c_float(0.088), 1, -1, -1, None)
     assert rc == CAP and b"static scratch" in lib.ulysses_last_error()
+
+
+def test_calibrate_mfma_argument_errors(lib):
+    lib.ulysses_calibrate_mfma.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_void_p]
+    lib.ulysses_calibrate_mfma_flops.restype = ctypes.c_size_t
+    need = 512 * 256 * 4
+    f = lambda out=A, nbytes=need, iters=8, valu=0: lib.ulysses_calibrate_mfma(out, nbytes, iters,
+                                                                              valu, None)
+    assert f(out=None) == NULL
+    assert f(nbytes=need - 1) == CAP
+    assert f(iters=0) == SHAPE
+    assert f(iters=12) == SHAPE
+    assert f(valu=2) == UNSUP
+    assert f(out=A + 2) == ALIGN
+    # 512 work-groups x 4 waves x iters x 8 accumulators x 2*32*32*16 FLOPs
+    assert lib.ulysses_calibrate_mfma_flops(8) == 512 * 4 * 8 * 8 * 32768
+    assert lib.ulysses_calibrate_mfma_flops(0) == 0

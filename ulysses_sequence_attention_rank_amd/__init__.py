@@ -23,6 +23,7 @@ __all__ = [
     "attn_bwd",
     "attn_fwd_workspace_bytes", "attn_bwd_workspace_bytes", "Layout", "view_layout",
     "attn_fwd_chunk", "attn_merge", "attn_merge_finish", "profile_start", "profile_stop", "profile_report",
+    "calibrate_mfma",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -42,7 +43,7 @@ EXPORTS = ("ulysses_a2a_pack", "ulysses_a2a_unpack", "ulysses_a2a_pack_multi",
            "ulysses_attn_fwd_workspace_bytes", "ulysses_attn_bwd_workspace_bytes", "ulysses_attn_bwd",
            "ulysses_tiled_mlp_workspace_bytes", "ulysses_tiled_mlp_fwd", "ulysses_tiled_mlp_bwd",
            "ulysses_profile_start", "ulysses_profile_stop", "ulysses_profile_report",
-           "ulysses_last_error")
+           "ulysses_calibrate_mfma", "ulysses_calibrate_mfma_flops", "ulysses_last_error")
 
 
 class UlyssesError(RuntimeError):
@@ -94,6 +95,9 @@ def load():
     lib.ulysses_profile_start.argtypes = [i32]
     lib.ulysses_profile_stop.argtypes = []
     lib.ulysses_profile_report.argtypes = [ctypes.c_char_p, sz]
+    lib.ulysses_calibrate_mfma.argtypes = [vp, sz, i32, i32, vp]
+    lib.ulysses_calibrate_mfma_flops.argtypes = [i32]
+    lib.ulysses_calibrate_mfma_flops.restype = sz
     lib.ulysses_last_error.argtypes = []
     lib.ulysses_last_error.restype = ctypes.c_char_p
     for fn in EXPORTS:
@@ -134,6 +138,21 @@ def profile_start(max_launches: int = 4096):
 
 def profile_stop():
     _check(load().ulysses_profile_stop(), "ulysses_profile_stop")
+
+
+def calibrate_mfma(iters: int, valu_per: int = 0, out: Optional[torch.Tensor] = None) -> int:
+    """One launch of the matrix-core calibration (a measurement aid, on the
+    current stream of ``out``'s device, default cuda:current): 512 work-groups,
+    every wave ``iters`` bf16 32x32x16 products on eight accumulators with
+    ``valu_per`` fp32 FMAs after each.  Returns the FLOPs it executes."""
+    if out is None:
+        out = torch.empty(512 * 256, dtype=torch.float32,
+                          device=torch.device("cuda", torch.cuda.current_device()))
+    _dev(out, "out", torch.float32)
+    lib = load()
+    _check(lib.ulysses_calibrate_mfma(_p(out), out.numel() * 4, int(iters), int(valu_per),
+                                      _stream(out.device)), "ulysses_calibrate_mfma")
+    return int(lib.ulysses_calibrate_mfma_flops(int(iters)))
 
 
 def profile_report() -> dict:

@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libulysses.so")
 SOURCES = ["api.cpp", "permute.hip", "segments.hip", "attn_fwd.hip", "attn_bwd.hip",
-           "attn_bwd_dkdv.hip", "mlp.hip"]
+           "attn_bwd_dkdv.hip", "mlp.hip", "calib.hip"]
 ARCH = os.environ.get("ULYSSES_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
