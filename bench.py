@@ -613,25 +613,27 @@ def measure_gemm_reference(dev, n=16384, reps=20):
 
 
 def measure_mfma_calibration(dev, iters=160000, reps=2):
-    """The library's matrix-core calibration: bf16 32x32x16 products on
-    register operands (pseudo-random, changing) with nothing else to do,
-    then with 8 fp32 FMAs beside each product; two CUs' worth of waves per
-    SIMD.  What the GPU sustains on products alone, at the clock it settles
-    at under that load.  Context only, not part of the step."""
+    """The library's matrix-core calibration: bf16 32x32x16 products with
+    nothing else to do (operands pseudo-random and changing), then with 8 fp32
+    FMAs beside each product, then with one and with both operands of each
+    product read from LDS (1 and 2 KiB a product); two waves per SIMD.  What
+    the GPU sustains on products alone and fed through LDS, at the clock it
+    settles at under each load.  Context only, not part of the step."""
     import torch
 
     import ulysses_sequence_attention_rank_amd as uly
     out = torch.empty(512 * 256, dtype=torch.float32, device=dev)
-    res = {"kind": "bf16 32x32x16 MFMA on register operands (library calibration)",
+    res = {"kind": "bf16 32x32x16 MFMA, pseudo-random operands (library calibration)",
            "iters": iters}
-    for name, valu in (("mfma_only", 0), ("with_8_fma_per_mfma", 8)):
-        uly.calibrate_mfma(iters // 10 // 8 * 8, valu, out)
+    for name, mode in (("registers", 0), ("registers_8_fma_per_mfma", 1),
+                       ("lds_1KiB_per_mfma", 2), ("lds_2KiB_per_mfma", 3)):
+        uly.calibrate_mfma(iters // 10 // 8 * 8, mode, out)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         flops = 0
         for _ in range(reps):
-            flops += uly.calibrate_mfma(iters, valu, out)
+            flops += uly.calibrate_mfma(iters, mode, out)
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1)

@@ -414,21 +414,23 @@ int ulysses_profile_report(char* buf, size_t buf_bytes);
  * Matrix-core calibration (a measurement aid, not part of the computation):
  * what the GPU's MFMA units sustain with nothing else to do, as context for
  * the attention kernels' rates against the published dense peak.
- * ulysses_calibrate_mfma(out, out_bytes, iters, valu_per, stream): one launch
- *   of 512 work-groups of 256 threads (two per CU); every wave runs iters
+ * ulysses_calibrate_mfma(out, out_bytes, iters, mode, stream): one launch of
+ *   512 work-groups of 256 threads (two per CU); every wave runs iters
  *   32x32x16 bf16 products (bf16 in, fp32 accumulate) on each of eight
- *   independent accumulators, the operands eight pseudo-random pairs per
- *   lane held in registers and cycled (changing data draws the power real
- *   tensors do), followed by valu_per (0, 4 or 8) independent fp32 FMAs per
- *   product.  No memory traffic in the loop.  out: device, at least
- *   512*256 floats (one checksum a thread, caller-owned scratch).  iters: a
- *   positive multiple of 8.  Asynchronous on `stream`.  Errors:
- *   ULY_ERR_NULL, ULY_ERR_CAPACITY (out_bytes), ULY_ERR_SHAPE (iters),
- *   ULY_ERR_UNSUPPORTED (valu_per), ULY_ERR_ALIGN, ULY_ERR_HIP.
+ *   independent accumulators, their operands pseudo-random and changing
+ *   from product to product (the power real tensors draw).  mode 0: operands
+ *   from registers, nothing else in the loop; 1: as 0 with 8 independent
+ *   fp32 FMAs after each product; 2: each product's B operand read from LDS
+ *   (1 KiB a product); 3: both operands from LDS (2 KiB a product).  No
+ *   global memory traffic in the loop.  out: device, at least 512*256
+ *   floats (one checksum a thread, caller-owned scratch).  iters: a positive
+ *   multiple of 8.  Asynchronous on `stream`.  Errors: ULY_ERR_NULL,
+ *   ULY_ERR_CAPACITY (out_bytes), ULY_ERR_SHAPE (iters), ULY_ERR_UNSUPPORTED
+ *   (mode), ULY_ERR_ALIGN, ULY_ERR_HIP.
  * ulysses_calibrate_mfma_flops(iters): the FLOPs one such launch executes
  *   (0 for iters <= 0).
  * ---------------------------------------------------------------------- */
-int ulysses_calibrate_mfma(float* out, size_t out_bytes, int iters, int valu_per, void* stream);
+int ulysses_calibrate_mfma(float* out, size_t out_bytes, int iters, int mode, void* stream);
 size_t ulysses_calibrate_mfma_flops(int iters);
 
 /* Reason for the last non-zero status returned on this thread ("" if none). */

@@ -286,13 +286,14 @@ def test_calibrate_mfma_argument_errors(lib):
                                            ctypes.c_int, ctypes.c_void_p]
     lib.ulysses_calibrate_mfma_flops.restype = ctypes.c_size_t
     need = 512 * 256 * 4
-    f = lambda out=A, nbytes=need, iters=8, valu=0: lib.ulysses_calibrate_mfma(out, nbytes, iters,
-                                                                              valu, None)
+    f = lambda out=A, nbytes=need, iters=8, mode=0: lib.ulysses_calibrate_mfma(out, nbytes, iters,
+                                                                             mode, None)
     assert f(out=None) == NULL
     assert f(nbytes=need - 1) == CAP
     assert f(iters=0) == SHAPE
     assert f(iters=12) == SHAPE
-    assert f(valu=2) == UNSUP
+    assert f(mode=4) == UNSUP
+    assert f(mode=-1) == UNSUP
     assert f(out=A + 2) == ALIGN
     # 512 work-groups x 4 waves x iters x 8 accumulators x 2*32*32*16 FLOPs
     assert lib.ulysses_calibrate_mfma_flops(8) == 512 * 4 * 8 * 8 * 32768

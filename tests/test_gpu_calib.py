@@ -10,11 +10,11 @@ from gpu_util import say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("valu_per", [0, 4, 8])
-def test_calibrate_mfma_runs(valu_per):
-    say(f"calibrate_mfma valu_per={valu_per}")
+@pytest.mark.parametrize("mode", [0, 1, 2, 3])
+def test_calibrate_mfma_runs(mode):
+    say(f"calibrate_mfma mode={mode}")
     out = torch.full((512 * 256,), float("nan"), dtype=torch.float32, device="cuda")
-    flops = uly.calibrate_mfma(64, valu_per, out)
+    flops = uly.calibrate_mfma(64, mode, out)
     torch.cuda.synchronize()
     assert flops == 512 * 4 * 64 * 8 * 2 * 32 * 32 * 16
     assert torch.isfinite(out).all()

@@ -140,17 +140,18 @@ def profile_stop():
     _check(load().ulysses_profile_stop(), "ulysses_profile_stop")
 
 
-def calibrate_mfma(iters: int, valu_per: int = 0, out: Optional[torch.Tensor] = None) -> int:
+def calibrate_mfma(iters: int, mode: int = 0, out: Optional[torch.Tensor] = None) -> int:
     """One launch of the matrix-core calibration (a measurement aid, on the
     current stream of ``out``'s device, default cuda:current): 512 work-groups,
-    every wave ``iters`` bf16 32x32x16 products on eight accumulators with
-    ``valu_per`` fp32 FMAs after each.  Returns the FLOPs it executes."""
+    every wave ``iters`` bf16 32x32x16 products on eight accumulators; mode 0
+    register operands, 1 with 8 fp32 FMAs per product, 2 one operand from LDS,
+    3 both from LDS.  Returns the FLOPs it executes."""
     if out is None:
         out = torch.empty(512 * 256, dtype=torch.float32,
                           device=torch.device("cuda", torch.cuda.current_device()))
     _dev(out, "out", torch.float32)
     lib = load()
-    _check(lib.ulysses_calibrate_mfma(_p(out), out.numel() * 4, int(iters), int(valu_per),
+    _check(lib.ulysses_calibrate_mfma(_p(out), out.numel() * 4, int(iters), int(mode),
                                       _stream(out.device)), "ulysses_calibrate_mfma")
     return int(lib.ulysses_calibrate_mfma_flops(int(iters)))
 

@@ -224,16 +224,15 @@ int ulysses_profile_start(int max_launches) {
   return ok();
 }
 
-int ulysses_calibrate_mfma(float* out, size_t out_bytes, int iters, int valu_per, void* stream) {
+int ulysses_calibrate_mfma(float* out, size_t out_bytes, int iters, int mode, void* stream) {
   if (!out) return fail(ULY_ERR_NULL, "NULL out");
   const size_t need = (size_t)uly::kCalibBlocks * 256 * sizeof(float);
   if (out_bytes < need) return fail(ULY_ERR_CAPACITY, "out of %zu bytes < %zu needed", out_bytes, need);
   if (iters <= 0 || iters % 8)
     return fail(ULY_ERR_SHAPE, "iters=%d: a positive multiple of 8", iters);
-  if (valu_per != 0 && valu_per != 4 && valu_per != 8)
-    return fail(ULY_ERR_UNSUPPORTED, "valu_per=%d: 0, 4 or 8", valu_per);
+  if (mode < 0 || mode > 3) return fail(ULY_ERR_UNSUPPORTED, "mode=%d: 0 to 3", mode);
   if (!aligned(out, 4)) return fail(ULY_ERR_ALIGN, "out needs 4-byte alignment");
-  return hip_status(uly::calib_mfma_launch(out, iters, valu_per, (hipStream_t)stream),
+  return hip_status(uly::calib_mfma_launch(out, iters, mode, (hipStream_t)stream),
                     "ulysses_calibrate_mfma launch");
 }
 

@@ -40,12 +40,11 @@ hipError_t mlp_fwd_launch(const MlpArgs& p, hipStream_t st);
 hipError_t mlp_bwd_launch(const MlpArgs& p, hipStream_t st);
 
 // The matrix-core calibration (calib.hip, a measurement aid): kCalibBlocks
-// work-groups of 256 threads, two per CU, each thread `iters` (a multiple of
-// 8) 32x32x16 bf16 products on each of its wave's eight accumulators, with
-// valu_per (0, 4 or 8) fp32 FMAs after each product; one float per thread
-// into out.
+// work-groups of 256 threads, two per CU, each wave `iters` (a multiple of 8)
+// 32x32x16 bf16 products on each of its eight accumulators, in `mode` 0-3
+// (see calib.hip); one float per thread into out.
 constexpr int kCalibBlocks = 512;
-hipError_t calib_mfma_launch(float* out, int iters, int valu_per, hipStream_t st);
+hipError_t calib_mfma_launch(float* out, int iters, int mode, hipStream_t st);
 
 // Number of splits of a reduction dimension for a kernel whose natural grid
 // has `wgs` work-groups of which `per_round` are resident at once on MI355X
