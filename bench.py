@@ -616,7 +616,8 @@ def measure_mfma_calibration(dev, iters=160000, reps=2):
     """The library's matrix-core calibration: bf16 32x32x16 products with
     nothing else to do (operands pseudo-random and changing), then with 8 fp32
     FMAs beside each product, then with one and with both operands of each
-    product read from LDS (1 and 2 KiB a product); two waves per SIMD.  What
+    product read from LDS (1 and 2 KiB a product), then with 8 exp2 (and, to
+    compare, 8 multiplies) beside each product; two waves per SIMD.  What
     the GPU sustains on products alone and fed through LDS, at the clock it
     settles at under each load.  Context only, not part of the step."""
     import torch
@@ -626,7 +627,8 @@ def measure_mfma_calibration(dev, iters=160000, reps=2):
     res = {"kind": "bf16 32x32x16 MFMA, pseudo-random operands (library calibration)",
            "iters": iters}
     for name, mode in (("registers", 0), ("registers_8_fma_per_mfma", 1),
-                       ("lds_1KiB_per_mfma", 2), ("lds_2KiB_per_mfma", 3)):
+                       ("lds_1KiB_per_mfma", 2), ("lds_2KiB_per_mfma", 3),
+                       ("registers_8_exp2_per_mfma", 4), ("registers_8_mul_per_mfma", 5)):
         uly.calibrate_mfma(iters // 10 // 8 * 8, mode, out)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -421,7 +421,9 @@ int ulysses_profile_report(char* buf, size_t buf_bytes);
  *   from product to product (the power real tensors draw).  mode 0: operands
  *   from registers, nothing else in the loop; 1: as 0 with 8 independent
  *   fp32 FMAs after each product; 2: each product's B operand read from LDS
- *   (1 KiB a product); 3: both operands from LDS (2 KiB a product).  No
+ *   (1 KiB a product); 3: both operands from LDS (2 KiB a product); 4: as 0
+ *   with 8 independent fp32 exp2 (each with two adds) after each product;
+ *   5: as 4 with a multiply in place of each exp2.  No
  *   global memory traffic in the loop.  out: device, at least 512*256
  *   floats (one checksum a thread, caller-owned scratch).  iters: a positive
  *   multiple of 8.  Asynchronous on `stream`.  Errors: ULY_ERR_NULL,

@@ -292,7 +292,7 @@ def test_calibrate_mfma_argument_errors(lib):
     assert f(nbytes=need - 1) == CAP
     assert f(iters=0) == SHAPE
     assert f(iters=12) == SHAPE
-    assert f(mode=4) == UNSUP
+    assert f(mode=6) == UNSUP
     assert f(mode=-1) == UNSUP
     assert f(out=A + 2) == ALIGN
     # 512 work-groups x 4 waves x iters x 8 accumulators x 2*32*32*16 FLOPs

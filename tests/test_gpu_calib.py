@@ -10,7 +10,7 @@ from gpu_util import say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("mode", [0, 1, 2, 3])
+@pytest.mark.parametrize("mode", [0, 1, 2, 3, 4, 5])
 def test_calibrate_mfma_runs(mode):
     say(f"calibrate_mfma mode={mode}")
     out = torch.full((512 * 256,), float("nan"), dtype=torch.float32, device="cuda")

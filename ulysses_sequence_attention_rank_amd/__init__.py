@@ -145,7 +145,8 @@ def calibrate_mfma(iters: int, mode: int = 0, out: Optional[torch.Tensor] = None
     current stream of ``out``'s device, default cuda:current): 512 work-groups,
     every wave ``iters`` bf16 32x32x16 products on eight accumulators; mode 0
     register operands, 1 with 8 fp32 FMAs per product, 2 one operand from LDS,
-    3 both from LDS.  Returns the FLOPs it executes."""
+    3 both from LDS, 4 with 8 exp2 per product, 5 as 4 with multiplies in
+    place of the exp2.  Returns the FLOPs it executes."""
     if out is None:
         out = torch.empty(512 * 256, dtype=torch.float32,
                           device=torch.device("cuda", torch.cuda.current_device()))

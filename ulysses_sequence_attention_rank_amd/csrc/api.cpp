@@ -230,7 +230,7 @@ int ulysses_calibrate_mfma(float* out, size_t out_bytes, int iters, int mode, vo
   if (out_bytes < need) return fail(ULY_ERR_CAPACITY, "out of %zu bytes < %zu needed", out_bytes, need);
   if (iters <= 0 || iters % 8)
     return fail(ULY_ERR_SHAPE, "iters=%d: a positive multiple of 8", iters);
-  if (mode < 0 || mode > 3) return fail(ULY_ERR_UNSUPPORTED, "mode=%d: 0 to 3", mode);
+  if (mode < 0 || mode > 5) return fail(ULY_ERR_UNSUPPORTED, "mode=%d: 0 to 5", mode);
   if (!aligned(out, 4)) return fail(ULY_ERR_ALIGN, "out needs 4-byte alignment");
   return hip_status(uly::calib_mfma_launch(out, iters, mode, (hipStream_t)stream),
                     "ulysses_calibrate_mfma launch");

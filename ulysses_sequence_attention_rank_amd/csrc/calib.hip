@@ -7,7 +7,10 @@
 //   0  operands from registers (eight pairs per lane, cycled);
 //   1  as 0, with 8 independent fp32 FMAs after each product;
 //   2  the B operand of each product read from LDS (1 KiB per product);
-//   3  both operands read from LDS (2 KiB per product).
+//   3  both operands read from LDS (2 KiB per product);
+//   4  as 0, with 8 independent exp2 (each with two adds) after each product;
+//   5  as 4 with a multiply in place of each exp2 (what the exp2 costs
+//      beyond an ordinary vector operation).
 // The sums land in `out` (one value per thread) so that nothing is
 // optimised away.
 #include "launch.hpp"
@@ -53,14 +56,26 @@ __global__ __launch_bounds__(256, 2) void calib_mfma_kernel(float* out, int iter
   for (int k = 0; k < 8; ++k)
     for (int e = 0; e < 16; ++e) acc[k][e] = 0.f;
   float v0 = threadIdx.x * 1e-7f, v1 = v0 + 1e-7f, v2 = v1 + 1e-7f, v3 = v2 + 1e-7f;
+  float xs[8], ss[8];
+  for (int j = 0; j < 8; ++j) {
+    xs[j] = -1.f + 0.1f * j + 1e-6f * threadIdx.x;
+    ss[j] = 0.f;
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if constexpr (MODE <= 1) {
+  if constexpr (MODE <= 1 || MODE >= 4) {
     for (int it = 0; it < iters; it += 8)
 #pragma unroll
       for (int u = 0; u < 8; ++u)
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[k], bv[(k + u) & 7], acc[k], 0, 0, 0);
+          if constexpr (MODE >= 4) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              xs[j] += 1e-7f;
+              ss[j] += MODE == 4 ? __builtin_amdgcn_exp2f(xs[j]) : xs[j] * 1.0001f;
+            }
+          }
           if constexpr (MODE == 1) {
             v0 = __builtin_fmaf(v0, 0.999f, 1e-9f);
             v1 = __builtin_fmaf(v1, 0.999f, 1e-9f);
@@ -85,6 +100,7 @@ __global__ __launch_bounds__(256, 2) void calib_mfma_kernel(float* out, int iter
       }
   }
   float s = v0 + v1 + v2 + v3;
+  for (int j = 0; j < 8; ++j) s += ss[j];
   for (int k = 0; k < 8; ++k)
     for (int e = 0; e < 16; ++e) s += acc[k][e];
   out[blockIdx.x * 256 + threadIdx.x] = s;
@@ -99,7 +115,9 @@ hipError_t calib_mfma_launch(float* out, int iters, int mode, hipStream_t st) {
     case 0: hipLaunchKernelGGL((calib_mfma_kernel<0>), grid, block, 0, st, out, iters); break;
     case 1: hipLaunchKernelGGL((calib_mfma_kernel<1>), grid, block, 0, st, out, iters); break;
     case 2: hipLaunchKernelGGL((calib_mfma_kernel<2>), grid, block, 0, st, out, iters); break;
-    default: hipLaunchKernelGGL((calib_mfma_kernel<3>), grid, block, 0, st, out, iters); break;
+    case 3: hipLaunchKernelGGL((calib_mfma_kernel<3>), grid, block, 0, st, out, iters); break;
+    case 4: hipLaunchKernelGGL((calib_mfma_kernel<4>), grid, block, 0, st, out, iters); break;
+    default: hipLaunchKernelGGL((calib_mfma_kernel<5>), grid, block, 0, st, out, iters); break;
   }
   return hipGetLastError();
 }

@@ -41,7 +41,7 @@ hipError_t mlp_bwd_launch(const MlpArgs& p, hipStream_t st);
 
 // The matrix-core calibration (calib.hip, a measurement aid): kCalibBlocks
 // work-groups of 256 threads, two per CU, each wave `iters` (a multiple of 8)
-// 32x32x16 bf16 products on each of its eight accumulators, in `mode` 0-3
+// 32x32x16 bf16 products on each of its eight accumulators, in `mode` 0-5
 // (see calib.hip); one float per thread into out.
 constexpr int kCalibBlocks = 512;
 hipError_t calib_mfma_launch(float* out, int iters, int mode, hipStream_t st);
